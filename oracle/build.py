@@ -1,0 +1,31 @@
+"""Build the CPU oracle library (oracle/liboracle.so) with gcc.
+
+Test infrastructure only: the oracle is a plain fp64 C implementation used by
+the tests, the smoke check and the benchmark's CPU-baseline leg.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCES = ["attn_oracle.c", "sage8_oracle.c"]
+LIB = os.path.join(HERE, "liboracle.so")
+
+# No fast-math and no FMA contraction: the quantisation steps must round
+# exactly as written.
+CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(HERE, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", *CFLAGS, *srcs, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,181 @@
+"""Fused attention forward for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libattn.so`` (the C ABI of ``include/attn.h``).
+It only marshals arguments: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
+
+    fwd(q, k, v, causal=False, scale=None, bias=None, out_dtype=None,
+        return_lse=False)                       # fp16 / bf16 path
+    prep = sage8_prep(q, k, v)                  # 8-bit preparation
+    fwd_sage8(prep, causal=False, ...)          # 8-bit forward
+    sageattn(q, k, v, causal=False, ...)        # both 8-bit steps
+
+Tensors are [B, H, N, d] contiguous CUDA (HIP) tensors, d in {64, 128}.
+``bias`` is fp32 [B, H, ceil(N/64), ceil(N/64)]: an additive logit per
+64-query x 64-key block in natural-log units.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fwd", "sage8_prep", "fwd_sage8", "sageattn", "AttnError", "Sage8Prepared",
+           "lib", "LIB_PATH", "status_str"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
+_DTYPE_CODE = {torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn.so with argument types set.  Raises if it has not
+    been built (``python __graft_entry__.py`` or ``bit_attention_attn_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run bit_attention_attn_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
+    for name in ("attn_fwd_f16", "attn_fwd_bf16"):
+        fn = getattr(L, name)
+        fn.argtypes = fwd_args
+        fn.restype = i
+    L.attn_sage8_workspace_size.argtypes = [i, i, i, i]
+    L.attn_sage8_workspace_size.restype = sz
+    L.attn_k_smooth_quant.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+    L.attn_k_smooth_quant.restype = i
+    L.attn_fwd_sage8.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
+    L.attn_fwd_sage8.restype = i
+    L.attn_status_str.argtypes = [i]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_abi_version.argtypes = []
+    L.attn_abi_version.restype = i
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B,H,N,d] tensor")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must share one dtype: float16 or bfloat16")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+
+
+def _check_bias(bias, B, H, N, device):
+    if bias is None:
+        return None
+    nb = (N + 63) // 64
+    if (bias.dtype != torch.float32 or tuple(bias.shape) != (B, H, nb, nb)
+            or not bias.is_contiguous() or bias.device != device):
+        raise ValueError(f"bias must be a contiguous fp32 [B,H,{nb},{nb}] tensor on {device}")
+    return bias
+
+
+def fwd(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False):
+    """Fused attention forward on fp16/bf16 inputs.  Returns O (and LSE in
+    natural-log units, fp32 [B,H,N], when return_lse)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    bias = _check_bias(bias, B, H, N, q.device)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    fn = lib().attn_fwd_bf16 if q.dtype == torch.bfloat16 else lib().attn_fwd_f16
+    with torch.cuda.device(q.device):
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                float(scale), _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(q.device))
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+    return (o, lse) if return_lse else o
+
+
+class Sage8Prepared:
+    """Workspace written by the 8-bit preparation, with the shape it was
+    prepared for (the forward must use the same shape)."""
+
+    def __init__(self, workspace, shape, in_dtype):
+        self.workspace = workspace
+        self.shape = tuple(shape)
+        self.in_dtype = in_dtype
+
+
+def sage8_prep(q, k, v, workspace=None):
+    """K smoothing and 8-bit quantisation of Q, K, V into a device workspace."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    L = lib()
+    need = L.attn_sage8_workspace_size(B, H, N, d)
+    if need == 0:
+        raise AttnError(2, "attn_sage8_workspace_size")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = L.attn_k_smooth_quant(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d,
+                                   _ptr(workspace), workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_k_smooth_quant")
+    return Sage8Prepared(workspace, (B, H, N, d), q.dtype)
+
+
+def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtype=None,
+              return_lse=False):
+    """8-bit fused forward from a prepared workspace."""
+    B, H, N, d = prep.shape
+    dev = prep.workspace.device
+    bias = _check_bias(bias, B, H, N, dev)
+    out_dtype = prep.in_dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    with torch.cuda.device(dev):
+        st = lib().attn_fwd_sage8(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d,
+                                  int(bool(causal)), float(scale), _ptr(bias),
+                                  _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_sage8")
+    return (o, lse) if return_lse else o
+
+
+def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False):
+    """8-bit attention in one call (preparation, then the forward)."""
+    prep = sage8_prep(q, k, v)
+    return fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
+                     return_lse=return_lse)

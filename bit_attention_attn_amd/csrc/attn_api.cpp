@@ -1,0 +1,154 @@
+// attn_api.cpp -- the extern "C" entry points declared in include/attn.h.
+//
+// Every argument check runs before any HIP call, so an invalid call returns
+// its status without touching the device.  There is no fallback: shapes,
+// dtypes or devices the kernels do not cover are errors.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+attn_status check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  const int64_t elems = (int64_t)B * H * N * d;
+  if (elems >= kMaxElems) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status check_common(void* o, float* lse, int B, int H, int N, int d, int causal, float scale,
+                         const float* bias) {
+  if (o == nullptr) return ATTN_ERR_NULL;
+  attn_status s = check_shape(B, H, N, d);
+  if (s != ATTN_OK) return s;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_ARG;
+  if (!aligned(o, 16)) return ATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  if (bias && !aligned(bias, 4)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+// 0 unknown, 1 gfx950, 2 other / unavailable; per device ordinal.
+std::atomic<int> g_dev_ok[64];
+
+attn_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
+  if (dev < 64) {
+    const int known = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (known == 1) return ATTN_OK;
+    if (known == 2) return ATTN_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+attn_status fwd16(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int N, int d, int causal, float scale, const float* bias, int out_dtype,
+                  void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
+  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
+  if (s != ATTN_OK) return s;
+  const int in_dtype = bf16 ? ATTN_DTYPE_BF16 : ATTN_DTYPE_F16;
+  if (out_dtype != in_dtype && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  attn::FwdArgs a{q, k, v, o, lse, bias, B, H, N, d, causal, scale,
+                  out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16)};
+  if (attn::launch_fwd16(a, bf16, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                         int N, int d, int causal, float scale, const float* bias, int out_dtype,
+                         void* stream) {
+  return fwd16(false, q, k, v, o, lse, B, H, N, d, causal, scale, bias, out_dtype, stream);
+}
+
+attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                          int N, int d, int causal, float scale, const float* bias, int out_dtype,
+                          void* stream) {
+  return fwd16(true, q, k, v, o, lse, B, H, N, d, causal, scale, bias, out_dtype, stream);
+}
+
+size_t attn_sage8_workspace_size(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != ATTN_OK) return 0;
+  return attn::sage8_layout(B, H, N, d).total;
+}
+
+attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
+                                int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
+  attn_status s = check_shape(B, H, N, d);
+  if (s != ATTN_OK) return s;
+  if (in_dtype != ATTN_DTYPE_F16 && in_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+  if (workspace_bytes < attn::sage8_layout(B, H, N, d).total) return ATTN_ERR_WORKSPACE;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  if (attn::launch_sage8_prep(q, k, v, in_dtype == ATTN_DTYPE_BF16, B, H, N, d, workspace,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
+                           int causal, float scale, const float* bias, int out_dtype, void* stream) {
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
+  if (s != ATTN_OK) return s;
+  if (out_dtype != ATTN_DTYPE_F16 && out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32)
+    return ATTN_ERR_DTYPE;
+  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  attn::FwdArgs a{nullptr, nullptr, nullptr, o, lse, bias, B, H, N, d, causal, scale,
+                  out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32
+                                              : (out_dtype == ATTN_DTYPE_BF16 ? attn::kOutBF16 : attn::kOutF16)};
+  if (attn::launch_fwd_sage8(workspace, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: B, H, N must be >= 1 and each tensor < 2^31 elements";
+    case ATTN_ERR_HEADDIM: return "ATTN_ERR_HEADDIM: head dimension must be 64 or 128";
+    case ATTN_ERR_DTYPE: return "ATTN_ERR_DTYPE: unsupported input/output dtype";
+    case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: pointer not aligned (tensors 16 B, workspace 256 B)";
+    case ATTN_ERR_ARG: return "ATTN_ERR_ARG: invalid argument (causal must be 0/1, scale finite)";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_DEVICE: return "ATTN_ERR_DEVICE: current device is not gfx950 (MI355X)";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown attn_status";
+  }
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// attn_common.hpp -- device helpers shared by the gfx950 attention kernels.
+//
+// Register layouts used throughout (verified on gfx950 for the 32x32 MFMA
+// family): for D = A*B with A of 32 rows and B of 32 columns,
+//   A operand: lane l holds row (l % 32), a lane-half-specific slice of k;
+//   B operand: lane l holds column (l % 32), the same k slice as A;
+//   C/D:       lane l holds column (l % 32) and rows
+//              8*(r/4) + 4*(l/32) + (r%4) for register r = 0..15.
+// Because k is a reduction index, any assignment of k to (lane half,
+// element) works as long as A and B agree; the kernels exploit this to feed
+// the accumulator of one product straight into the next as an operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 32x32x16 MFMA on 16-bit inputs packed as 4 dwords per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// Two fp32 values to a packed pair of 16-bit floats, round to nearest even.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  f32x2_t v = {x, y};
+  if constexpr (BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+}
+
+// Values of this lane and of its partner (lane ^ 32).  With both operands
+// equal, permlane32_swap returns (x[l], x[l^32]) in some order per lane, so
+// max/sum of the pair is the reduction over the two lane halves.  The two
+// results are first copied into plain integers: bit-casting the builtin's
+// result elements directly to float lowers both to the first element.
+__device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t u0 = p[0];
+  const uint32_t u1 = p[1];
+  a = __uint_as_float(u0);
+  b = __uint_as_float(u1);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor32_min(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return fminf(a, b);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return a + b;
+}
+
+// Transposing LDS read of four 16-bit values.  Within each group of 16 lanes,
+// lane 4a+b receives element b of the 8-byte rows addressed by lanes a, a+4,
+// a+8 and a+12 of the group (verified on gfx950).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup -> work item: consecutive work items are placed on the same XCD
+// (hardware hands workgroups to the 8 XCDs round-robin), so the query tiles
+// of one head share that XCD's L2 while they stream the same keys/values.
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  if ((n & 7) != 0) return wg;
+  return (wg & 7) * (n >> 3) + (wg >> 3);
+}
+
+}  // namespace attn

@@ -1,0 +1,42 @@
+// attn_internal.hpp -- launch interface between the C ABI layer and the
+// kernels.  Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum OutKind : int { kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2 };
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;         // nullable
+  const float* bias;  // nullable, [B,H,nb,nb]
+  int B, H, N, d;
+  int causal;
+  float scale;
+  int out_kind;       // OutKind
+};
+
+// 16-bit path (fp16 when bf16 == false).
+hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream);
+
+// 8-bit path.
+struct Sage8Layout {
+  // byte offsets inside the workspace, each 256-byte aligned
+  size_t qq, kq, vq, sq, sk, sv, kmean, kpart, vpart;
+  size_t total;
+  int nblk;    // ceil(N/64): per-64-row blocks of Q and K
+  int nchunk;  // token chunks of the column reductions
+};
+Sage8Layout sage8_layout(int B, int H, int N, int d);
+hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H,
+                             int N, int d, void* ws, hipStream_t stream);
+hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,151 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention forward.
+ *
+ * The library computes, for every batch b, head h and query i,
+ *
+ *     O[b,h,i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:]
+ *                             + bias[b,h,i/64,j/64] ) V[b,h,j,:]
+ *
+ * over the keys j the mask allows (causal: j <= i).  This is the attention
+ * formula of page 4 ("FlashAttention (TR)", section on the problems of
+ * standard attention), with the masking step of the single fused kernel
+ * (same page, section on fusing all operations into one kernel) and the
+ * optional additive log-form gate of page 5 ("SAS", the log-form gate placed
+ * inside the attention softmax).  The N x N score matrix never reaches
+ * device memory: keys are processed in blocks with a running maximum and a
+ * running sum (page 4, online softmax section) inside one kernel that
+ * writes only the final output (page 4, fused kernel section).
+ *
+ * The 8-bit path follows page 1 ("SageAttention", claim vs reality
+ * section): K is mean-centred over tokens, Q K^T runs in INT8 with one fp32
+ * scale per 64-row block, P goes to FP8 e4m3 for the P V product, and the
+ * products are accumulated in two levels in fp32.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are contiguous [B,H,N,d], d innermost, in device memory, with
+ *    16-byte aligned base pointers.  d must be 64 or 128; B, H, N >= 1;
+ *    B*H*N*d must fit in 2^31 elements per tensor.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no mutable state between calls and is safe to call from several
+ *    host threads (on distinct output buffers).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream).  Every argument check runs before any launch: a non-zero
+ *    status means nothing was launched and nothing was written.  Faults of
+ *    the device itself surface at stream synchronisation.
+ *  - There is no fallback path: an unsupported shape, dtype or device is an
+ *    error, never a slower materialising implementation (page 3, the
+ *    glossary entry's warning about silent fallbacks).
+ *  - NaN or Inf in the inputs propagate.  A row whose every key is masked
+ *    (possible only through -inf bias entries) gives O = 0 and LSE = -inf.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,      /* a required pointer is NULL                   */
+    ATTN_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 elts */
+    ATTN_ERR_HEADDIM = 3,   /* d is not 64 or 128                           */
+    ATTN_ERR_DTYPE = 4,     /* unsupported input/output dtype combination   */
+    ATTN_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned             */
+    ATTN_ERR_ARG = 6,       /* scale not finite, causal not 0/1, ...        */
+    ATTN_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required      */
+    ATTN_ERR_DEVICE = 8,    /* current device is not gfx950                 */
+    ATTN_ERR_HIP = 9        /* a HIP runtime call or a launch failed        */
+} attn_status;
+
+/* Element types of inputs and outputs. */
+typedef enum {
+    ATTN_DTYPE_F16 = 0,
+    ATTN_DTYPE_BF16 = 1,
+    ATTN_DTYPE_F32 = 2
+} attn_dtype;
+
+/*
+ * attn_fwd_f16 / attn_fwd_bf16 -- fused attention forward (fp16 / bf16).
+ *
+ *  q, k, v    [B,H,N,d] fp16 (attn_fwd_f16) or bf16 (attn_fwd_bf16), read only.
+ *  o          [B,H,N,d] output; out_dtype is the input dtype or ATTN_DTYPE_F32.
+ *  lse        [B,H,N] fp32 natural-log log-sum-exp of each row's scaled,
+ *             biased scores (nullable: not written when NULL).
+ *  causal     0 or 1; 1 lets query i see keys j <= i.
+ *  scale      finite multiplier of Q.K (1/sqrt(d) for standard attention).
+ *  bias       nullable fp32 [B,H,nb,nb], nb = ceil(N/64): additive logit
+ *             (natural-log units, not multiplied by scale) for each
+ *             64-query x 64-key block.  -inf entries mask whole blocks.
+ *  Products run on the matrix cores with fp32 accumulation; P is rounded
+ *  to the input dtype for the P V product.
+ */
+attn_status attn_fwd_f16(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int B, int H, int N, int d, int causal,
+                         float scale, const float* bias, int out_dtype,
+                         void* stream);
+attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
+                          float* lse, int B, int H, int N, int d, int causal,
+                          float scale, const float* bias, int out_dtype,
+                          void* stream);
+
+/*
+ * attn_sage8_workspace_size -- bytes of device workspace that
+ * attn_k_smooth_quant fills and attn_fwd_sage8 reads for this shape
+ * (0 when the shape is invalid).  The workspace holds the INT8 Q and K,
+ * the FP8 V (in the layout the P V product reads), their fp32 scales and
+ * the K mean; its layout is private to the library.
+ */
+size_t attn_sage8_workspace_size(int B, int H, int N, int d);
+
+/*
+ * attn_k_smooth_quant -- the 8-bit preparation (page 1, "SageAttention":
+ * mean-centring of K before INT8 quantisation; FP8 for the second product).
+ *
+ *  q, k, v    [B,H,N,d] in in_dtype (ATTN_DTYPE_F16 or ATTN_DTYPE_BF16).
+ *  workspace  device buffer of at least attn_sage8_workspace_size bytes,
+ *             256-byte aligned; fully overwritten.
+ *  Steps: kmean[b,h,c] = mean over all N tokens of K (sum in fp64, rounded
+ *  once to fp32); INT8 codes of Q and of K - kmean with one scale per
+ *  64-row block (scale = amax/127, code = rne(x * (127/amax)), clamped to
+ *  +-127); e4m3 codes of V with one scale per (b,h,channel) (scale =
+ *  amax/448, code = e4m3_rne(v * (448/amax))).  A zero amax gives scale 1.
+ */
+attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v,
+                                int in_dtype, int B, int H, int N, int d,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * attn_fwd_sage8 -- 8-bit fused forward from a prepared workspace.
+ *
+ *  workspace  written by attn_k_smooth_quant with the same B, H, N, d
+ *             (the library cannot check this; the Python binding bundles
+ *             the two so they cannot disagree).
+ *  o          [B,H,N,d] in out_dtype (F16, BF16 or F32).
+ *  lse, causal, scale, bias as for attn_fwd_bf16.
+ *  S = Qq Kq^T in INT8 with int32 accumulation, dequantised with the two
+ *  block scales; online softmax in fp32; P^ = e4m3(448 P); each key block's
+ *  P^ V partial accumulates in fp32 (level 1) and is added to the rescaled
+ *  running output in fp32 (level 2); the V scales and 1/(448 l) are applied
+ *  once at the end.
+ */
+attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B,
+                           int H, int N, int d, int causal, float scale,
+                           const float* bias, int out_dtype, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_str(int status);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,93 @@
+"""The C ABI: the library loads, exports every function include/attn.h
+declares, and rejects invalid arguments with the documented status before any
+HIP call (so these run without a GPU; no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_attention_attn_amd as attn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn.h")
+
+OK, E_NULL, E_SHAPE, E_HEADDIM, E_DTYPE, E_ALIGN, E_ARG, E_WS, E_DEV, E_HIP = range(10)
+F16, BF16, F32 = 0, 1, 2
+FAKE = 0x100000  # 16- and 256-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = attn.lib()
+    names = _declared_functions()
+    assert {"attn_fwd_f16", "attn_fwd_bf16", "attn_sage8_workspace_size", "attn_k_smooth_quant",
+            "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.attn_abi_version() == 1
+    for s in range(10):
+        assert len(attn.status_str(s)) > 4
+
+
+def _fwd(fn, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=1, N=64, d=64, causal=0, scale=0.125,
+         bias=None, out=BF16):
+    return fn(q, k, v, o, lse, B, H, N, d, causal, scale, bias, out, None)
+
+
+@pytest.mark.parametrize("name,dt", [("attn_fwd_bf16", BF16), ("attn_fwd_f16", F16)])
+def test_fwd_validation(name, dt):
+    fn = getattr(attn.lib(), name)
+    assert _fwd(fn, q=None, out=dt) == E_NULL
+    assert _fwd(fn, o=None, out=dt) == E_NULL
+    assert _fwd(fn, B=0, out=dt) == E_SHAPE
+    assert _fwd(fn, N=0, out=dt) == E_SHAPE
+    assert _fwd(fn, H=-1, out=dt) == E_SHAPE
+    assert _fwd(fn, d=96, out=dt) == E_HEADDIM
+    assert _fwd(fn, d=256, out=dt) == E_HEADDIM
+    assert _fwd(fn, B=1 << 10, H=1 << 10, N=1 << 10, d=128, out=dt) == E_SHAPE  # 2^37 elements
+    assert _fwd(fn, causal=2, out=dt) == E_ARG
+    assert _fwd(fn, scale=float("nan"), out=dt) == E_ARG
+    assert _fwd(fn, scale=float("inf"), out=dt) == E_ARG
+    assert _fwd(fn, out=F16 if dt == BF16 else BF16) == E_DTYPE
+    assert _fwd(fn, out=7) == E_DTYPE
+    assert _fwd(fn, q=FAKE + 8, out=dt) == E_ALIGN
+    assert _fwd(fn, o=FAKE + 2, out=dt) == E_ALIGN
+    assert _fwd(fn, lse=FAKE + 2, out=dt) == E_ALIGN
+
+
+def test_sage8_validation():
+    L = attn.lib()
+    assert L.attn_sage8_workspace_size(1, 1, 64, 96) == 0
+    assert L.attn_sage8_workspace_size(0, 1, 64, 64) == 0
+    need = L.attn_sage8_workspace_size(1, 2, 100, 64)
+    assert need >= 3 * 2 * 128 * 64  # three 8-bit tensors padded to 128 rows
+    prep = L.attn_k_smooth_quant
+    assert prep(None, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need, None) == E_NULL
+    assert prep(FAKE, FAKE, FAKE, F32, 1, 2, 100, 64, FAKE, need, None) == E_DTYPE
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 96, FAKE, need, None) == E_HEADDIM
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, None, need, None) == E_WS
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need - 1, None) == E_WS
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE + 16, need, None) == E_ALIGN
+    fwd8 = L.attn_fwd_sage8
+    assert fwd8(None, FAKE, None, 1, 2, 100, 64, 0, 0.1, None, BF16, None) == E_WS
+    assert fwd8(FAKE, None, None, 1, 2, 100, 64, 0, 0.1, None, BF16, None) == E_NULL
+    assert fwd8(FAKE, FAKE, None, 1, 2, 100, 64, 3, 0.1, None, BF16, None) == E_ARG
+    assert fwd8(FAKE, FAKE, None, 1, 2, 100, 64, 0, 0.1, None, 9, None) == E_DTYPE
+    assert fwd8(FAKE + 64, FAKE, None, 1, 2, 100, 64, 0, 0.1, None, BF16, None) == E_ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error; a GPU is visible")
+def test_no_device_is_an_error_not_a_fallback():
+    assert _fwd(attn.lib().attn_fwd_bf16) == E_DEV
+
+
+def test_python_binding_rejects_cpu_tensors():
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.fwd(q, q, q)

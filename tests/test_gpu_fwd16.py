@@ -1,0 +1,162 @@
+"""GPU parity of the fp16/bf16 fused forward against the fp64 oracle.
+
+Bar (attention forward, fp16/bf16): max abs error <= 1e-2 and mean abs error
+<= 1e-3 against the fp64 oracle fed the same rounded inputs.  Small shapes
+compare every row (several 128-query tiles, 64-key blocks and ragged tails);
+the full-size workloads compare the sampled parity rows and check the whole
+output for NaN/Inf.  Every call goes through the C ABI via the binding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_attention_attn_amd as attn
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 1e-2, 1e-3
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _run_and_check(inp, causal, scale, out_dtype=None, rows=None, lse_tol=2e-3, label=""):
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    bias = inp["bias"].to(DEV) if inp["bias"] is not None else None
+    print(f"[gpu] fwd16 {label} shape={tuple(q.shape)} {q.dtype} causal={causal}", flush=True)
+    o, lse = attn.fwd(q, k, v, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
+                      return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    qn, kn, vn = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    bn = inp["bias"].numpy() if inp["bias"] is not None else None
+    if rows is None:
+        o_ref, l_ref = oracle.attn_full(qn, kn, vn, causal=causal, scale=scale, bias=bn)
+        got, got_l = _np(o).astype(np.float64), _np(lse).astype(np.float64)
+    else:
+        o_ref, l_ref = oracle.attn_rows(qn, kn, vn, rows, causal=causal, scale=scale, bias=bn)
+        got = workloads.gather_rows(o, rows)
+        idx = torch.as_tensor(rows, device=DEV)
+        got_l = lse[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+    m = workloads.error_metrics(got, o_ref)
+    assert m["max_abs"] <= MAX_ABS and m["mean_abs"] <= MEAN_ABS, (label, m)
+    assert np.abs(got_l - l_ref).max() <= lse_tol, (label, np.abs(got_l - l_ref).max())
+    return o, lse, m
+
+
+SWEEP_N = [1, 17, 63, 64, 65, 127, 128, 129, 200, 256, 300]
+
+
+@pytest.mark.parametrize("N", SWEEP_N)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_small_sweep_bf16(N, d, causal, with_bias):
+    inp = workloads.make_inputs(1, 2, N, d, "bf16", seed=N * 31 + d + causal, gate=with_bias)
+    _run_and_check(inp, causal, 1 / math.sqrt(d), label=f"sweep N={N} d={d}")
+
+
+@pytest.mark.parametrize("N", [1, 65, 200, 256])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("out", ["same", "f32"])
+def test_small_sweep_f16(N, d, causal, out):
+    inp = workloads.make_inputs(2, 1, N, d, "f16", seed=N + d, gate=causal)
+    _run_and_check(inp, causal, 1 / math.sqrt(d), out_dtype=torch.float32 if out == "f32" else None,
+                   label=f"f16 N={N} d={d}")
+
+
+def test_bf16_fp32_output():
+    inp = workloads.make_inputs(2, 3, 190, 128, "bf16", seed=3)
+    o, _, _ = _run_and_check(inp, True, 0.09, out_dtype=torch.float32, label="bf16->f32")
+    assert o.dtype == torch.float32
+
+
+def test_workload1_tiny_exact_all_rows():
+    cfg, inp = workloads.config_inputs(1)
+    o, _, m = _run_and_check(inp, cfg["causal"], 1 / math.sqrt(cfg["d"]), out_dtype=torch.float32,
+                             label="workload 1")
+    assert o.dtype == torch.float32 and o.shape == (1, 2, 256, 64)
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3, 5])
+def test_full_size_workloads_sampled_rows(cfg_id):
+    cfg, inp = workloads.config_inputs(cfg_id)
+    rows = workloads.parity_rows(cfg["B"], cfg["H"], cfg["N"], seed=cfg_id)
+    _run_and_check(inp, cfg["causal"], 1 / math.sqrt(cfg["d"]), rows=rows, label=f"workload {cfg_id}")
+
+
+def test_determinism_and_causal_row0():
+    inp = workloads.make_inputs(2, 4, 1000, 128, "bf16", seed=21)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    outs = [attn.fwd(q, k, v, causal=True) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    # causal row 0 sees only key 0: P = 1 exactly, so O[0] is V[0] bit for bit
+    assert torch.equal(outs[0][:, :, 0], v[:, :, 0])
+
+
+def test_k_shift_invariance_gpu():
+    inp = workloads.make_inputs(1, 2, 500, 64, "bf16", seed=22)
+    q, v = inp["q"].to(DEV), inp["v"].to(DEV)
+    # K on a 1/8 grid and small integer shifts: K + shift stays exact in bf16
+    k = ((inp["k"].float() * 8).round().clamp(-40, 40) / 8).to(torch.bfloat16).to(DEV)
+    shift = (torch.arange(64, device=DEV) % 5 - 2).float()
+    k2 = (k.float() + shift).to(torch.bfloat16)
+    assert torch.equal(k2.float(), k.float() + shift)
+    o1 = attn.fwd(q, k, v, causal=True)
+    o2 = attn.fwd(q, k2, v, causal=True)
+    assert (o1.float() - o2.float()).abs().max().item() <= MAX_ABS
+
+
+def test_q_zero_gives_prefix_means():
+    inp = workloads.make_inputs(1, 2, 300, 128, "bf16", seed=23)
+    q = torch.zeros_like(inp["q"]).to(DEV)
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+    o = attn.fwd(q, k, v, causal=True, out_dtype=torch.float32)
+    ref = torch.cumsum(v.double(), dim=2) / torch.arange(1, 301, device=DEV, dtype=torch.float64)[None, None, :, None]
+    assert (o.double() - ref).abs().max().item() <= 1e-2
+
+
+def test_no_quadratic_memory():
+    B, H, N, d = 1, 8, 16384, 128
+    q = torch.randn((B, H, N, d), device=DEV, dtype=torch.bfloat16)
+    k, v = torch.randn_like(q), torch.randn_like(q)
+    attn.fwd(q, k, v, causal=True)  # warm the allocator path
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    o, lse = attn.fwd(q, k, v, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    grown = torch.cuda.max_memory_allocated() - base
+    assert grown <= o.numel() * 2 + lse.numel() * 4 + (1 << 20), grown  # never B*H*N^2
+    assert grown < B * H * N * N // 64
+
+
+def test_fully_masked_rows_and_minus_inf_bias():
+    inp = workloads.make_inputs(1, 1, 192, 64, "bf16", seed=24)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    bias = torch.zeros((1, 1, 3, 3), dtype=torch.float32)
+    bias[0, 0, 1, :] = float("-inf")      # query block 1 sees nothing
+    bias[0, 0, 0, 1:] = float("-inf")     # query block 0 sees only key block 0
+    o, lse = attn.fwd(q, k, v, causal=False, bias=bias.to(DEV), out_dtype=torch.float32, return_lse=True)
+    assert (o[0, 0, 64:128] == 0).all() and torch.isneginf(lse[0, 0, 64:128]).all()
+    o_ref, l_ref = oracle.attn_full(inp["q"].float().numpy(), inp["k"].float().numpy(),
+                                    inp["v"].float().numpy(), causal=False, scale=0.125,
+                                    bias=bias.numpy())
+    sel = np.r_[0:64, 128:192]
+    assert np.abs(o[0, 0].double().cpu().numpy()[sel] - o_ref[0, 0][sel]).max() <= MAX_ABS
+
+
+def test_negative_and_zero_scale():
+    inp = workloads.make_inputs(1, 2, 150, 64, "f16", seed=25)
+    for scale in (-0.2, 0.0):
+        _run_and_check(inp, True, scale, label=f"scale={scale}")
+        _run_and_check(inp, False, scale, label=f"scale={scale}")

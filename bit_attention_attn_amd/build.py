@@ -18,7 +18,12 @@ SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_sage8.hip"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no packed fp32 VALU instructions in device code.
+# -amdgpu-mfma-vgpr-form: matrix results stay in VGPRs, where the softmax
+# reads them, instead of AGPRs that need a copy per element.
+# -fno-honor-nans: max/min of matrix results need no NaN-quieting copies (a
+# NaN score still reaches the output through exp2); infinities stay honoured.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+         "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
 

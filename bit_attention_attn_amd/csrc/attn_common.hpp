@@ -58,6 +58,19 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   }
 }
 
+// acc + x.lo + x.hi for a packed pair of 16-bit floats (one dot-product
+// instruction against the pair (1, 1)).
+template <bool BF16>
+__device__ __forceinline__ float sum2_acc(uint32_t x, float acc) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                           __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), __builtin_bit_cast(f16x2_t, 0x3C003C00u),
+                                  acc, false);
+  }
+}
+
 // Values of this lane and of its partner (lane ^ 32).  With both operands
 // equal, permlane32_swap returns (x[l], x[l^32]) in some order per lane, so
 // max/sum of the pair is the reduction over the two lane halves.  The two

@@ -5,15 +5,20 @@
 // with a running maximum and running sum; one fused kernel that writes only
 // the final result) without forming the N x N score matrix anywhere.
 //
-// Work split: one workgroup of 4 waves per (b, h, 128-query tile); each wave
-// owns 32 queries.  Keys and values stream through LDS in blocks of 64,
-// double buffered: the global loads of block j+1 are in flight while block j
-// is computed.
+// Work split: one workgroup of NW waves per (b, h, query tile); each wave
+// owns QS x 32 queries (QS MFMA column tiles, so one K or V operand read from
+// LDS feeds QS matrix instructions).  Two waves share each SIMD (from two
+// workgroups when NW = 4, from one when NW = 8), so one wave's softmax runs
+// on the vector ALU while the other's products run on the matrix cores.
+// Keys and values stream through LDS in blocks of 64; the global loads of a
+// future block are in flight while the current one is computed.  With PIPE
+// the S^T product of block j+1 is issued in the same stretch of code as the
+// softmax of block j, so one wave can also overlap the two by itself.
 //
 // Per key block and wave:
-//   S^T = K Q^T on the matrix cores (32x32x16, fp32 accumulation).  Computing
-//       the transpose puts one query per lane column, so the row maximum and
-//       row sum over keys reduce inside a lane plus one lane-half exchange.
+//   S^T = K Q^T (32x32x16 MFMA, fp32 accumulation): one query per lane
+//       column, so the row maximum and row sum over keys reduce inside a lane
+//       plus one exchange between the two lane halves.
 //   softmax in base 2: the scale is folded into c = scale*log2(e); the bias
 //       (natural-log units) is one scalar per 64x64 block, so the block
 //       maximum of c*S + bias is c*max(S) + bias.
@@ -30,14 +35,25 @@
 #include "attn_internal.hpp"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace attn {
 namespace {
 
-constexpr int kBM = 128;      // queries per workgroup
 constexpr int kBN = 64;       // keys per block
-constexpr int kThreads = 256; // 4 waves
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+
+// Tiling: QS query tiles of 32 per wave, NW waves per workgroup, PIPE as
+// above.  Buffers: without PIPE, block j+1 (K and V) is loaded during block
+// j; with PIPE, K of block j+2 and V of block j+1 are.
+template <int QS, int NW, bool PIPE>
+struct Tiling {
+  static constexpr int kWQ = 32 * QS;            // queries per wave
+  static constexpr int kBM = NW * kWQ;           // queries per workgroup
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kKbuf = PIPE ? 3 : 2;
+  static constexpr int kVbuf = 2;
+};
 
 struct Fwd16Params {
   const uint16_t* q;
@@ -50,27 +66,45 @@ struct Fwd16Params {
   int nq;      // query tiles per head
   int nb;      // ceil(N/64), bias blocks per side
   int ntiles;  // B*H*nq
-  float c;     // scale * log2(e)
+  float c;     // scale * log2(e), never 0
   int out_f32;
 };
 
-template <int D>
+template <int D, int QS, int NW, bool PIPE>
 struct Fwd16Smem {
-  static constexpr int kRow = D + 8;       // padded row, elements
-  static constexpr int kTile = kBN * kRow; // elements per K or V tile
-  static constexpr int kElems = 4 * kTile; // two buffers of (K, V)
+  using T = Tiling<QS, NW, PIPE>;
+  // Padded rows.  K: 16 bytes of padding, so the 16-byte operand reads of 16
+  // consecutive rows fall on distinct banks.  V: the transposing reads touch
+  // 4 consecutive rows x 64 bytes per half wave; a row stride of 288 bytes
+  // (d = 128) or 192 bytes (d = 64) spreads them over the banks (measured
+  // on gfx950: 107 B/clk/CU against 62 B/clk/CU at a 272-byte stride).
+  static constexpr int kKRow = D + 8;
+  static constexpr int kVRow = D == 128 ? D + 16 : D + 32;
+  static constexpr int kKTile = kBN * kKRow;
+  static constexpr int kVTile = kBN * kVRow;
+  static constexpr int kLoop = T::kKbuf * kKTile + T::kVbuf * kVTile;
+  static constexpr int kStage = NW * T::kWQ * (D + 4) * 2;  // fp32 output staging, 16-bit units
+  static constexpr int kElems = kLoop > kStage ? kLoop : kStage;
 };
 
-template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(Fwd16Params p) {
-  using S = Fwd16Smem<D>;
-  constexpr int kRow = S::kRow;
-  constexpr int kTile = S::kTile;
+template <int D, bool BF16, bool CAUSAL, int QS, int NW, bool PIPE>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
+  using TL = Tiling<QS, NW, PIPE>;
+  using S = Fwd16Smem<D, QS, NW, PIPE>;
+  constexpr int kWQ = TL::kWQ, kBM = TL::kBM, kThreads = TL::kThreads;
+  constexpr int kKbuf = TL::kKbuf, kVbuf = TL::kVbuf;
+  constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
+  constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
+  constexpr int kCpr = D / 8;  // 16-byte chunks of data per row
+  constexpr int kDT = D / 32;  // 32-row tiles of O^T
+  constexpr int kKS = D / 16;  // k-steps of S^T = K Q^T
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::kElems];
+  uint16_t* const kbase_lds = smem;                   // kKbuf K tiles
+  uint16_t* const vbase_lds = smem + kKbuf * kKTile;  // kVbuf V tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -80,148 +114,171 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(Fwd16Params p) {
   if (CAUSAL) qt = p.nq - 1 - qt;  // heaviest tiles first
   const int N = p.N;
   const int q0 = qt * kBM;
-  const int qw0 = q0 + wave * 32;
-  const int qi = qw0 + l32;
+  const int qw0 = q0 + wave * kWQ;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Q = p.q + head;
   const uint16_t* __restrict__ K = p.k + head;
   const uint16_t* __restrict__ V = p.v + head;
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16kk + 8hf .. +7].
-  u32x4_t qf[D / 16];
-  {
-    const bool ok = qi < N;
-    const uint16_t* src = Q + (size_t)(ok ? qi : 0) * D + 8 * hf;
+  // Q^T as the B operand of S^T = K Q^T: for query sub-tile qs the lane holds
+  // Q[qw0 + 32qs + l32][16kk + 8hf .. +7].  Rows past N read row N-1 (their
+  // results are never stored).
+  u32x4_t qf[QS][kKS];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4_t x = *(const u32x4_t*)(src + 16 * kk);
-      qf[kk] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
-    }
+  for (int qs = 0; qs < QS; ++qs) {
+    const int row = min(qw0 + 32 * qs + l32, N - 1);
+    const uint16_t* src = Q + (size_t)row * D + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) qf[qs][kk] = *(const u32x4_t*)(src + 16 * kk);
   }
 
   const int kend = CAUSAL ? min(N, q0 + kBM) : N;
   const int nkb = (kend + kBN - 1) / kBN;
-
-  // Loader: a 64 x D tile is 64*D/8 chunks of 16 bytes.
-  constexpr int kCpr = D / 8;
-  constexpr int kNld = kBN * kCpr / kThreads;
-  u32x4_t kr[kNld], vr[kNld];
-  auto load_tile = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < kNld; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / kCpr, ch = idx % kCpr;
-      const int key = kb * kBN + row;
-      if (key < N) {
-        kr[i] = *(const u32x4_t*)(K + (size_t)key * D + ch * 8);
-        vr[i] = *(const u32x4_t*)(V + (size_t)key * D + ch * 8);
-      } else {
-        kr[i] = u32x4_t{0u, 0u, 0u, 0u};
-        vr[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * 2 * kTile;
-#pragma unroll
-    for (int i = 0; i < kNld; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / kCpr, ch = idx % kCpr;
-      *(u32x4_t*)(ks + row * kRow + ch * 8) = kr[i];
-      *(u32x4_t*)(ks + kTile + row * kRow + ch * 8) = vr[i];
-    }
-  };
-
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
-  float m_run = -INFINITY;  // running max, log2 units (same in both lane halves)
-  float l_run = 0.f;        // this lane's partial row sum
-  const float c = p.c;
-  const bool pos = c >= 0.f;
-  // a wave whose queries all lie past N computes nothing (it still loads and
-  // synchronises); the clamp keeps its bias row inside the tensor
+  // last key block this wave computes (causal: its diagonal block)
+  const int wave_last = CAUSAL ? min(nkb - 1, qw0 / kBN) : nkb - 1;
   const bool wave_has_rows = qw0 < N;
-  const int qb64 = min(qw0 >> 6, p.nb - 1);
+
+  // ---- loader: a 64 x D tile is 64*D/8 chunks of 16 bytes, staged through
+  // registers; key rows past N read row N-1 (masked later), so every load is
+  // unconditional.
+  constexpr int kNst = kBN * kCpr / kThreads;
+  u32x4_t kst[kNst], vst[kNst];
+  auto load_k = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      const int key = min(kb * kBN + row, N - 1);
+      kst[i] = *(const u32x4_t*)(K + (size_t)key * D + ch * 8);
+    }
+  };
+  auto load_v = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      const int key = min(kb * kBN + row, N - 1);
+      vst[i] = *(const u32x4_t*)(V + (size_t)key * D + ch * 8);
+    }
+  };
+  auto store_k = [&](int buf) {
+    uint16_t* ks = kbase_lds + buf * kKTile;
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      *(u32x4_t*)(ks + row * kKRow + ch * 8) = kst[i];
+    }
+  };
+  auto store_v = [&](int buf) {
+    uint16_t* vs = vbase_lds + buf * kVTile;
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      *(u32x4_t*)(vs + row * kVRow + ch * 8) = vst[i];
+    }
+  };
+
+  // ---- per-wave online-softmax state
+  f32x16_t o[kDT][QS];
+  float m_run[QS], l_run[QS];  // running max (log2 units, equal in both lane halves), partial sums
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) o[dt][qs] = f32x16_t{};
+    m_run[qs] = -INFINITY;
+    l_run[qs] = 0.f;
+  }
+  const float c = p.c;
+  const bool pos = c > 0.f;
+  const float sent = pos ? -INFINITY : INFINITY;
+  const int qb64 = min(qw0 / kBN, p.nb - 1);
   const float* bias_row = p.bias ? p.bias + ((size_t)bh * p.nb + (size_t)qb64) * p.nb : nullptr;
 
-  // transposing-read coordinates for the V^T operand
+  // transposing-read coordinates for the V^T operand: this lane addresses row
+  // 16kk + vkey (and +8) at column 32dt + vcol
   const int g16 = lane >> 4, t16 = lane & 15;
   const int vkey = 4 * hf + (t16 >> 2);
   const int vcol = 16 * (g16 & 1) + 4 * (t16 & 3);
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkb) load_tile(j + 1);
-    const int kbase = j * kBN;
-    const bool active = wave_has_rows && (!CAUSAL || kbase <= qw0 + 31);
-    if (active) {
-      const uint16_t* Ks = smem + buf * 2 * kTile;
-      const uint16_t* Vs = Ks + kTile;
-
-      // ---- S^T = K Q^T for keys [kbase, kbase+64): two 32-key tiles
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+  // ---- S^T = K Q^T for one key block (two 32-key tiles x QS query tiles)
+  auto qk = [&](int buf, f32x16_t (&s)[2][QS]) {
+    const uint16_t* Ks = kbase_lds + buf * kKTile + l32 * kKRow + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+    for (int qs = 0; qs < QS; ++qs) s[0][qs] = s[1][qs] = f32x16_t{};
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          const u32x4_t a = *(const u32x4_t*)(Ks + (32 * T + l32) * kRow + 16 * kk + 8 * hf);
-          s[T] = mfma32x32x16<BF16>(a, qf[kk], s[T]);
+    for (int kk = 0; kk < kKS; ++kk)
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        // row 32T + l32, columns 16kk + 8hf .. +7
+        const u32x4_t a = *(const u32x4_t*)(Ks + 32 * T * kKRow + 16 * kk);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) s[T][qs] = mfma32x32x16<BF16>(a, qf[qs][kk], s[T][qs]);
+      }
+  };
+
+  // ---- masking of the causal diagonal block and the tail block (keys past
+  // N): masked scores become +-inf, so c*S is -inf and P = exp2(-inf) = 0.
+  auto apply_mask = [&](int j, f32x16_t (&s)[2][QS]) {
+    const int kb0 = j * kBN;
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + 32 * T + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int qi = qw0 + 32 * qs + l32;
+          const bool m = (CAUSAL && key > qi) || key >= N;
+          s[T][qs][r] = m ? sent : s[T][qs][r];
         }
-      }
+  };
+  auto needs_mask = [&](int j) { return (CAUSAL && j == wave_last) || (j + 1) * kBN > N; };
 
-      // ---- mask (diagonal and tail blocks only)
-      const bool need_mask = (CAUSAL && kbase + kBN - 1 > qw0) || (kbase + kBN > N);
-      const float sent = pos ? -INFINITY : INFINITY;
-      uint32_t mbits = 0u;
-      if (need_mask) {
+  // ---- block maximum and lazy rescale of the running state; returns the
+  // exponent offsets kc = bias - m (log2 units) of the block
+  auto block_max = [&](int j, f32x16_t (&s)[2][QS], float (&kc)[QS]) {
+    const float bl = bias_row ? bias_row[j] * kLog2e : 0.f;
+    float m_blk[QS];
+    bool need_any = false;
 #pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 32 * T + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool m = (CAUSAL && key > qi) || key >= N;
-            if (m) {
-              s[T][r] = sent;
-              mbits |= 1u << (16 * T + r);
-            }
-          }
-      }
-
-      // ---- block maximum of c*S (+ bias, constant over the block)
-      float mx;
+    for (int qs = 0; qs < QS; ++qs) {
+      float a0;
       if (pos) {
-        float a0 = fmaxf(s[0][0], s[1][0]);
+        a0 = fmaxf(s[0][qs][0], s[1][qs][0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) a0 = fmaxf(a0, fmaxf(s[0][r], s[1][r]));
-        mx = xor32_max(a0);
+        for (int r = 1; r < 16; ++r) a0 = fmaxf(a0, fmaxf(s[0][qs][r], s[1][qs][r]));
+        a0 = xor32_max(a0);
       } else {
-        float a0 = fminf(s[0][0], s[1][0]);
+        a0 = fminf(s[0][qs][0], s[1][qs][0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) a0 = fminf(a0, fminf(s[0][r], s[1][r]));
-        mx = xor32_min(a0);
+        for (int r = 1; r < 16; ++r) a0 = fminf(a0, fminf(s[0][qs][r], s[1][qs][r]));
+        a0 = xor32_min(a0);
       }
-      const float bl = bias_row ? bias_row[j] * kLog2e : 0.f;
-      const float m_blk = (mx == sent) ? -INFINITY : fmaf(mx, c, bl);
-
-      // ---- lazy rescale of the running state
-      const bool need = m_blk > m_run + kTau;
-      if (__any(need)) {
-        const float m_new = need ? m_blk : m_run;
-        const float alpha = exp2_approx(m_run - m_new);
-        l_run *= alpha;
+      m_blk[qs] = (a0 == sent) ? -INFINITY : fmaf(a0, c, bl);
+      need_any |= m_blk[qs] > m_run[qs] + kTau;
+    }
+    if (__any(need_any)) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-        m_run = m_new;
+      for (int qs = 0; qs < QS; ++qs) {
+        const bool need = m_blk[qs] > m_run[qs] + kTau;
+        const float m_new = need ? m_blk[qs] : m_run[qs];
+        const float alpha = exp2_approx(m_run[qs] - m_new);
+        l_run[qs] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) o[dt][qs] *= alpha;
+        m_run[qs] = m_new;
       }
-      const float kc = bl - ((m_run == -INFINITY) ? 0.f : m_run);
+    }
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) kc[qs] = bl - ((m_run[qs] == -INFINITY) ? 0.f : m_run[qs]);
+  };
 
-      // ---- P = exp2(c*S + bias - m), packed as the B operand of O^T += V^T P^T
-      u32x4_t pb[4];
+  // ---- P = exp2(c*S + bias - m) as the B operand of O^T += V^T P^T.  Masked
+  // scores are +-inf, so c*S is -inf and P is 0 (c is never 0: the host
+  // passes the smallest normal float for a zero scale).  The row sum adds
+  // the rounded P values the product uses.
+  auto exp_pv = [&](int buf, f32x16_t (&s)[2][QS], const float (&kc)[QS]) {
+    u32x4_t pb[4][QS];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
       float lsum = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -229,58 +286,128 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(Fwd16Params p) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int r = 8 * t + e;
-          float p0 = exp2_approx(fmaf(s[T][r], c, kc));
-          float p1 = exp2_approx(fmaf(s[T][r + 1], c, kc));
-          if (need_mask) {
-            p0 = (mbits >> (16 * T + r)) & 1u ? 0.f : p0;
-            p1 = (mbits >> (16 * T + r + 1)) & 1u ? 0.f : p1;
-          }
-          lsum += p0 + p1;
-          pb[kk][e >> 1] = pack2<BF16>(p0, p1);
+          const float p0 = exp2_approx(fmaf(s[T][qs][r], c, kc[qs]));
+          const float p1 = exp2_approx(fmaf(s[T][qs][r + 1], c, kc[qs]));
+          const uint32_t pk = pack2<BF16>(p0, p1);
+          lsum = sum2_acc<BF16>(pk, lsum);
+          pb[kk][qs][e >> 1] = pk;
         }
       }
-      l_run += lsum;
-
-      // ---- O^T += V^T P^T; V^T via transposing reads of the row-major tile
+      l_run[qs] += lsum;
+    }
+    const uint16_t* Vs = vbase_lds + buf * kVTile + vkey * kVRow + vcol;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const uint16_t* vp = Vs + (16 * kk + vkey) * kRow + 32 * dt + vcol;
-          const u32x2_t lo = lds_read_tr16(vp);
-          const u32x2_t hi = lds_read_tr16(vp + 8 * kRow);
-          const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-          o[dt] = mfma32x32x16<BF16>(a, pb[kk], o[dt]);
-        }
+      for (int dt = 0; dt < kDT; ++dt) {
+        const uint16_t* vp = Vs + 16 * kk * kVRow + 32 * dt;
+        const u32x2_t lo = lds_read_tr16(vp);
+        const u32x2_t hi = lds_read_tr16(vp + 8 * kVRow);
+        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) o[dt][qs] = mfma32x32x16<BF16>(a, pb[kk][qs], o[dt][qs]);
       }
     }
-    if (j + 1 < nkb) store_tile(buf ^ 1);
+  };
+
+  if constexpr (!PIPE) {
+    // ---- block j+1 loads while block j computes
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
     __syncthreads();
+    f32x16_t sc[2][QS];
+    for (int j = 0; j < nkb; ++j) {
+      const bool more = j + 1 < nkb;
+      if (more) {
+        load_k(j + 1);
+        load_v(j + 1);
+      }
+      if (wave_has_rows && j <= wave_last) {
+        qk(j & 1, sc);
+        if (needs_mask(j)) apply_mask(j, sc);
+        float kc[QS];
+        block_max(j, sc, kc);
+        exp_pv(j & 1, sc, kc);
+      }
+      if (more) {
+        store_k((j + 1) & 1);
+        store_v((j + 1) & 1);
+      }
+      __syncthreads();
+    }
+  } else {
+    // ---- pipelined: in iteration j, S of block j+1 is computed next to the
+    // softmax and P V of block j.  K of block j+2 and V of block j+1 load
+    // meanwhile; K buffers rotate over 3, V over 2.  A buffer is overwritten
+    // only after the barrier that follows its last read.
+    load_k(0);
+    store_k(0);
+    if (nkb > 1) {
+      load_k(1);
+      store_k(1);
+    }
+    load_v(0);
+    store_v(0);
+    __syncthreads();
+    f32x16_t sa[2][QS], sb[2][QS];
+    if (wave_has_rows) qk(0, sa);
+    auto step = [&](int j, f32x16_t (&s_cur)[2][QS], f32x16_t (&s_nxt)[2][QS]) {
+      const bool kmore = j + 2 < nkb, vmore = j + 1 < nkb;
+      if (kmore) load_k(j + 2);
+      if (vmore) load_v(j + 1);
+      const bool act = wave_has_rows && j <= wave_last;
+      if (act && needs_mask(j)) apply_mask(j, s_cur);
+      if (wave_has_rows && j + 1 <= wave_last) qk((j + 1) % kKbuf, s_nxt);
+      if (act) {
+        float kc[QS];
+        block_max(j, s_cur, kc);
+        exp_pv(j % kVbuf, s_cur, kc);
+      }
+      if (kmore) store_k((j + 2) % kKbuf);
+      if (vmore) store_v((j + 1) % kVbuf);
+      __syncthreads();
+    };
+    int j = 0;
+    for (; j + 1 < nkb; j += 2) {
+      step(j, sa, sb);
+      step(j + 1, sb, sa);
+    }
+    if (j < nkb) step(j, sa, sb);
   }
 
   // ---- epilogue: normalise, LSE, stage through LDS, coalesced stores
-  const float l_tot = xor32_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (p.lse != nullptr && hf == 0 && qi < N)
-    p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  float inv[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const float l_tot = xor32_sum(l_run[qs]);
+    inv[qs] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int qi = qw0 + 32 * qs + l32;
+    if (p.lse != nullptr && hf == 0 && qi < N)
+      p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
 
   if (p.out_f32) {
     constexpr int kSt = D + 4;  // floats per staged row
-    float* st = reinterpret_cast<float*>(smem) + wave * 32 * kSt;
+    float* st = reinterpret_cast<float*>(smem) + wave * kWQ * kSt;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hf;
-        f32x4_t w = {o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
-                     o[dt][4 * g + 3] * inv};
-        *(f32x4_t*)(st + l32 * kSt + d) = w;
-      }
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * hf;
+          const float iv = inv[qs];
+          f32x4_t w = {o[dt][qs][4 * g] * iv, o[dt][qs][4 * g + 1] * iv, o[dt][qs][4 * g + 2] * iv,
+                       o[dt][qs][4 * g + 3] * iv};
+          *(f32x4_t*)(st + (32 * qs + l32) * kSt + d) = w;
+        }
     __syncthreads();
     float* O = reinterpret_cast<float*>(p.o) + head;
     constexpr int kCh = D / 4;  // 16-byte chunks per row
 #pragma unroll
-    for (int it = 0; it < 32 * kCh / 64; ++it) {
+    for (int it = 0; it < kWQ * kCh / 64; ++it) {
       const int idx = lane + 64 * it;
       const int row = idx / kCh, ch = idx % kCh;
       const int q = qw0 + row;
@@ -288,21 +415,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(Fwd16Params p) {
     }
   } else {
     constexpr int kSt = D + 8;  // 16-bit elements per staged row
-    uint16_t* st = smem + wave * 32 * kSt;
+    uint16_t* st = smem + wave * kWQ * kSt;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hf;
-        u32x2_t w = {pack2<BF16>(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
-                     pack2<BF16>(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
-        *(u32x2_t*)(st + l32 * kSt + d) = w;
-      }
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * hf;
+          const float iv = inv[qs];
+          u32x2_t w = {pack2<BF16>(o[dt][qs][4 * g] * iv, o[dt][qs][4 * g + 1] * iv),
+                       pack2<BF16>(o[dt][qs][4 * g + 2] * iv, o[dt][qs][4 * g + 3] * iv)};
+          *(u32x2_t*)(st + (32 * qs + l32) * kSt + d) = w;
+        }
     __syncthreads();
     uint16_t* O = reinterpret_cast<uint16_t*>(p.o) + head;
     constexpr int kCh = D / 8;
 #pragma unroll
-    for (int it = 0; it < 32 * kCh / 64; ++it) {
+    for (int it = 0; it < kWQ * kCh / 64; ++it) {
       const int idx = lane + 64 * it;
       const int row = idx / kCh, ch = idx % kCh;
       const int q = qw0 + row;
@@ -311,8 +441,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(Fwd16Params p) {
   }
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, int QS, int NW, bool PIPE>
 hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
+  using TL = Tiling<QS, NW, PIPE>;
   Fwd16Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -321,18 +452,50 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.bias = a.bias;
   p.N = a.N;
-  p.nq = (a.N + kBM - 1) / kBM;
+  p.nq = (a.N + TL::kBM - 1) / TL::kBM;
   p.nb = (a.N + 63) / 64;
   p.ntiles = a.B * a.H * p.nq;
+  // c = scale*log2(e).  A zero scale is passed as the smallest normal float:
+  // masked scores are +-inf and inf*0 would be NaN, while any finite score
+  // below 2^100 in magnitude times 2^-126 is below an ulp of the exponent.
   p.c = (float)((double)a.scale * 1.4426950408889634);
+  if (p.c == 0.f) p.c = 1.17549435e-38f;
   p.out_f32 = a.out_kind == kOutF32;
-  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL>), dim3(p.ntiles), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW, PIPE>), dim3(p.ntiles), dim3(TL::kThreads), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+// Tiling per head dimension.  ATTN_FWD16_TILING selects another variant, to
+// compare them on the GPU.  Measured on MI355X (TFLOPS):
+//   d = 128 (prefill 4x32x4096 / long-context 1x32x32768, causal):
+//     QS1 NW8 (default) 688 / 1076; QS1 NW4 688 / 1003; QS1 NW8 PIPE 653 /
+//     1030; QS1 NW4 PIPE 497 / 634 (LDS allows one workgroup per CU).
+//   d = 64 (DiT-gated 2x24x16384, bias): QS2 NW4 (default) 923; QS1 NW4 854;
+//     QS1 NW8 PIPE 780; QS2 NW4 PIPE 583 (spills).
+int tiling_override() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_FWD16_TILING");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
 }
 
 template <bool BF16, bool CAUSAL>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  return a.d == 64 ? launch_impl<64, BF16, CAUSAL>(a, stream) : launch_impl<128, BF16, CAUSAL>(a, stream);
+  const int t = tiling_override();
+  if (a.d == 64) {
+    switch (t) {
+      case 1: return launch_impl<64, BF16, CAUSAL, 1, 4, false>(a, stream);
+      case 2: return launch_impl<64, BF16, CAUSAL, 1, 8, true>(a, stream);
+      default: return launch_impl<64, BF16, CAUSAL, 2, 4, false>(a, stream);
+    }
+  }
+  switch (t) {
+    case 1: return launch_impl<128, BF16, CAUSAL, 1, 4, false>(a, stream);
+    case 2: return launch_impl<128, BF16, CAUSAL, 1, 8, true>(a, stream);
+    default: return launch_impl<128, BF16, CAUSAL, 1, 8, false>(a, stream);
+  }
 }
 
 }  // namespace

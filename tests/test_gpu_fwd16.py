@@ -137,7 +137,7 @@ def test_no_quadratic_memory():
     torch.cuda.synchronize()
     grown = torch.cuda.max_memory_allocated() - base
     assert grown <= o.numel() * 2 + lse.numel() * 4 + (1 << 20), grown  # never B*H*N^2
-    assert grown < B * H * N * N // 64
+    assert grown < B * H * N * N * 2 // 64  # a bf16 score matrix would be B*H*N^2*2 bytes
 
 
 def test_fully_masked_rows_and_minus_inf_bias():

@@ -25,7 +25,7 @@ import os
 import torch
 
 __all__ = ["fwd", "sage8_prep", "fwd_sage8", "sageattn", "AttnError", "Sage8Prepared",
-           "lib", "LIB_PATH", "status_str"]
+           "sage8_workspace_views", "lib", "LIB_PATH", "status_str"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.attn_sage8_workspace_size.restype = sz
     L.attn_k_smooth_quant.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     L.attn_k_smooth_quant.restype = i
+    L.attn_sage8_workspace_layout.argtypes = [i, i, i, i, ctypes.POINTER(sz), i]
+    L.attn_sage8_workspace_layout.restype = i
     L.attn_fwd_sage8.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
     L.attn_fwd_sage8.restype = i
     L.attn_status_str.argtypes = [i]
@@ -179,3 +181,39 @@ def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, retur
     prep = sage8_prep(q, k, v)
     return fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
                      return_lse=return_lse)
+
+
+def sage8_workspace_views(prep: Sage8Prepared) -> dict:
+    """Views of the prepared data inside the workspace (for inspection and
+    tests): qq, kq int8 [B,H,Np,d]; sq, sk fp32 [B,H,nblk]; sv, kmean fp32
+    [B,H,d]; vq uint8 e4m3 codes in the library's layout [B,H,nblk,d,64];
+    vq_logical uint8 [B,H,Np,d] (the same codes in token order)."""
+    B, H, N, d = prep.shape
+    vals = (ctypes.c_size_t * 9)()
+    if lib().attn_sage8_workspace_layout(B, H, N, d, vals, 9) != 9:
+        raise AttnError(2, "attn_sage8_workspace_layout")
+    off_qq, off_kq, off_vq, off_sq, off_sk, off_sv, off_km, np_, nblk = (int(x) for x in vals)
+    ws = prep.workspace
+
+    def region(off, count, dtype):
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + nbytes].view(dtype)
+
+    out = dict(
+        qq=region(off_qq, B * H * np_ * d, torch.int8).view(B, H, np_, d),
+        kq=region(off_kq, B * H * np_ * d, torch.int8).view(B, H, np_, d),
+        vq=region(off_vq, B * H * np_ * d, torch.uint8).view(B, H, nblk, d, 64),
+        sq=region(off_sq, B * H * nblk, torch.float32).view(B, H, nblk),
+        sk=region(off_sk, B * H * nblk, torch.float32).view(B, H, nblk),
+        sv=region(off_sv, B * H * d, torch.float32).view(B, H, d),
+        kmean=region(off_km, B * H * d, torch.float32).view(B, H, d),
+    )
+    # byte 32h + 16T + 4g + u of a row holds key 32T + 8g + 4h + u of the block
+    pos = torch.empty(64, dtype=torch.long)
+    for key in range(64):
+        T, kin = key // 32, key % 32
+        h, g, u = (kin // 4) % 2, kin // 8, kin % 4
+        pos[key] = 32 * h + 16 * T + 4 * g + u
+    vq = out["vq"][..., pos.to(ws.device)]                      # [B,H,nblk,d,64 keys]
+    out["vq_logical"] = vq.permute(0, 1, 2, 4, 3).reshape(B, H, np_, d)
+    return out

@@ -97,6 +97,15 @@ size_t attn_sage8_workspace_size(int B, int H, int N, int d) {
   return attn::sage8_layout(B, H, N, d).total;
 }
 
+int attn_sage8_workspace_layout(int B, int H, int N, int d, size_t* out, int n) {
+  if (check_shape(B, H, N, d) != ATTN_OK || out == nullptr || n <= 0) return 0;
+  const attn::Sage8Layout L = attn::sage8_layout(B, H, N, d);
+  const size_t vals[9] = {L.qq, L.kq, L.vq, L.sq, L.sk, L.sv, L.kmean, (size_t)L.nblk * 64, (size_t)L.nblk};
+  const int m = n < 9 ? n : 9;
+  for (int i = 0; i < m; ++i) out[i] = vals[i];
+  return m;
+}
+
 attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
                                 int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
       for (int qs = 0; qs < QS; ++qs) {
         const bool need = m_blk[qs] > m_run[qs] + kTau;
         const float m_new = need ? m_blk[qs] : m_run[qs];
-        const float alpha = exp2_approx(m_run[qs] - m_new);
+        const float alpha = need ? exp2_approx(m_run[qs] - m_new) : 1.f;
         l_run[qs] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) o[dt][qs] *= alpha;

@@ -29,9 +29,9 @@ hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream);
 // 8-bit path.
 struct Sage8Layout {
   // byte offsets inside the workspace, each 256-byte aligned
-  size_t qq, kq, vq, sq, sk, sv, kmean, kpart, vpart;
+  size_t qq, kq, vq, sq, sk, sv, vinv, kmean, kpart, vpart;
   size_t total;
-  int nblk;    // ceil(N/64): per-64-row blocks of Q and K
+  int nblk;    // 64-row blocks of the token count padded to a multiple of 128
   int nchunk;  // token chunks of the column reductions
 };
 Sage8Layout sage8_layout(int B, int H, int N, int d);

@@ -1,17 +1,54 @@
-// attn_sage8.hip -- 8-bit path: workspace layout (kernels follow).
+// attn_sage8.hip -- the 8-bit (SageAttention-style) path on gfx950.
+//
+// Page 1 ("SageAttention", claim vs reality section): the first product
+// Q K^T runs on INT8 matrix units after K is mean-centred (softmax is
+// shift-invariant, so the centring changes no output), the softmax output P
+// lies in [0, 1] and goes to FP8 for the second product P V, and the two are
+// combined with a two-level accumulation.
+//
+// Preparation (HBM-bound, three kernels):
+//   colstats  per 256-token chunk of each (b,h): fp64 column sums of K and
+//             fp32 column absmax of V.
+//   finalize  per (b,h): kmean = (sum of chunk sums) / N rounded once to
+//             fp32; V scale = absmax/448 and its inverse 448/absmax (1 if 0).
+//   quant     per 64-row block: Q and K - kmean to INT8 with one fp32 scale
+//             per block (scale = absmax/127, code = rne(x * (127/absmax)),
+//             clamp +-127); V to e4m3 (code = e4m3_rne(v * inv)), written
+//             through LDS into the per-block transposed layout that the P V
+//             product reads.
+// Forward: S^T = Kq Qq^T on 32x32x32 INT8 MFMA (int32, exact), scaled by
+// sq*sk*scale*log2(e) per 64x64 block; online softmax in base 2 with a lazy
+// running maximum (raised only when a block maximum exceeds it by more than
+// kTau8 = 2); P^ = e4m3(448 * 2^(t - m - kTau8)) <= 448 becomes the B operand
+// of a 32x32x64 FP8 MFMA straight from the S^T registers; V^T comes from the
+// prepared tile.  Level one of the accumulation is the fp32 sum over the 64
+// keys of a block inside one matrix instruction, level two the fp32 running
+// output carried across blocks.  The V scales and 1/l are applied once.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
+#include <math.h>
+
 namespace attn {
 
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+namespace {
+
+constexpr int kQB = 64;        // rows per INT8 scale block (and keys per block)
+constexpr int kChunk = 256;    // tokens per column-statistics chunk
+constexpr float kTau8 = 2.0f;  // lazy-rescale threshold of the 8-bit path (log2 units)
+// log2(448) - kTau8: P^ = e4m3(2^(t - m + kPlog)) stays <= 448
+constexpr float kPlog = 6.807354922057604f;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
 
 Sage8Layout sage8_layout(int B, int H, int N, int d) {
   Sage8Layout L{};
   const size_t bh = (size_t)B * H;
   const size_t np = (size_t)((N + 127) / 128) * 128;  // tokens padded to whole 128-row tiles
-  L.nblk = (int)(np / 64);
-  L.nchunk = (N + 255) / 256;
+  L.nblk = (int)(np / kQB);
+  L.nchunk = (N + kChunk - 1) / kChunk;
   size_t off = 0;
   L.qq = off; off = align256(off + bh * np * d);
   L.kq = off; off = align256(off + bh * np * d);
@@ -19,6 +56,7 @@ Sage8Layout sage8_layout(int B, int H, int N, int d) {
   L.sq = off; off = align256(off + bh * L.nblk * sizeof(float));
   L.sk = off; off = align256(off + bh * L.nblk * sizeof(float));
   L.sv = off; off = align256(off + bh * d * sizeof(float));
+  L.vinv = off; off = align256(off + bh * d * sizeof(float));
   L.kmean = off; off = align256(off + bh * d * sizeof(float));
   L.kpart = off; off = align256(off + bh * (size_t)L.nchunk * d * sizeof(double));
   L.vpart = off; off = align256(off + bh * (size_t)L.nchunk * d * sizeof(float));
@@ -26,11 +64,539 @@ Sage8Layout sage8_layout(int B, int H, int N, int d) {
   return L;
 }
 
-hipError_t launch_sage8_prep(const void*, const void*, const void*, bool, int, int, int, int, void*,
-                             hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+// Position of key k (0..63 in its block) inside the lane order of the P^T
+// operand: the S^T accumulator gives lane half h the keys 32T + 8g + 4h + u
+// (register r = 4g + u of tile T); byte e = 16T + r of half h is the key at
+// position 32h + e.
+__device__ __forceinline__ int key_pos(int k) {
+  const int T = k >> 5, kin = k & 31;
+  const int h = (kin >> 2) & 1, g = kin >> 3, u = kin & 3;
+  return 32 * h + 16 * T + 4 * g + u;
 }
 
-hipError_t launch_fwd_sage8(const void*, const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+template <bool BF16>
+__device__ __forceinline__ float in_to_f32(uint16_t x) {
+  if constexpr (BF16) {
+    return __uint_as_float((uint32_t)x << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+}
+
+// ---- colstats: grid (nchunk, B*H), 256 threads --------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                      int N, double* __restrict__ kpart,
+                                                      float* __restrict__ vpart, int nchunk) {
+  constexpr int kCpr = D / 8;          // 16-byte chunks per row
+  constexpr int kRows = 256 / kCpr;    // rows per pass
+  __shared__ double ssum[kRows][D];
+  __shared__ float smax[kRows][D];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
+  const size_t head = (size_t)bh * N * D;
+  double acc[8];
+  float mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] = 0.0;
+    mx[e] = 0.f;
+  }
+  const int n0 = chunk * kChunk;
+  for (int r = rg; r < kChunk; r += kRows) {
+    const int n = n0 + r;
+    if (n >= N) break;
+    const u32x4_t kx = *(const u32x4_t*)(k + head + (size_t)n * D + ch * 8);
+    const u32x4_t vx = *(const u32x4_t*)(v + head + (size_t)n * D + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t kb = (uint16_t)(kx[e >> 1] >> (16 * (e & 1)));
+      const uint16_t vb = (uint16_t)(vx[e >> 1] >> (16 * (e & 1)));
+      acc[e] += (double)in_to_f32<BF16>(kb);
+      mx[e] = fmaxf(mx[e], fabsf(in_to_f32<BF16>(vb)));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ssum[rg][ch * 8 + e] = acc[e];
+    smax[rg][ch * 8 + e] = mx[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double s = 0.0;
+    float m = 0.f;
+    for (int g = 0; g < kRows; ++g) {
+      s += ssum[g][tid];
+      m = fmaxf(m, smax[g][tid]);
+    }
+    kpart[((size_t)bh * nchunk + chunk) * D + tid] = s;
+    vpart[((size_t)bh * nchunk + chunk) * D + tid] = m;
+  }
+}
+
+// ---- finalize: grid B*H, D threads --------------------------------------
+template <int D>
+__global__ __launch_bounds__(D) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
+                                                    int nchunk, int N, float* __restrict__ kmean,
+                                                    float* __restrict__ sv, float* __restrict__ vinv) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  double s = 0.0;
+  float m = 0.f;
+  for (int ch = 0; ch < nchunk; ++ch) {
+    s += kpart[((size_t)bh * nchunk + ch) * D + c];
+    m = fmaxf(m, vpart[((size_t)bh * nchunk + ch) * D + c]);
+  }
+  kmean[(size_t)bh * D + c] = (float)(s / (double)N);
+  sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+  vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
+}
+
+// Block-wide max of a non-negative float over 256 threads (4 waves).
+__device__ __forceinline__ float block_max256(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ uint32_t q8(float y, float inv) {
+  float r = rintf(y * inv);
+  r = fminf(fmaxf(r, -127.f), 127.f);
+  return (uint32_t)((int)r & 0xFF);
+}
+
+// ---- quant: grid (nblk, B*H), 256 threads --------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v, int N, int np, int nblk,
+                                                   const float* __restrict__ kmean, const float* __restrict__ vinv,
+                                                   int8_t* __restrict__ qq, int8_t* __restrict__ kq,
+                                                   uint8_t* __restrict__ vq, float* __restrict__ sq,
+                                                   float* __restrict__ sk) {
+  constexpr int kCpr = D / 8;
+  constexpr int kRows = 256 / kCpr;      // rows per pass
+  constexpr int kPass = kQB / kRows;     // passes over the 64-row block
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[D][kQB];  // transposed, permuted V codes
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
+  const size_t head = (size_t)bh * N * D;
+  const size_t headp = (size_t)bh * np * D;
+  const int n0 = blk * kQB;
+
+  float xq[kPass][8], xk[kPass][8];
+  float km[8], vi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    km[e] = kmean[(size_t)bh * D + ch * 8 + e];
+    vi[e] = vinv[(size_t)bh * D + ch * 8 + e];
+  }
+  float aq = 0.f, ak = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPass; ++i) {
+    const int r = rg + i * kRows, n = n0 + r;
+    u32x4_t qx = {0u, 0u, 0u, 0u}, kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (n < N) {
+      qx = *(const u32x4_t*)(q + head + (size_t)n * D + ch * 8);
+      kx = *(const u32x4_t*)(k + head + (size_t)n * D + ch * 8);
+      vx = *(const u32x4_t*)(v + head + (size_t)n * D + ch * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t qb = (uint16_t)(qx[e >> 1] >> (16 * (e & 1)));
+      const uint16_t kb = (uint16_t)(kx[e >> 1] >> (16 * (e & 1)));
+      const uint16_t vb = (uint16_t)(vx[e >> 1] >> (16 * (e & 1)));
+      xq[i][e] = in_to_f32<BF16>(qb);
+      xk[i][e] = n < N ? in_to_f32<BF16>(kb) - km[e] : 0.f;
+      aq = fmaxf(aq, fabsf(xq[i][e]));
+      ak = fmaxf(ak, fabsf(xk[i][e]));
+      // V code, byte-scattered into the transposed tile
+      const float t = in_to_f32<BF16>(vb) * vi[e];
+      const uint32_t code = n < N ? (__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false) & 0xFF) : 0u;
+      vt[ch * 8 + e][key_pos(r)] = (uint8_t)code;
+    }
+  }
+  aq = block_max256(aq, red);
+  ak = block_max256(ak, red);
+  const float inv_q = aq > 0.f ? __fdiv_rn(127.0f, aq) : 1.0f;
+  const float inv_k = ak > 0.f ? __fdiv_rn(127.0f, ak) : 1.0f;
+  if (tid == 0) {
+    sq[(size_t)bh * nblk + blk] = aq > 0.f ? __fdiv_rn(aq, 127.0f) : 1.0f;
+    sk[(size_t)bh * nblk + blk] = ak > 0.f ? __fdiv_rn(ak, 127.0f) : 1.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kPass; ++i) {
+    const int r = rg + i * kRows, n = n0 + r;
+    u32x2_t wq, wk;
+    wq[0] = q8(xq[i][0], inv_q) | q8(xq[i][1], inv_q) << 8 | q8(xq[i][2], inv_q) << 16 | q8(xq[i][3], inv_q) << 24;
+    wq[1] = q8(xq[i][4], inv_q) | q8(xq[i][5], inv_q) << 8 | q8(xq[i][6], inv_q) << 16 | q8(xq[i][7], inv_q) << 24;
+    wk[0] = q8(xk[i][0], inv_k) | q8(xk[i][1], inv_k) << 8 | q8(xk[i][2], inv_k) << 16 | q8(xk[i][3], inv_k) << 24;
+    wk[1] = q8(xk[i][4], inv_k) | q8(xk[i][5], inv_k) << 8 | q8(xk[i][6], inv_k) << 16 | q8(xk[i][7], inv_k) << 24;
+    *(u32x2_t*)(qq + headp + (size_t)n * D + ch * 8) = wq;
+    *(u32x2_t*)(kq + headp + (size_t)n * D + ch * 8) = wk;
+  }
+  __syncthreads();
+  // V tile: D rows of 64 bytes, contiguous per block -> 16-byte stores
+  uint8_t* vdst = vq + headp + (size_t)blk * kQB * D;
+  for (int idx = tid; idx < D * kQB / 16; idx += 256) {
+    const int row = idx / (kQB / 16), c16 = idx % (kQB / 16);
+    *(u32x4_t*)(vdst + row * kQB + c16 * 16) = *(const u32x4_t*)(&vt[row][c16 * 16]);
+  }
+}
+
+template <int D, bool BF16>
+hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, int N, void* ws,
+                     hipStream_t stream) {
+  const Sage8Layout L = sage8_layout(B, H, N, D);
+  char* w = static_cast<char*>(ws);
+  const int bh = B * H;
+  const int np = L.nblk * kQB;
+  hipLaunchKernelGGL((sage8_colstats<D, BF16>), dim3(L.nchunk, bh), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N,
+                     reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk);
+  hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3(D), 0, stream,
+                     reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
+                     L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
+                     reinterpret_cast<float*>(w + L.vinv));
+  hipLaunchKernelGGL((sage8_quant<D, BF16>), dim3(L.nblk, bh), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), N, np, L.nblk,
+                     reinterpret_cast<const float*>(w + L.kmean), reinterpret_cast<const float*>(w + L.vinv),
+                     reinterpret_cast<int8_t*>(w + L.qq), reinterpret_cast<int8_t*>(w + L.kq),
+                     reinterpret_cast<uint8_t*>(w + L.vq), reinterpret_cast<float*>(w + L.sq),
+                     reinterpret_cast<float*>(w + L.sk));
+  return hipGetLastError();
+}
+
+// =========================================================================
+// Forward
+// =========================================================================
+
+struct Fwd8Params {
+  const int8_t* qq;
+  const int8_t* kq;
+  const uint8_t* vq;
+  const float* sq;
+  const float* sk;
+  const float* sv;
+  const float* kmean;
+  void* o;
+  float* lse;
+  const float* bias;
+  int N, np, nblk;
+  int nq;      // query tiles per head
+  int nb;      // ceil(N/64), bias blocks per side
+  int ntiles;  // B*H*nq
+  float c;     // scale * log2(e), never 0
+  int out_kind;
+};
+
+constexpr int kNW8 = 4;                // waves per workgroup
+constexpr int kBM8 = 32 * kNW8;        // queries per workgroup
+constexpr int kThreads8 = 64 * kNW8;
+
+template <int D>
+struct Fwd8Smem {
+  // K tile: 64 keys x D bytes, rows padded by 16 bytes (16-byte operand reads
+  // of 16 consecutive rows on distinct banks).  V tile: D rows of 64 bytes
+  // (the block's keys in operand order), padded by 16 bytes.
+  static constexpr int kKRow = D + 16;
+  static constexpr int kVRow = kQB + 16;
+  static constexpr int kKTile = kQB * kKRow;
+  static constexpr int kVTile = D * kVRow;
+  static constexpr int kLoop = 2 * (kKTile + kVTile);
+  static constexpr int kStage = kNW8 * 32 * (D + 4) * 4;  // fp32 output staging, bytes
+  static constexpr int kBytes = kLoop > kStage ? kLoop : kStage;
+};
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
+  using S = Fwd8Smem<D>;
+  constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
+  constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
+  constexpr int kDT = D / 32;  // 32-row tiles of O^T
+  constexpr int kKS = D / 32;  // k-steps of the INT8 product (32 per step)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::kBytes];
+  uint8_t* const kl = smem;               // 2 K tiles
+  uint8_t* const vl = smem + 2 * kKTile;  // 2 V tiles
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int tile = xcd_remap(blockIdx.x, p.ntiles);
+  const int bh = tile / p.nq;
+  int qt = tile - bh * p.nq;
+  if (CAUSAL) qt = p.nq - 1 - qt;
+  const int N = p.N;
+  const int q0 = qt * kBM8;
+  const int qw0 = q0 + wave * 32;
+  const size_t headp = (size_t)bh * p.np * D;
+  const int8_t* __restrict__ Qq = p.qq + headp;
+  const int8_t* __restrict__ Kq = p.kq + headp;
+  const uint8_t* __restrict__ Vq = p.vq + headp;
+
+  // Qq^T as the B operand: lane holds Qq[qw0 + l32][32kk + 16hf .. +15]
+  // (rows up to the padded length are valid zero codes).
+  u32x4_t qf[kKS];
+#pragma unroll
+  for (int kk = 0; kk < kKS; ++kk) qf[kk] = *(const u32x4_t*)(Qq + (size_t)(qw0 + l32) * D + 32 * kk + 16 * hf);
+  const float sqw = p.sq[(size_t)bh * p.nblk + qw0 / kQB];
+
+  const int kend = CAUSAL ? min(N, q0 + kBM8) : N;
+  const int nkb = (kend + kQB - 1) / kQB;
+  const int wave_last = CAUSAL ? min(nkb - 1, qw0 / kQB) : nkb - 1;
+  const bool wave_has_rows = qw0 < N;
+
+  // loader: K tile 64*D bytes and V tile D*64 bytes, 16-byte chunks
+  constexpr int kNld = kQB * D / 16 / kThreads8;
+  u32x4_t kst[kNld], vst[kNld];
+  auto load_kv = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < kNld; ++i) {
+      const int idx = tid + i * kThreads8;
+      kst[i] = *(const u32x4_t*)(Kq + (size_t)kb * kQB * D + idx * 16);
+      vst[i] = *(const u32x4_t*)(Vq + (size_t)kb * kQB * D + idx * 16);
+    }
+  };
+  auto store_kv = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kNld; ++i) {
+      const int idx = tid + i * kThreads8;
+      const int kr = idx / (D / 16), kc = idx % (D / 16);
+      *(u32x4_t*)(kl + buf * kKTile + kr * kKRow + kc * 16) = kst[i];
+      const int vr = idx / (kQB / 16), vc = idx % (kQB / 16);
+      *(u32x4_t*)(vl + buf * kVTile + vr * kVRow + vc * 16) = vst[i];
+    }
+  };
+
+  f32x16_t o[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = p.c;
+  const bool pos = c > 0.f;
+  const float sent = pos ? -INFINITY : INFINITY;
+  const int qb64 = min(qw0 / kQB, p.nb - 1);
+  const float* bias_row = p.bias ? p.bias + ((size_t)bh * p.nb + (size_t)qb64) * p.nb : nullptr;
+  const float* skrow = p.sk + (size_t)bh * p.nblk;
+
+  load_kv(0);
+  store_kv(0);
+  __syncthreads();
+  for (int j = 0; j < nkb; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < nkb;
+    if (more) load_kv(j + 1);
+    if (wave_has_rows && j <= wave_last) {
+      // ---- S^T = Kq Qq^T, exact int32
+      const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
+      i32x16_t si[2] = {i32x16_t{}, i32x16_t{}};
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk)
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+          const u32x4_t a = *(const u32x4_t*)(Ks + 32 * T * kKRow + 32 * kk);
+          si[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
+                                                        __builtin_bit_cast(i32x4_t, qf[kk]), si[T], 0, 0, 0);
+        }
+      // dequantised, base 2: t = S_int * f + bias*log2(e)
+      const float f = (sqw * skrow[j]) * c;
+      f32x16_t s[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[T][r] = (float)si[T][r];
+      if ((CAUSAL && j == wave_last) || (j + 1) * kQB > N) {
+        const int kb0 = j * kQB, qi = qw0 + l32;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + 32 * T + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool m = (CAUSAL && key > qi) || key >= N;
+            s[T][r] = m ? sent : s[T][r];
+          }
+      }
+      const float bl = bias_row ? bias_row[j] * kLog2e : 0.f;
+      float a0;
+      if (pos) {
+        a0 = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) a0 = fmaxf(a0, fmaxf(s[0][r], s[1][r]));
+        a0 = xor32_max(a0);
+      } else {
+        a0 = fminf(s[0][0], s[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) a0 = fminf(a0, fminf(s[0][r], s[1][r]));
+        a0 = xor32_min(a0);
+      }
+      const float m_blk = (a0 == sent) ? -INFINITY : fmaf(a0, f, bl);
+      const bool need = m_blk > m_run + kTau8;
+      if (__any(need)) {
+        const float m_new = need ? m_blk : m_run;
+        // rows that keep their maximum keep alpha = 1 (also a row still at -inf)
+        const float alpha = need ? exp2_approx(m_run - m_new) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float kc = (bl - ((m_run == -INFINITY) ? 0.f : m_run)) + kPlog;
+      // ---- P^ in e4m3 as the B operand (byte e = 16T + r), row sum of the
+      // unquantised values
+      u32x4_t pl, ph;
+      float lsum = 0.f;
+      float pv[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        pv[e] = exp2_approx(fmaf(s[e >> 4][e & 15], f, kc));
+        lsum += pv[e];
+      }
+      l_run += lsum;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pl[w] = pack_fp8x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
+        ph[w] = pack_fp8x4(pv[16 + 4 * w], pv[16 + 4 * w + 1], pv[16 + 4 * w + 2], pv[16 + 4 * w + 3]);
+      }
+      const i32x8_t bop = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3],
+                           (int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3]};
+      // ---- O^T += Vq^T P^T over the 64 keys (one FP8 instruction per d tile)
+      const uint8_t* Vs = vl + buf * kVTile + l32 * kVRow + 32 * hf;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+        const u32x4_t a0v = *(const u32x4_t*)(Vs + 32 * dt * kVRow);
+        const u32x4_t a1v = *(const u32x4_t*)(Vs + 32 * dt * kVRow + 16);
+        const i32x8_t aop = {(int)a0v[0], (int)a0v[1], (int)a0v[2], (int)a0v[3],
+                             (int)a1v[0], (int)a1v[1], (int)a1v[2], (int)a1v[3]};
+        o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, o[dt], 0, 0, 0, 0, 0, 0);
+      }
+    }
+    if (more) store_kv((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc * sv[d] / l; LSE = (m + log2 l - kPlog) ln 2 plus
+  // the shift scale * sq * (Qq . kmean) that the centring of K removed from
+  // every score of the row (the output does not depend on it, the LSE does)
+  const float l_tot = xor32_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int qi = qw0 + l32;
+  if (p.lse != nullptr) {
+    const float* kmh = p.kmean + (size_t)bh * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int code = (int)(int8_t)(qf[kk][e >> 2] >> (8 * (e & 3)));
+        dot = fmaf((float)code, kmh[32 * kk + 16 * hf + e], dot);
+      }
+    dot = xor32_sum(dot);
+    if (hf == 0 && qi < N)
+      p.lse[(size_t)bh * N + qi] =
+          l_tot > 0.f ? (m_run + __log2f(l_tot) - kPlog + c * (sqw * dot)) * kLn2 : -INFINITY;
+  }
+  const float* svh = p.sv + (size_t)bh * D;
+  constexpr int kSt = D + 4;
+  float* st = reinterpret_cast<float*>(smem) + wave * 32 * kSt;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * hf;
+      const f32x4_t svv = *(const f32x4_t*)(svh + d);
+      f32x4_t w = {o[dt][4 * g] * svv[0] * inv, o[dt][4 * g + 1] * svv[1] * inv,
+                   o[dt][4 * g + 2] * svv[2] * inv, o[dt][4 * g + 3] * svv[3] * inv};
+      *(f32x4_t*)(st + l32 * kSt + d) = w;
+    }
+  __syncthreads();
+  const size_t head = (size_t)bh * N * D;
+  if (p.out_kind == kOutF32) {
+    float* O = reinterpret_cast<float*>(p.o) + head;
+    constexpr int kCh = D / 4;
+#pragma unroll
+    for (int it = 0; it < 32 * kCh / 64; ++it) {
+      const int idx = lane + 64 * it, row = idx / kCh, ch = idx % kCh, q = qw0 + row;
+      if (q < N) *(f32x4_t*)(O + (size_t)q * D + 4 * ch) = *(const f32x4_t*)(st + row * kSt + 4 * ch);
+    }
+  } else {
+    uint16_t* O = reinterpret_cast<uint16_t*>(p.o) + head;
+    const bool bf = p.out_kind == kOutBF16;
+    constexpr int kCh = D / 8;
+#pragma unroll
+    for (int it = 0; it < 32 * kCh / 64; ++it) {
+      const int idx = lane + 64 * it, row = idx / kCh, ch = idx % kCh, q = qw0 + row;
+      if (q < N) {
+        const f32x4_t a = *(const f32x4_t*)(st + row * kSt + 8 * ch);
+        const f32x4_t b = *(const f32x4_t*)(st + row * kSt + 8 * ch + 4);
+        u32x4_t w;
+        if (bf) {
+          w = u32x4_t{pack2<true>(a[0], a[1]), pack2<true>(a[2], a[3]), pack2<true>(b[0], b[1]),
+                      pack2<true>(b[2], b[3])};
+        } else {
+          w = u32x4_t{pack2<false>(a[0], a[1]), pack2<false>(a[2], a[3]), pack2<false>(b[0], b[1]),
+                      pack2<false>(b[2], b[3])};
+        }
+        *(u32x4_t*)(O + (size_t)q * D + 8 * ch) = w;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  const Sage8Layout L = sage8_layout(a.B, a.H, a.N, D);
+  const char* w = static_cast<const char*>(ws);
+  Fwd8Params p;
+  p.qq = reinterpret_cast<const int8_t*>(w + L.qq);
+  p.kq = reinterpret_cast<const int8_t*>(w + L.kq);
+  p.vq = reinterpret_cast<const uint8_t*>(w + L.vq);
+  p.sq = reinterpret_cast<const float*>(w + L.sq);
+  p.sk = reinterpret_cast<const float*>(w + L.sk);
+  p.sv = reinterpret_cast<const float*>(w + L.sv);
+  p.kmean = reinterpret_cast<const float*>(w + L.kmean);
+  p.o = a.o;
+  p.lse = a.lse;
+  p.bias = a.bias;
+  p.N = a.N;
+  p.nblk = L.nblk;
+  p.np = L.nblk * kQB;
+  p.nq = (a.N + kBM8 - 1) / kBM8;
+  p.nb = (a.N + 63) / 64;
+  p.ntiles = a.B * a.H * p.nq;
+  p.c = (float)((double)a.scale * 1.4426950408889634);
+  if (p.c == 0.f) p.c = 1.17549435e-38f;
+  p.out_kind = a.out_kind;
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(p.ntiles), dim3(kThreads8), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
+                             void* ws, hipStream_t stream) {
+  if (d == 64) return bf16 ? prep_impl<64, true>(q, k, v, B, H, N, ws, stream)
+                           : prep_impl<64, false>(q, k, v, B, H, N, ws, stream);
+  return bf16 ? prep_impl<128, true>(q, k, v, B, H, N, ws, stream)
+              : prep_impl<128, false>(q, k, v, B, H, N, ws, stream);
+}
+
+hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 64) return a.causal ? fwd8_impl<64, true>(ws, a, stream) : fwd8_impl<64, false>(ws, a, stream);
+  return a.causal ? fwd8_impl<128, true>(ws, a, stream) : fwd8_impl<128, false>(ws, a, stream);
+}
 
 }  // namespace attn

@@ -103,6 +103,18 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 size_t attn_sage8_workspace_size(int B, int H, int N, int d);
 
 /*
+ * attn_sage8_workspace_layout -- where the prepared data sit inside the
+ * workspace, for inspection and tests.  Writes up to n values to out, in
+ * this order: byte offsets of Qq, Kq, Vq, sQ, sK, sV, kmean, then the padded
+ * token count Np and the number of 64-row blocks nblk.  Layouts: Qq, Kq int8
+ * [B,H,Np,d]; sQ, sK fp32 [B,H,nblk]; sV, kmean fp32 [B,H,d]; Vq e4m3
+ * [B,H,nblk,d,64] where byte 32h + 16T + 4g + u of a row holds key
+ * 32T + 8g + 4h + u of the block (the operand order of the P V product).
+ * Returns the number of values written, 0 for an invalid shape.
+ */
+int attn_sage8_workspace_layout(int B, int H, int N, int d, size_t* out, int n);
+
+/*
  * attn_k_smooth_quant -- the 8-bit preparation (page 1, "SageAttention":
  * mean-centring of K before INT8 quantisation; FP8 for the second product).
  *
@@ -129,10 +141,12 @@ attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v,
  *  o          [B,H,N,d] in out_dtype (F16, BF16 or F32).
  *  lse, causal, scale, bias as for attn_fwd_bf16.
  *  S = Qq Kq^T in INT8 with int32 accumulation, dequantised with the two
- *  block scales; online softmax in fp32; P^ = e4m3(448 P); each key block's
- *  P^ V partial accumulates in fp32 (level 1) and is added to the rescaled
- *  running output in fp32 (level 2); the V scales and 1/(448 l) are applied
- *  once at the end.
+ *  block scales; online softmax in fp32 with a running maximum m that is
+ *  raised only when a 64-key block's maximum exceeds it by more than 2 (log2
+ *  units); P^ = e4m3(448 * 2^(t - m - 2)) <= 448; each key block's P^ V
+ *  partial accumulates in fp32 inside one matrix instruction (level 1) and
+ *  is added to the rescaled running output in fp32 (level 2); the V scales
+ *  and 1/l are applied once at the end.
  */
 attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B,
                            int H, int N, int d, int causal, float scale,

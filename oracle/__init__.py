@@ -18,6 +18,9 @@ Functions (each cites what it follows in the C source):
                         "claim vs reality": K smoothing, INT8 Q/K, FP8).
 * ``sage8_emulate_rows`` -- the blocked 8-bit forward modelled in fp64
                         (same passage: FP8 P, two-level accumulation).
+* ``sage8_emulate_rows_fp32`` -- the same with the GPU kernel's fp32
+                        decisions (lazy running maximum, P scale), for a
+                        tight comparison with the GPU.
 * ``e4m3_encode``, ``e4m3_decode`` -- OCP FP8 E4M3 from its definition.
 """
 import ctypes
@@ -61,10 +64,14 @@ def _load():
     lib.sage8_oracle_quant_int8.restype = _int
     lib.sage8_oracle_quant_v.argtypes = [_ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]
     lib.sage8_oracle_quant_v.restype = _int
-    lib.sage8_oracle_emulate_rows.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+    lib.sage8_oracle_emulate_rows.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                               _i64, _i64, _i64, _i64, _int, _dbl, _i64,
                                               _int, _ptr, _i64, _ptr, _ptr, _int]
     lib.sage8_oracle_emulate_rows.restype = _int
+    lib.sage8_oracle_emulate_rows_fp32.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                                   _i64, _i64, _i64, _i64, _int, ctypes.c_float,
+                                                   _ptr, _i64, _ptr, _ptr, _int]
+    lib.sage8_oracle_emulate_rows_fp32.restype = _int
     _lib = lib
     return lib
 
@@ -215,10 +222,37 @@ def sage8_emulate_rows(prep, rows, causal=False, scale=None, bias=None, kv_block
     r = _rows(rows)
     out = np.zeros((r.shape[0], d), dtype=np.float64)
     lse = np.zeros((r.shape[0],), dtype=np.float64)
+    km = _f32(prep["kmean"]) if prep.get("kmean") is not None else None
     rc = _load().sage8_oracle_emulate_rows(_p(qq), _p(kq), _p(vq), _p(sq), _p(sk), _p(sv),
-                                           _p(bias), B, H, N, d, int(bool(causal)), float(scale),
+                                           _p(km), _p(bias), B, H, N, d, int(bool(causal)), float(scale),
                                            int(kv_block), int(p_mode), _p(r), r.shape[0],
                                            _p(out), _p(lse), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"sage8_oracle_emulate_rows failed with code {rc}")
+    return out, lse
+
+
+def sage8_emulate_rows_fp32(prep, rows, causal=False, scale=None, bias=None, nthreads=0):
+    """Blocked 8-bit forward with the kernel's fp32 decisions (64-key blocks,
+    running maximum raised only past +2 in log2 units, P^ = e4m3(448*2^(t-m-2))).
+    Returns (O [nrows,d], LSE [nrows]) in fp64."""
+    qq = np.ascontiguousarray(prep["qq"], dtype=np.int8)
+    kq = np.ascontiguousarray(prep["kq"], dtype=np.int8)
+    vq = np.ascontiguousarray(prep["vq"], dtype=np.uint8)
+    sq, sk, sv = _f32(prep["sq"]), _f32(prep["sk"]), _f32(prep["sv"])
+    B, H, N, d = qq.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if bias is not None:
+        bias = _f32(bias)
+    r = _rows(rows)
+    out = np.zeros((r.shape[0], d), dtype=np.float64)
+    lse = np.zeros((r.shape[0],), dtype=np.float64)
+    km = _f32(prep["kmean"]) if prep.get("kmean") is not None else None
+    rc = _load().sage8_oracle_emulate_rows_fp32(_p(qq), _p(kq), _p(vq), _p(sq), _p(sk), _p(sv),
+                                                _p(km), _p(bias), B, H, N, d, int(bool(causal)),
+                                                float(np.float32(scale)), _p(r), r.shape[0],
+                                                _p(out), _p(lse), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"sage8_oracle_emulate_rows_fp32 failed with code {rc}")
     return out, lse

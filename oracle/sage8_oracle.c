@@ -34,9 +34,11 @@
  *     after the running output is rescaled (level 2).
  *
  * Steps 1-3 are integer/byte results and are reproduced bit for bit by the
- * GPU prep; the emulator of steps 4-5 is a model of the blocked algorithm in
- * fp64 and agrees with the GPU up to fp32 summation order and rare one-code
- * FP8 rounding differences.
+ * GPU prep.  sage8_oracle_emulate_rows models steps 4-5 in fp64 as read
+ * above.  sage8_oracle_emulate_rows_fp32 runs the same algorithm with the
+ * GPU kernel's own fp32 decisions (its lazily raised running maximum and P
+ * scale, see there); it agrees with the GPU up to summation order and rare
+ * one-code FP8 rounding differences from the hardware exponential.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -200,7 +202,7 @@ int sage8_oracle_quant_v(const float* v, int64_t B, int64_t H, int64_t N,
 int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                               const uint8_t* vq, const float* sq,
                               const float* sk, const float* sv,
-                              const float* bias, int64_t B, int64_t H,
+                              const float* kmean, const float* bias, int64_t B, int64_t H,
                               int64_t N, int64_t d, int causal, double scale,
                               int64_t kv_block, int p_mode,
                               const int64_t* rows, int64_t nrows, double* out,
@@ -289,8 +291,149 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
             }
             for (int64_t c = 0; c < d; ++c)
                 o[c] = (l > 0.0) ? o[c] * (double)sv[bh * d + c] / (E4M3_MAX * l) : 0.0;
-            if (lse)
-                lse[r] = (l > 0.0) ? m + log(l) : -INFINITY;
+            if (lse) {
+                /* the centring of K shifted every score of the row by
+                 * scale * (dequantised q) . kmean; add it back to the LSE */
+                double shift = 0.0;
+                if (kmean)
+                    for (int64_t c = 0; c < d; ++c)
+                        shift += (double)qi[c] * (double)kmean[bh * d + c];
+                lse[r] = (l > 0.0) ? m + log(l) + scale * sqi * shift : -INFINITY;
+            }
+        }
+        free(s);
+        free(blk);
+    }
+    return failed ? 3 : 0;
+}
+
+/* ---- the blocked 8-bit forward with the GPU kernel's fp32 decisions ------ */
+
+/*
+ * Same algorithm as sage8_oracle_emulate_rows, but every quantity that
+ * decides an FP8 code or a rescale is formed in fp32 with the operations and
+ * the order the GPU kernel uses (the pages leave these choices open; where
+ * floating point decides a quantised code, both sides take the decision in
+ * the kernel's precision):
+ *   c = fp32(scale * log2(e)) (the smallest normal float if that is 0),
+ *   f = (sq * sk) * c, t = fmaf(float(S_int), f, bias * log2(e)),
+ *   the running maximum m (log2 units) is raised only when a block maximum
+ *   exceeds it by more than 2, kc = (bias*log2e - m) + (log2(448) - 2),
+ *   P^ = e4m3(fp32(2^fmaf(float(S_int), f, kc))) <= 448.
+ * Exponentials are evaluated in fp64 and rounded to fp32 (the kernel's
+ * hardware exp2 is within about one fp32 ulp of that); sums are in fp64.
+ * kv_block is 64, as in the kernel.
+ */
+int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
+                                   const uint8_t* vq, const float* sq,
+                                   const float* sk, const float* sv,
+                                   const float* kmean, const float* bias, int64_t B, int64_t H,
+                                   int64_t N, int64_t d, int causal,
+                                   float scale, const int64_t* rows,
+                                   int64_t nrows, double* out, double* lse,
+                                   int nthreads)
+{
+    if (!qq || !kq || !vq || !sq || !sk || !sv || !rows || !out || B <= 0 ||
+        H <= 0 || N <= 0 || d <= 0 || nrows < 0)
+        return 1;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N)
+            return 2;
+    }
+    const int64_t kvb = 64;
+    const int64_t nqk = (N + SAGE_QK_BLOCK - 1) / SAGE_QK_BLOCK;
+    const int64_t nbb = (N + SAGE_BIAS_BLOCK - 1) / SAGE_BIAS_BLOCK;
+    const float log2e_f = 1.4426950408889634f;
+    const float tau = 2.0f;
+    const float plog = (float)6.807354922057604; /* log2(448) - 2 */
+    float c = (float)((double)scale * 1.4426950408889634);
+    if (c == 0.0f)
+        c = 1.17549435e-38f;
+    double vdec[256];
+    for (int cc = 0; cc < 256; ++cc)
+        vdec[cc] = sage8_e4m3_decode((uint8_t)cc);
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        float* s = (float*)malloc((size_t)kvb * sizeof(float));
+        double* blk = (double*)malloc((size_t)d * sizeof(double));
+        if (!s || !blk) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!s || !blk)
+                continue;
+            const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            const int64_t bh = b * H + h;
+            const int8_t* qi = qq + (bh * N + i) * d;
+            const float sqi = sq[bh * nqk + i / SAGE_QK_BLOCK];
+            double* o = out + r * d;
+            for (int64_t cc = 0; cc < d; ++cc)
+                o[cc] = 0.0;
+            float m = -INFINITY;
+            double l = 0.0;
+            const int64_t jend = causal ? i + 1 : N;
+            for (int64_t j0 = 0; j0 < jend; j0 += kvb) {
+                const int64_t j1 = (j0 + kvb < jend) ? j0 + kvb : jend;
+                const float f = (sqi * sk[bh * nqk + j0 / SAGE_QK_BLOCK]) * c;
+                const float bl = bias ? bias[(bh * nbb + i / SAGE_BIAS_BLOCK) * nbb +
+                                             j0 / SAGE_BIAS_BLOCK] * log2e_f
+                                      : 0.0f;
+                float ext = (f > 0.0f) ? -INFINITY : INFINITY;
+                for (int64_t j = j0; j < j1; ++j) {
+                    const int8_t* kj = kq + (bh * N + j) * d;
+                    int64_t acc = 0;
+                    for (int64_t cc = 0; cc < d; ++cc)
+                        acc += (int64_t)qi[cc] * (int64_t)kj[cc];
+                    s[j - j0] = (float)acc; /* exact: |acc| < 2^24 */
+                    if (f > 0.0f ? s[j - j0] > ext : s[j - j0] < ext)
+                        ext = s[j - j0];
+                }
+                const float m_blk = fmaf(ext, f, bl);
+                if (m_blk > m + tau) {
+                    const double alpha = (m == -INFINITY) ? 0.0 : exp2((double)m - (double)m_blk);
+                    for (int64_t cc = 0; cc < d; ++cc)
+                        o[cc] *= alpha;
+                    l *= alpha;
+                    m = m_blk;
+                }
+                const float base = (m == -INFINITY) ? 0.0f : m;
+                const float kc = (bl - base) + plog;
+                for (int64_t cc = 0; cc < d; ++cc)
+                    blk[cc] = 0.0;
+                for (int64_t j = j0; j < j1; ++j) {
+                    const float p = (float)exp2((double)fmaf(s[j - j0], f, kc));
+                    l += (double)p;
+                    const double ph = vdec[sage8_e4m3_encode((double)p)];
+                    if (ph == 0.0)
+                        continue;
+                    const uint8_t* vj = vq + (bh * N + j) * d;
+                    for (int64_t cc = 0; cc < d; ++cc)
+                        blk[cc] += ph * vdec[vj[cc]]; /* level 1 */
+                }
+                for (int64_t cc = 0; cc < d; ++cc)
+                    o[cc] += blk[cc]; /* level 2 */
+            }
+            for (int64_t cc = 0; cc < d; ++cc)
+                o[cc] = (l > 0.0) ? o[cc] * (double)sv[bh * d + cc] / l : 0.0;
+            if (lse) {
+                double shift = 0.0;
+                if (kmean)
+                    for (int64_t cc = 0; cc < d; ++cc)
+                        shift += (double)qi[cc] * (double)kmean[bh * d + cc];
+                lse[r] = (l > 0.0) ? ((double)m + log2(l) - (double)plog) * 0.6931471805599453 +
+                                         (double)scale * (double)sqi * shift
+                                   : -INFINITY;
+            }
         }
         free(s);
         free(blk);

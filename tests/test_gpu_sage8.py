@@ -1,0 +1,231 @@
+"""GPU parity of the 8-bit path (K smoothing + INT8 Q/K + FP8 P and V).
+
+Three bars, each against code under oracle/ only:
+  * preparation: bit-exact against the oracle's quantisers (K mean, INT8
+    codes and block scales of Q and of the centred K, e4m3 codes and channel
+    scales of V; padded rows hold zero codes);
+  * forward against the fp32-decision model of the blocked 8-bit forward
+    (same lazy running maximum, same e4m3 P^), fed the oracle's quantised
+    data: max abs <= EMU_MAX_ABS, mean abs <= EMU_MEAN_ABS on fp32 output
+    (plus one ulp of |O| for a bf16 / fp16 output).
+    The remaining difference is the device exp2/log2 (about 1 ulp), which
+    can move an e4m3 rounding of P^ by one code, and the fp32 order of sums;
+  * forward against the exact fp64 attention of the same rounded inputs:
+    cosine >= 0.999 per compared set of rows; rel-L1 is recorded and held
+    under REL_L1_FLOOR, the error of the 8-bit recipe itself (INT8 Q K^T,
+    e4m3 P and e4m3 V), which the fp64 model of the recipe reproduces on
+    the CPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_attention_attn_amd as attn
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 2e-5, 1e-4
+COS_MIN, REL_L1_FLOOR = 0.999, 0.05
+
+
+def _prep_both(inp):
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    prep = attn.sage8_prep(q, k, v)
+    ref = oracle.sage8_prepare(*(inp[n].float().numpy() for n in ("q", "k", "v")))
+    return prep, ref
+
+
+def _rows_all(B, H, N):
+    return np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(N)], dtype=np.int64)
+
+
+def _gather_lse(lse, rows):
+    idx = torch.as_tensor(rows, device=lse.device)
+    return lse[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+
+
+def _check(inp, causal, scale, rows=None, out_dtype=torch.float32, label="", check_oracle=True):
+    B, H, N, d = inp["q"].shape
+    print(f"[gpu] sage8 {label} shape={(B, H, N, d)} {inp['q'].dtype} causal={causal}", flush=True)
+    prep, ref = _prep_both(inp)
+    bias = inp["bias"].to(DEV) if inp["bias"] is not None else None
+    o, lse = attn.fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    if rows is None:
+        rows = _rows_all(B, H, N)
+    got = workloads.gather_rows(o, rows)
+    got_l = _gather_lse(lse, rows)
+    bn = inp["bias"].numpy() if inp["bias"] is not None else None
+    o_emu, l_emu = oracle.sage8_emulate_rows_fp32(ref, rows, causal=causal, scale=scale, bias=bn)
+    m_emu = workloads.error_metrics(got, o_emu)
+    fin = np.isfinite(l_emu)
+    assert np.array_equal(fin, np.isfinite(got_l)), label
+    lse_err = float(np.abs(got_l[fin] - l_emu[fin]).max()) if fin.any() else 0.0
+    print(f"    vs fp32 model: {m_emu} lse {lse_err:.2e}", flush=True)
+    # a bf16 / fp16 output adds its own rounding: half an ulp of |O| (2^-9
+    # resp. 2^-12 relative), bounded here by a full ulp
+    rel = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}[o.dtype]
+    excess = np.abs(got - o_emu) - (EMU_MAX_ABS + rel * np.abs(o_emu))
+    assert excess.max() <= 0, (label, m_emu, float(excess.max()))
+    assert m_emu["mean_abs"] <= EMU_MEAN_ABS + rel * float(np.abs(o_emu).mean()), (label, m_emu)
+    assert lse_err <= EMU_LSE, (label, lse_err)
+    m_ref = None
+    if check_oracle:
+        qn, kn, vn = (inp[n].float().numpy() for n in ("q", "k", "v"))
+        o_ref, _ = oracle.attn_rows(qn, kn, vn, rows, causal=causal, scale=scale, bias=bn)
+        m_ref = workloads.error_metrics(got, o_ref)
+        print(f"    vs fp64 attention: {m_ref}", flush=True)
+        assert m_ref["cos"] >= COS_MIN and m_ref["rel_l1"] <= REL_L1_FLOOR, (label, m_ref)
+    return prep, ref, o, lse, m_emu, m_ref
+
+
+# ---------------------------------------------------------------- preparation
+
+PREP_N = [1, 63, 64, 65, 200, 256, 300, 1000]
+
+
+@pytest.mark.parametrize("N", PREP_N)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prep_bit_exact(N, d, dtype):
+    inp = workloads.make_inputs(2, 2, N, d, dtype, seed=7 * N + d, outliers=(N % 2 == 0))
+    print(f"[gpu] sage8 prep N={N} d={d} {dtype}", flush=True)
+    prep, ref = _prep_both(inp)
+    torch.cuda.synchronize()
+    views = attn.sage8_workspace_views(prep)
+    np_ = views["qq"].shape[2]
+    assert np_ % 128 == 0 and np_ >= N
+    cpu = {k: v.cpu() for k, v in views.items()}
+    assert np.array_equal(cpu["kmean"].numpy().view(np.uint32), ref["kmean"].view(np.uint32))
+    for name in ("qq", "kq"):
+        assert np.array_equal(cpu[name][:, :, :N].numpy(), ref[name]), name
+        assert not cpu[name][:, :, N:].any(), f"{name} padding"
+    nb = (N + 63) // 64
+    for name in ("sq", "sk"):
+        assert np.array_equal(cpu[name][:, :, :nb].numpy().view(np.uint32), ref[name].view(np.uint32)), name
+    assert np.array_equal(cpu["sv"].numpy().view(np.uint32), ref["sv"].view(np.uint32))
+    assert np.array_equal(cpu["vq_logical"][:, :, :N].numpy(), ref["vq"])
+    assert not cpu["vq_logical"][:, :, N:].any()
+
+
+def test_prep_constant_columns():
+    """K constant along a channel centres to exact zeros; V zero in a channel
+    takes scale 1 and codes 0."""
+    inp = workloads.make_inputs(1, 2, 130, 64, "bf16", seed=5)
+    inp["k"][:, :, :, 3] = 1.5
+    inp["v"][:, :, :, 7] = 0.0
+    prep, ref = _prep_both(inp)
+    views = {k: v.cpu() for k, v in attn.sage8_workspace_views(prep).items()}
+    assert (views["kmean"][:, :, 3] == 1.5).all()
+    assert not views["kq"][:, :, :, 3].any()
+    assert (views["sv"][:, :, 7] == 1.0).all()
+    assert not views["vq_logical"][:, :, :, 7].any()
+    assert np.array_equal(views["kq"][:, :, :130].numpy(), ref["kq"])
+
+
+# -------------------------------------------------------------------- forward
+
+FWD_N = [1, 17, 64, 65, 127, 128, 129, 200, 300]
+
+
+@pytest.mark.parametrize("N", FWD_N)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_small_sweep(N, d, causal, with_bias):
+    inp = workloads.make_inputs(1, 2, N, d, "bf16", seed=N * 13 + d + causal, gate=with_bias)
+    _check(inp, causal, 1 / math.sqrt(d), label=f"sweep N={N} d={d} bias={with_bias}",
+           check_oracle=N >= 64)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("out", ["same", "f32"])
+def test_dtypes(dtype, out):
+    inp = workloads.make_inputs(2, 3, 333, 128, dtype, seed=11, outliers=True)
+    tdt = workloads.torch_dtype(dtype)
+    _, _, o, _, _, _ = _check(inp, True, 0.088, out_dtype=torch.float32 if out == "f32" else tdt,
+                              label=f"{dtype}->{out}")
+    assert o.dtype == (torch.float32 if out == "f32" else tdt)
+
+
+def test_outliers_long_rows():
+    """Channel outliers in Q and K (what the centring of K is for) over
+    several hundred 64-key blocks."""
+    inp = workloads.make_inputs(1, 2, 2048, 128, "bf16", seed=21, outliers=True)
+    rows = workloads.parity_rows(1, 2, 2048, seed=21, n_random=32)
+    _check(inp, True, 1 / math.sqrt(128), rows=rows, label="outliers N=2048")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
+def test_scale_edge_cases(scale):
+    """Zero scale gives uniform weights, a negative scale flips the order of
+    the scores, a large one makes the rows peaky."""
+    inp = workloads.make_inputs(1, 2, 150, 64, "bf16", seed=31)
+    _check(inp, True, scale, label=f"scale={scale}", check_oracle=scale != 0.5)
+
+
+def test_fully_masked_rows():
+    """A -inf block bias masks whole rows of blocks: those rows give O = 0
+    and LSE = -inf, like the exact definition."""
+    inp = workloads.make_inputs(1, 1, 192, 64, "bf16", seed=41, gate=True)
+    inp["bias"][0, 0, 1, :] = -math.inf
+    _, _, o, lse, _, _ = _check(inp, False, 0.125, label="masked", check_oracle=False)
+    assert (o[0, 0, 64:128] == 0).all()
+    assert torch.isneginf(lse[0, 0, 64:128]).all()
+
+
+def test_workspace_reuse_smaller_shape():
+    """A workspace sized for a large shape serves a smaller one, and stale
+    data from the first call does not leak into the second."""
+    big = workloads.make_inputs(1, 2, 700, 128, "bf16", seed=51)
+    small = workloads.make_inputs(1, 1, 90, 64, "bf16", seed=52)
+    prep_big = attn.sage8_prep(*(big[n].to(DEV) for n in ("q", "k", "v")))
+    ws = prep_big.workspace
+    o_big = attn.fwd_sage8(prep_big, causal=True)
+    prep_small = attn.sage8_prep(*(small[n].to(DEV) for n in ("q", "k", "v")), workspace=ws)
+    o_small = attn.fwd_sage8(prep_small, causal=False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_big).all()
+    ref = oracle.sage8_prepare(*(small[n].float().numpy() for n in ("q", "k", "v")))
+    rows = _rows_all(1, 1, 90)
+    o_emu, _ = oracle.sage8_emulate_rows_fp32(ref, rows, causal=False, scale=1 / 8)
+    m = workloads.error_metrics(workloads.gather_rows(o_small, rows), o_emu)
+    assert m["max_abs"] <= EMU_MAX_ABS, m
+
+
+def test_deterministic():
+    inp = workloads.make_inputs(2, 2, 500, 128, "bf16", seed=61)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o1 = attn.sageattn(q, k, v, causal=True)
+    o2 = attn.sageattn(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_sageattn_matches_two_step():
+    inp = workloads.make_inputs(1, 2, 260, 64, "f16", seed=71)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o1 = attn.sageattn(q, k, v, causal=False, scale=0.1)
+    o2 = attn.fwd_sage8(attn.sage8_prep(q, k, v), causal=False, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("cfg_id", [4, 5, 2])
+def test_workload_sampled_rows(cfg_id):
+    """Full-size workloads in the launch configuration the benchmark times:
+    sampled rows against the fp32 model and the exact attention."""
+    cfg, inp = workloads.config_inputs(cfg_id)
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    rows = workloads.parity_rows(B, H, N, seed=cfg_id, n_random=24)
+    _check(inp, cfg["causal"], 1 / math.sqrt(d), rows=rows, out_dtype=torch.bfloat16,
+           label=f"workload {cfg['name']}")

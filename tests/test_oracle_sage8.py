@@ -194,3 +194,41 @@ def test_emulator_floor_on_outlier_workload():
     m = workloads.error_metrics(o_emu, o_ref)
     assert m["cos"] >= 0.999, m
     assert 0.02 < m["rel_l1"] < 0.06, m
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_emulator_closed_form_q_zero(causal):
+    """Q = 0: every score is 0, so P = 2^(log2(448) - 2) = 112, which e4m3
+    represents exactly; O is then the (prefix) mean of the dequantised V and
+    LSE = ln(number of visible keys)."""
+    prep, _, _, v = _lossless_prep(1, 2, 150, 16, seed=9)
+    prep["qq"] = np.zeros_like(prep["qq"])
+    rows = [(0, h, i) for h in range(2) for i in (0, 1, 63, 64, 65, 100, 149)]
+    o, lse = oracle.sage8_emulate_rows_fp32(prep, rows, causal=causal, scale=0.3)
+    vd = v.astype(np.float64)
+    for n, (_, h, i) in enumerate(rows):
+        ref = vd[0, h, : i + 1].mean(axis=0) if causal else vd[0, h].mean(axis=0)
+        np.testing.assert_allclose(o[n], ref, rtol=0, atol=1e-12)
+        # log2(448) - 2 is an fp32 constant in this model: LSE to fp32 accuracy
+        np.testing.assert_allclose(lse[n], math.log(i + 1 if causal else 150), rtol=0, atol=1e-6)
+
+
+def test_fp32_emulator_matches_recipe_floor():
+    """The kernel-precision emulator on a scaled-down workload-4 distribution
+    against the fp64 oracle: same accuracy class as the fp64 model."""
+    inp = workloads.make_inputs(1, 2, 1024, 128, "bf16", seed=4, outliers=True)
+    q, k, v = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    prep = oracle.sage8_prepare(q, k, v)
+    rows = workloads.parity_rows(1, 2, 1024, seed=4, n_random=48)
+    scale = 1 / math.sqrt(128)
+    o_ref, l_ref = oracle.attn_rows(q, k, v, rows, causal=True, scale=scale)
+    o32, l32 = oracle.sage8_emulate_rows_fp32(prep, rows, causal=True, scale=scale)
+    o64, _ = oracle.sage8_emulate_rows(prep, rows, causal=True, scale=scale)
+    m = workloads.error_metrics(o32, o_ref)
+    assert m["cos"] >= 0.999 and 0.02 < m["rel_l1"] < 0.06, m
+    # the two models differ only in where P is rounded
+    assert workloads.error_metrics(o32, o64)["rel_l1"] < 0.03
+    # the LSE includes the shift that the centring of K removed
+    assert np.abs(l32 - l_ref).max() < 0.05
+    _, l64 = oracle.sage8_emulate_rows(prep, rows, causal=True, scale=scale)
+    assert np.abs(l64 - l_ref).max() < 0.05

@@ -16,14 +16,16 @@
 //             clamp +-127); V to e4m3 (code = e4m3_rne(v * inv)), written
 //             through LDS into the per-block transposed layout that the P V
 //             product reads.
-// Forward: S^T = Kq Qq^T on 32x32x32 INT8 MFMA (int32, exact), scaled by
-// sq*sk*scale*log2(e) per 64x64 block; online softmax in base 2 with a lazy
-// running maximum (raised only when a block maximum exceeds it by more than
-// kTau8 = 2); P^ = e4m3(448 * 2^(t - m - kTau8)) <= 448 becomes the B operand
-// of a 32x32x64 FP8 MFMA straight from the S^T registers; V^T comes from the
-// prepared tile.  Level one of the accumulation is the fp32 sum over the 64
-// keys of a block inside one matrix instruction, level two the fp32 running
-// output carried across blocks.  The V scales and 1/l are applied once.
+// Forward: S^T = Kq Qq^T on 32x32x32 INT8 MFMA (int32, exact, read as fp32
+// through an offset), scaled by sq*sk*scale*log2(e) per 64x64 block; online
+// softmax in base 2 with a lazy running maximum (raised only when a block
+// maximum exceeds it by more than kTau8 = 2); P^ = e4m3(448 * 2^(t - m -
+// kTau8)) <= 448 becomes the B operand of a 32x32x64 FP8 MFMA straight from
+// the S^T registers; V^T comes from the prepared tile.  Level one of the
+// accumulation is the fp32 sum over the 64 keys of a block inside one matrix
+// instruction, level two the fp32 running output carried across blocks.  The
+// normaliser l is the sum of the same P^ (a 16x16x128 FP8 product with a 0/1
+// mask); the V scales and 1/l are applied once.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
@@ -299,6 +301,12 @@ struct Fwd8Params {
 constexpr int kNW8 = 4;                // waves per workgroup
 constexpr int kBM8 = 32 * kNW8;        // queries per workgroup
 constexpr int kThreads8 = 64 * kNW8;
+// The INT8 accumulators start from the bit pattern of 1.5 * 2^23: with
+// |S| < 2^22 (true for d <= 128: 128 * 127^2 < 2^22) the int32 sum
+// 0x4B400000 + S read as fp32 is exactly 12582912 + S, so the scores leave
+// the matrix unit as floats and the offset is folded into the exponent.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
 
 template <int D>
 struct Fwd8Smem {
@@ -309,9 +317,7 @@ struct Fwd8Smem {
   static constexpr int kVRow = kQB + 16;
   static constexpr int kKTile = kQB * kKRow;
   static constexpr int kVTile = D * kVRow;
-  static constexpr int kLoop = 2 * (kKTile + kVTile);
-  static constexpr int kStage = kNW8 * 32 * (D + 4) * 4;  // fp32 output staging, bytes
-  static constexpr int kBytes = kLoop > kStage ? kLoop : kStage;
+  static constexpr int kBytes = 2 * (kKTile + kVTile);
 };
 
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
@@ -382,10 +388,20 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
     }
   };
 
+  // Row sums of P^ on the matrix unit: a 16x16x128 FP8 product of a 0/1
+  // mask with the P^T operand.  Lane m + 16g of the mask is row m, key group
+  // g; ones in lanes 0 and 32 (row 0, groups 0 and 2 = both halves of
+  // queries 0..15) and in lanes 20 and 52 (row 4, groups 1 and 3 = queries
+  // 16..31) put the sum of query l32 in register 0 of lane l32 (lanes 32..63
+  // hold zeros).
+  const uint32_t onew = (lane == 0 || lane == 32 || lane == 20 || lane == 52) ? 0x38383838u : 0u;  // e4m3 1.0
+  const i32x8_t ones = {(int)onew, (int)onew, (int)onew, (int)onew, (int)onew, (int)onew, (int)onew, (int)onew};
+  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+
   f32x16_t o[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
   const float c = p.c;
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
@@ -401,9 +417,13 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
     const bool more = j + 1 < nkb;
     if (more) load_kv(j + 1);
     if (wave_has_rows && j <= wave_last) {
-      // ---- S^T = Kq Qq^T, exact int32
+      // ---- S^T = Kq Qq^T on top of the offset, exact
       const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
-      i32x16_t si[2] = {i32x16_t{}, i32x16_t{}};
+      i32x16_t si[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) si[T][r] = kMagicBits;
 #pragma unroll
       for (int kk = 0; kk < kKS; ++kk)
 #pragma unroll
@@ -412,13 +432,12 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
           si[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
                                                         __builtin_bit_cast(i32x4_t, qf[kk]), si[T], 0, 0, 0);
         }
-      // dequantised, base 2: t = S_int * f + bias*log2(e)
+      // s = kMagic + S_int; base 2: t = S_int * f + bias*log2(e)
+      //                               = s * f + g,  g = bias*log2(e) - kMagic * f
       const float f = (sqw * skrow[j]) * c;
       f32x16_t s[2];
 #pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[T][r] = (float)si[T][r];
+      for (int T = 0; T < 2; ++T) s[T] = __builtin_bit_cast(f32x16_t, si[T]);
       if ((CAUSAL && j == wave_last) || (j + 1) * kQB > N) {
         const int kb0 = j * kQB, qi = qw0 + l32;
 #pragma unroll
@@ -431,6 +450,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
           }
       }
       const float bl = bias_row ? bias_row[j] * kLog2e : 0.f;
+      const float g = fmaf(-kMagic, f, bl);
       float a0;
       if (pos) {
         a0 = fmaxf(s[0][0], s[1][0]);
@@ -443,36 +463,29 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
         for (int r = 1; r < 16; ++r) a0 = fminf(a0, fminf(s[0][r], s[1][r]));
         a0 = xor32_min(a0);
       }
-      const float m_blk = (a0 == sent) ? -INFINITY : fmaf(a0, f, bl);
+      const float m_blk = (a0 == sent) ? -INFINITY : fmaf(a0, f, g);
       const bool need = m_blk > m_run + kTau8;
       if (__any(need)) {
         const float m_new = need ? m_blk : m_run;
         // rows that keep their maximum keep alpha = 1 (also a row still at -inf)
         const float alpha = need ? exp2_approx(m_run - m_new) : 1.f;
-        l_run *= alpha;
+        lacc[0] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
         m_run = m_new;
       }
-      const float kc = (bl - ((m_run == -INFINITY) ? 0.f : m_run)) + kPlog;
-      // ---- P^ in e4m3 as the B operand (byte e = 16T + r), row sum of the
-      // unquantised values
-      u32x4_t pl, ph;
-      float lsum = 0.f;
-      float pv[32];
+      const float kc = (g - ((m_run == -INFINITY) ? 0.f : m_run)) + kPlog;
+      // ---- P^ in e4m3 as the B operand (byte e = 16T + r)
+      uint32_t pw[8];
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        pv[e] = exp2_approx(fmaf(s[e >> 4][e & 15], f, kc));
-        lsum += pv[e];
+      for (int w = 0; w < 8; ++w) {
+        const int T = w >> 2, r0 = 4 * (w & 3);
+        pw[w] = pack_fp8x4(exp2_approx(fmaf(s[T][r0], f, kc)), exp2_approx(fmaf(s[T][r0 + 1], f, kc)),
+                           exp2_approx(fmaf(s[T][r0 + 2], f, kc)), exp2_approx(fmaf(s[T][r0 + 3], f, kc)));
       }
-      l_run += lsum;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pl[w] = pack_fp8x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
-        ph[w] = pack_fp8x4(pv[16 + 4 * w], pv[16 + 4 * w + 1], pv[16 + 4 * w + 2], pv[16 + 4 * w + 3]);
-      }
-      const i32x8_t bop = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3],
-                           (int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3]};
+      const i32x8_t bop = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
+                           (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+      lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, bop, lacc, 0, 0, 0, 0, 0, 0);
       // ---- O^T += Vq^T P^T over the 64 keys (one FP8 instruction per d tile)
       const uint8_t* Vs = vl + buf * kVTile + l32 * kVRow + 32 * hf;
 #pragma unroll
@@ -488,10 +501,10 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc * sv[d] / l; LSE = (m + log2 l - kPlog) ln 2 plus
-  // the shift scale * sq * (Qq . kmean) that the centring of K removed from
-  // every score of the row (the output does not depend on it, the LSE does)
-  const float l_tot = xor32_sum(l_run);
+  // ---- epilogue: O = acc * sv[d] / l with l = sum of P^; LSE = (m + log2 l
+  // - kPlog) ln 2 plus the shift scale * sq * (Qq . kmean) that the centring
+  // of K removed from every score of the row (O does not depend on it)
+  const float l_tot = xor32_sum(lacc[0]);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int qi = qw0 + l32;
   if (p.lse != nullptr) {
@@ -509,51 +522,27 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
       p.lse[(size_t)bh * N + qi] =
           l_tot > 0.f ? (m_run + __log2f(l_tot) - kPlog + c * (sqw * dot)) * kLn2 : -INFINITY;
   }
+  if (qi >= N) return;
+  // lane (l32, hf) holds d = 32dt + 8g + 4hf + u of query qi: 16-byte (fp32)
+  // or 8-byte (fp16 / bf16) stores straight from the accumulators
   const float* svh = p.sv + (size_t)bh * D;
-  constexpr int kSt = D + 4;
-  float* st = reinterpret_cast<float*>(smem) + wave * 32 * kSt;
+  const size_t orow = ((size_t)bh * N + qi) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * dt + 8 * g + 4 * hf;
       const f32x4_t svv = *(const f32x4_t*)(svh + d);
-      f32x4_t w = {o[dt][4 * g] * svv[0] * inv, o[dt][4 * g + 1] * svv[1] * inv,
-                   o[dt][4 * g + 2] * svv[2] * inv, o[dt][4 * g + 3] * svv[3] * inv};
-      *(f32x4_t*)(st + l32 * kSt + d) = w;
-    }
-  __syncthreads();
-  const size_t head = (size_t)bh * N * D;
-  if (p.out_kind == kOutF32) {
-    float* O = reinterpret_cast<float*>(p.o) + head;
-    constexpr int kCh = D / 4;
-#pragma unroll
-    for (int it = 0; it < 32 * kCh / 64; ++it) {
-      const int idx = lane + 64 * it, row = idx / kCh, ch = idx % kCh, q = qw0 + row;
-      if (q < N) *(f32x4_t*)(O + (size_t)q * D + 4 * ch) = *(const f32x4_t*)(st + row * kSt + 4 * ch);
-    }
-  } else {
-    uint16_t* O = reinterpret_cast<uint16_t*>(p.o) + head;
-    const bool bf = p.out_kind == kOutBF16;
-    constexpr int kCh = D / 8;
-#pragma unroll
-    for (int it = 0; it < 32 * kCh / 64; ++it) {
-      const int idx = lane + 64 * it, row = idx / kCh, ch = idx % kCh, q = qw0 + row;
-      if (q < N) {
-        const f32x4_t a = *(const f32x4_t*)(st + row * kSt + 8 * ch);
-        const f32x4_t b = *(const f32x4_t*)(st + row * kSt + 8 * ch + 4);
-        u32x4_t w;
-        if (bf) {
-          w = u32x4_t{pack2<true>(a[0], a[1]), pack2<true>(a[2], a[3]), pack2<true>(b[0], b[1]),
-                      pack2<true>(b[2], b[3])};
-        } else {
-          w = u32x4_t{pack2<false>(a[0], a[1]), pack2<false>(a[2], a[3]), pack2<false>(b[0], b[1]),
-                      pack2<false>(b[2], b[3])};
-        }
-        *(u32x4_t*)(O + (size_t)q * D + 8 * ch) = w;
+      const f32x4_t w = {o[dt][4 * g] * svv[0] * inv, o[dt][4 * g + 1] * svv[1] * inv,
+                         o[dt][4 * g + 2] * svv[2] * inv, o[dt][4 * g + 3] * svv[3] * inv};
+      if (p.out_kind == kOutF32) {
+        *(f32x4_t*)(reinterpret_cast<float*>(p.o) + orow + d) = w;
+      } else if (p.out_kind == kOutBF16) {
+        *(u32x2_t*)(reinterpret_cast<uint16_t*>(p.o) + orow + d) = u32x2_t{pack2<true>(w[0], w[1]), pack2<true>(w[2], w[3])};
+      } else {
+        *(u32x2_t*)(reinterpret_cast<uint16_t*>(p.o) + orow + d) = u32x2_t{pack2<false>(w[0], w[1]), pack2<false>(w[2], w[3])};
       }
     }
-  }
 }
 
 template <int D, bool CAUSAL>

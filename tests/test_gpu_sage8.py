@@ -9,7 +9,10 @@ Three bars, each against code under oracle/ only:
     data: max abs <= EMU_MAX_ABS, mean abs <= EMU_MEAN_ABS on fp32 output
     (plus one ulp of |O| for a bf16 / fp16 output).
     The remaining difference is the device exp2/log2 (about 1 ulp), which
-    can move an e4m3 rounding of P^ by one code, and the fp32 order of sums;
+    can move an e4m3 rounding of P^ by one code (of the order of one element
+    in 10^5; the code is in both the numerator and the normaliser, so on a
+    peaky row it moves O and LSE by up to about 1e-3), and the fp32 order of
+    sums;
   * forward against the exact fp64 attention of the same rounded inputs:
     cosine >= 0.999 per compared set of rows; rel-L1 is recorded and held
     under REL_L1_FLOOR, the error of the 8-bit recipe itself (INT8 Q K^T,
@@ -29,7 +32,7 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 2e-5, 1e-4
+EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 5e-5, 1e-3
 COS_MIN, REL_L1_FLOOR = 0.999, 0.05
 
 

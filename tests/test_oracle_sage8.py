@@ -232,3 +232,34 @@ def test_fp32_emulator_matches_recipe_floor():
     assert np.abs(l32 - l_ref).max() < 0.05
     _, l64 = oracle.sage8_emulate_rows(prep, rows, causal=True, scale=scale)
     assert np.abs(l64 - l_ref).max() < 0.05
+
+
+@pytest.mark.parametrize("which", ["fp64", "fp32"])
+def test_normaliser_is_sum_of_quantised_p(which):
+    """Two keys whose probabilities stand in the ratio 2^-1.5.  Hand-derived:
+    K centres to rows +-1 (codes +-127, both scales 1/127 after the centring
+    by kmean = 1), Q = e_0 (code 127, scale 1/127), so S = +-127 and the
+    scores differ by 2 * scale.  With scale = 0.75 ln 2 the weights are 1 and
+    2^-1.5.  fp64 model: 448 * 2^-1.5 = 158.39 rounds to the e4m3 value 160
+    (neighbours 144 and 160, midpoint 152); fp32 model: 112 * 2^-1.5 = 39.60
+    rounds to 40 (neighbours 36 and 40, midpoint 38).  V = rows (1, 0) in
+    channel 0 (scale 1/448, codes exact).  With l = sum of the quantised
+    weights, O[0] = 448 / (448 + 160) = 112 / (112 + 40) = 0.736842...; the
+    unquantised sum would give 1 / (1 + 2^-1.5) = 0.738796..."""
+    d = 64
+    q = np.zeros((1, 1, 2, d), np.float32)
+    q[0, 0, :, 0] = 1.0
+    k = np.zeros((1, 1, 2, d), np.float32)
+    k[0, 0, 0, 0], k[0, 0, 1, 0] = 2.0, 0.0
+    v = np.zeros((1, 1, 2, d), np.float32)
+    v[0, 0, 0, 0] = 1.0
+    prep = oracle.sage8_prepare(q, k, v)
+    assert prep["kq"][0, 0, 0, 0] == 127 and prep["kq"][0, 0, 1, 0] == -127
+    rows = np.array([[0, 0, 0]])
+    scale = 0.75 * math.log(2.0)
+    if which == "fp64":
+        o, _ = oracle.sage8_emulate_rows(prep, rows, causal=False, scale=scale)
+    else:
+        o, _ = oracle.sage8_emulate_rows_fp32(prep, rows, causal=False, scale=scale)
+    assert abs(o[0, 0] - 448.0 / 608.0) < 1e-6
+    assert abs(o[0, 0] - 1.0 / (1.0 + 2.0 ** -1.5)) > 1e-3

@@ -24,8 +24,8 @@
 // the S^T registers; V^T comes from the prepared tile.  Level one of the
 // accumulation is the fp32 sum over the 64 keys of a block inside one matrix
 // instruction, level two the fp32 running output carried across blocks.  The
-// normaliser l is the sum of the same P^ (a 16x16x128 FP8 product with a 0/1
-// mask); the V scales and 1/l are applied once.
+// normaliser l sums the fp32 values of P before they are quantised; the V
+// scales and 1/l are applied once.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
@@ -388,20 +388,10 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
     }
   };
 
-  // Row sums of P^ on the matrix unit: a 16x16x128 FP8 product of a 0/1
-  // mask with the P^T operand.  Lane m + 16g of the mask is row m, key group
-  // g; ones in lanes 0 and 32 (row 0, groups 0 and 2 = both halves of
-  // queries 0..15) and in lanes 20 and 52 (row 4, groups 1 and 3 = queries
-  // 16..31) put the sum of query l32 in register 0 of lane l32 (lanes 32..63
-  // hold zeros).
-  const uint32_t onew = (lane == 0 || lane == 32 || lane == 20 || lane == 52) ? 0x38383838u : 0u;  // e4m3 1.0
-  const i32x8_t ones = {(int)onew, (int)onew, (int)onew, (int)onew, (int)onew, (int)onew, (int)onew, (int)onew};
-  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
-
   f32x16_t o[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x16_t{};
-  float m_run = -INFINITY;
+  float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
@@ -469,23 +459,27 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
         const float m_new = need ? m_blk : m_run;
         // rows that keep their maximum keep alpha = 1 (also a row still at -inf)
         const float alpha = need ? exp2_approx(m_run - m_new) : 1.f;
-        lacc[0] *= alpha;
+        l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
         m_run = m_new;
       }
       const float kc = (g - ((m_run == -INFINITY) ? 0.f : m_run)) + kPlog;
-      // ---- P^ in e4m3 as the B operand (byte e = 16T + r)
+      // ---- P^ in e4m3 as the B operand (byte e = 16T + r); the row sum
+      // adds the fp32 values before quantisation
       uint32_t pw[8];
+      float lsum = 0.f;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int T = w >> 2, r0 = 4 * (w & 3);
-        pw[w] = pack_fp8x4(exp2_approx(fmaf(s[T][r0], f, kc)), exp2_approx(fmaf(s[T][r0 + 1], f, kc)),
-                           exp2_approx(fmaf(s[T][r0 + 2], f, kc)), exp2_approx(fmaf(s[T][r0 + 3], f, kc)));
+        const float e0 = exp2_approx(fmaf(s[T][r0], f, kc)), e1 = exp2_approx(fmaf(s[T][r0 + 1], f, kc));
+        const float e2 = exp2_approx(fmaf(s[T][r0 + 2], f, kc)), e3 = exp2_approx(fmaf(s[T][r0 + 3], f, kc));
+        lsum += (e0 + e1) + (e2 + e3);
+        pw[w] = pack_fp8x4(e0, e1, e2, e3);
       }
+      l_run += lsum;
       const i32x8_t bop = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                            (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-      lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, bop, lacc, 0, 0, 0, 0, 0, 0);
       // ---- O^T += Vq^T P^T over the 64 keys (one FP8 instruction per d tile)
       const uint8_t* Vs = vl + buf * kVTile + l32 * kVRow + 32 * hf;
 #pragma unroll
@@ -501,10 +495,10 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc * sv[d] / l with l = sum of P^; LSE = (m + log2 l
-  // - kPlog) ln 2 plus the shift scale * sq * (Qq . kmean) that the centring
-  // of K removed from every score of the row (O does not depend on it)
-  const float l_tot = xor32_sum(lacc[0]);
+  // ---- epilogue: O = acc * sv[d] / l; LSE = (m + log2 l - kPlog) ln 2 plus
+  // the shift scale * sq * (Qq . kmean) that the centring of K removed from
+  // every score of the row (O does not depend on it)
+  const float l_tot = xor32_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int qi = qw0 + l32;
   if (p.lse != nullptr) {

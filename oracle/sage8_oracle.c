@@ -29,10 +29,7 @@
  *  4. P in FP8: P^ = e4m3(448 * P) where P = exp(s - m) with m the running
  *     maximum after the current key block, so 448 * P <= 448 never
  *     saturates.  The pages do not say which P the row sum l adds up; here
- *     it is the quantised P^, the same weights the numerator uses, so O is
- *     a convex combination of the dequantised V rows (on the pages'
- *     workloads this is as accurate as summing the unquantised P: rel-L1
- *     0.0372 against 0.0373 on a 2048-token causal sample).
+ *     it is the unquantised P, as in the full-precision online softmax.
  *  5. Two-level accumulation: the products of one key block are summed into
  *     a fresh partial (level 1), which is then added to the running output
  *     after the running output is rescaled (level 2).
@@ -279,9 +276,9 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                 double lb = 0.0;
                 for (int64_t j = j0; j < j1; ++j) {
                     const double p = exp(s[j - j0] - mnew);
+                    lb += p;
                     const double ph = p_mode ? vdec[sage8_e4m3_encode(E4M3_MAX * p)]
                                              : E4M3_MAX * p;
-                    lb += ph;
                     if (ph == 0.0)
                         continue;
                     const uint8_t* vj = vq + (bh * N + j) * d;
@@ -294,7 +291,7 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                 m = mnew;
             }
             for (int64_t c = 0; c < d; ++c)
-                o[c] = (l > 0.0) ? o[c] * (double)sv[bh * d + c] / l : 0.0;
+                o[c] = (l > 0.0) ? o[c] * (double)sv[bh * d + c] / (E4M3_MAX * l) : 0.0;
             if (lse) {
                 /* the centring of K shifted every score of the row by
                  * scale * (dequantised q) . kmean; add it back to the LSE */
@@ -302,7 +299,7 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                 if (kmean)
                     for (int64_t c = 0; c < d; ++c)
                         shift += (double)qi[c] * (double)kmean[bh * d + c];
-                lse[r] = (l > 0.0) ? m + log(l / E4M3_MAX) + scale * sqi * shift : -INFINITY;
+                lse[r] = (l > 0.0) ? m + log(l) + scale * sqi * shift : -INFINITY;
             }
         }
         free(s);
@@ -326,7 +323,7 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
  *   the block maximum is m_blk = fmaf(M + S_max, f, g) (S_min when f < 0),
  *   the running maximum m (log2 units) is raised only when a block maximum
  *   exceeds it by more than 2, kc = (g - m) + (log2(448) - 2),
- *   P^ = e4m3(fp32(2^fmaf(M + S, f, kc))) <= 448, l = sum of P^.
+ *   P^ = e4m3(fp32(2^fmaf(M + S, f, kc))) <= 448, l = sum of the fp32 values.
  * Exponentials are evaluated in fp64 and rounded to fp32 (the kernel's
  * hardware exp2 is within about one fp32 ulp of that); sums are in fp64.
  * kv_block is 64, as in the kernel.
@@ -421,8 +418,8 @@ int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
                     blk[cc] = 0.0;
                 for (int64_t j = j0; j < j1; ++j) {
                     const float p = (float)exp2((double)fmaf(magic + s[j - j0], f, kc));
+                    l += (double)p;
                     const double ph = vdec[sage8_e4m3_encode((double)p)];
-                    l += ph;
                     if (ph == 0.0)
                         continue;
                     const uint8_t* vj = vq + (bh * N + j) * d;

@@ -10,9 +10,8 @@ Three bars, each against code under oracle/ only:
     (plus one ulp of |O| for a bf16 / fp16 output).
     The remaining difference is the device exp2/log2 (about 1 ulp), which
     can move an e4m3 rounding of P^ by one code (of the order of one element
-    in 10^5; the code is in both the numerator and the normaliser, so on a
-    peaky row it moves O and LSE by up to about 1e-3), and the fp32 order of
-    sums;
+    in 10^5; on a peaky row such a code moves O by up to about 1e-3), and the
+    fp32 order of sums;
   * forward against the exact fp64 attention of the same rounded inputs:
     cosine >= 0.999 per compared set of rows; rel-L1 is recorded and held
     under REL_L1_FLOOR, the error of the 8-bit recipe itself (INT8 Q K^T,
@@ -32,7 +31,7 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 5e-5, 1e-3
+EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 5e-5, 1e-4
 COS_MIN, REL_L1_FLOOR = 0.999, 0.05
 
 

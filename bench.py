@@ -1,21 +1,30 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 
 A step is one pass of the whole hot path over the LLM-prefill workload
-(B=4, H=32, N=4096, d=128, causal, bf16 inputs): the bf16 fused forward, then
-the 8-bit preparation and the 8-bit fused forward on the same inputs.  Inputs
-are resident in device memory before the timed region.  ``value`` is the
-attention FLOPs the step computes (4*B*H*N^2*d/2 per forward, two forwards)
-divided by the step time.  Per-kernel times come from HIP events recorded on
-the stream the kernels run on.  Other workloads are timed after the main
-loop and reported under ``workloads`` (they are not part of ``value``).
+(B=4, H=32, N=4096, d=128, causal, bf16 Q/K/V ~ N(0,1), scale 1/sqrt(128),
+bf16 output): the bf16 fused forward, then the 8-bit preparation (K mean,
+INT8 Q/K, e4m3 V into a preallocated workspace) and the 8-bit fused forward
+on the same inputs.  Inputs are resident in device memory before the timed
+region and no cache is flushed between steps.  ``value`` is the attention
+FLOPs the step computes (two forwards, 4*B*H*N^2*d/2 each) divided by the
+step time.  Each kernel launch is bracketed by HIP events on the stream the
+kernels run on (torch's current stream, which the binding passes to the
+library), giving per-kernel averages; ``roofline`` describes the kernel with
+the largest share of the step.  Other workloads are timed after the main loop
+and reported under ``workloads`` (not part of ``value``).
 
 Prints ONE JSON line.  Only one GPU is supported: --gpus above 1 exits.
+
+Extra modes (for profiler runs):
+    --workload W --path bf16|sage8   run one workload's path --steps times
+    --copy-bytes NBYTES              run a plain device copy --steps times
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,7 +37,22 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPS and % of MFMA peak at 1 MI355X (bf16 and int8/fp8)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, datasheet
 PEAK_8BIT_TFLOPS = 5000.0   # MI355X dense fp8 / int8 MFMA, datasheet
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
+
+# HBM traffic per launch (bytes) from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# runs on the LLM-prefill workload, scaled by the same counters on a plain
+# 1 GiB device copy (FETCH_SIZE reads half the copied bytes: factor 2;
+# WRITE_SIZE reads them exactly: factor 1); profiles/llm-prefill_hbm-traffic.txt.
+# Valid only for the kernel sources it was taken on: the sha256 of the listed
+# sources must match, else traffic is reported as null.
+TRAFFIC = {
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 539997696,
+              "sha256": "8b5e33c5d06b06cbf6436c656a7dd63dc19253a52bcadf57f96b5741368794ce"},
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 338315008,
+             "sha256": "556d3a81c37ec833abfe1121213cd6dd7b04eabffe50f91310d7fd57b980f724"},
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880664576,
+              "sha256": "556d3a81c37ec833abfe1121213cd6dd7b04eabffe50f91310d7fd57b980f724"},
+}
 
 
 def parse():
@@ -38,16 +62,38 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workload", type=int, default=0,
                     help="profiling mode: run only this workload (1-5) --steps times and print its timing")
     ap.add_argument("--path", default="bf16", choices=["bf16", "sage8"],
                     help="profiling mode: which path to run")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration mode: time a plain device copy of this many bytes")
     return ap.parse_args()
 
 
+def log(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "bit_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(key):
+    t = TRAFFIC[key]
+    if t["bytes"] is None or t["sha256"] != sources_sha(t["sources"]):
+        return None
+    return t["bytes"]
+
+
 def _time_launches(fn, iters, stream):
-    """Average ms of fn() over iters launches, timed by event pairs on stream."""
+    """Per-launch ms of fn() over iters launches, from event pairs on stream."""
     import torch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
@@ -56,9 +102,18 @@ def _time_launches(fn, iters, stream):
         fn()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms.sort()
-    return sum(ms) / len(ms), ms[len(ms) // 2], ms[0]
+    return sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+
+
+def _stats(ms):
+    ms = sorted(ms)
+    return dict(ms_avg=round(sum(ms) / len(ms), 4), ms_median=round(ms[len(ms) // 2], 4), ms_min=round(ms[0], 4))
+
+
+def prep_bytes(B, H, N, d):
+    """Algorithmic bytes of the 8-bit preparation: Q, K, V (2 bytes) read
+    once, Qq, Kq, Vq (1 byte) written once; scales and means are < 0.1%."""
+    return B * H * N * d * (3 * 2 + 3 * 1)
 
 
 def cpu_baseline(inp, cfg, seconds):
@@ -82,13 +137,13 @@ def cpu_baseline(inp, cfg, seconds):
         flops += float((4.0 * d * vis).sum())
         done_rows += batch
         batch = min(batch * 2, 4096)
-    return dict(value=flops / elapsed / 1e12, unit="TFLOPS", cores=oracle.max_threads(), kind="oracle",
-                sample=f"{done_rows} random query rows of the {cfg['name']} workload "
-                       f"(fp64 three-loop oracle, {elapsed:.1f} s; flops counted as 4*d per visible key)")
+    return dict(value=round(flops / elapsed / 1e12, 6), unit="TFLOPS", cores=oracle.max_threads(), kind="oracle",
+                sample=f"{done_rows} random query rows of the {cfg['name']} workload, fp64 three-loop oracle "
+                       f"(OpenMP over rows) for {elapsed:.1f} s; flops counted as 4*d per visible key, as on the GPU")
 
 
 def profile_one(args):
-    """Run one workload's kernel --steps times (for rocprofv3 runs)."""
+    """Run one workload's path --steps times (for rocprofv3 runs)."""
     import torch
     import bit_attention_attn_amd as attn
     import workloads
@@ -101,26 +156,46 @@ def profile_one(args):
     if args.path == "bf16":
         fn = lambda: attn.fwd(q, k, v, causal=cfg["causal"], bias=bias, out_dtype=out_dtype)  # noqa: E731
     else:
+        ws = attn.sage8_prep(q, k, v).workspace
+
         def fn():
-            prep = attn.sage8_prep(q, k, v)
+            prep = attn.sage8_prep(q, k, v, workspace=ws)
             return attn.fwd_sage8(prep, causal=cfg["causal"], bias=bias, out_dtype=out_dtype)
     for _ in range(args.warmup):
         fn()
-    avg, med, mn = _time_launches(fn, args.steps, torch.cuda.current_stream(dev))
-    print(json.dumps({"workload": cfg["name"], "path": args.path, "ms_avg": round(avg, 4),
-                      "ms_min": round(mn, 4), "tflops": round(F / (avg * 1e-3) / 1e12, 2)}), flush=True)
+    ms = _time_launches(fn, args.steps, torch.cuda.current_stream(dev))
+    st = _stats(ms)
+    print(json.dumps({"workload": cfg["name"], "path": args.path, **st,
+                      "tflops": round(F / (st["ms_avg"] * 1e-3) / 1e12, 2)}), flush=True)
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of --copy-bytes bytes, --steps times:
+    the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = args.copy_bytes // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        y.copy_(x)
+    ms = _time_launches(lambda: y.copy_(x), args.steps, torch.cuda.current_stream(dev))
+    st = _stats(ms)
+    print(json.dumps({"copy_bytes": n * 4, **st,
+                      "GBs_read_plus_write": round(2 * n * 4 / (st["ms_avg"] * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(attention heads shard across GPUs with no communication; see the design notes).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(attention heads shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
     import torch
     import __graft_entry__
     __graft_entry__._ensure_built()
+    if args.copy_bytes:
+        return copy_calibration(args)
     if args.workload:
         return profile_one(args)
     import bit_attention_attn_amd as attn
@@ -131,37 +206,70 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     cfg, inp = workloads.config_inputs(2)
+    log(f"inputs ready: {cfg['name']}")
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     F = workloads.flops(B, H, N, d, causal)
+    ws = attn.sage8_prep(q, k, v).workspace
     torch.cuda.synchronize()
 
-    def bf16_fwd():
-        return attn.fwd(q, k, v, causal=causal)
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        attn.fwd(q, k, v, causal=causal)
+        if ev is not None:
+            ev[1].record(stream)
+        prep = attn.sage8_prep(q, k, v, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        attn.fwd_sage8(prep, causal=causal)
+        if ev is not None:
+            ev[3].record(stream)
 
     for _ in range(args.warmup):
-        bf16_fwd()
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(K):
-        ev[s][0].record(stream)
-        bf16_fwd()
-        ev[s][1].record(stream)
+        step(ev[s])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    bf16_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    bf16_avg = sum(bf16_ms) / K
     ms_per_step = total_ms / K
-    flops_per_step = F
-    value = flops_per_step / (ms_per_step * 1e-3) / 1e12
-    bf16_tflops = F / (bf16_avg * 1e-3) / 1e12
+    log(f"timed {K} steps: {ms_per_step:.4f} ms per step")
+    k16 = _stats([e[0].elapsed_time(e[1]) for e in ev])
+    kprep = _stats([e[1].elapsed_time(e[2]) for e in ev])
+    k8 = _stats([e[2].elapsed_time(e[3]) for e in ev])
+    value = 2 * F / (ms_per_step * 1e-3) / 1e12
+
+    tf16 = F / (k16["ms_avg"] * 1e-3) / 1e12
+    tf8 = F / (k8["ms_avg"] * 1e-3) / 1e12
+    tf8_e2e = F / ((k8["ms_avg"] + kprep["ms_avg"]) * 1e-3) / 1e12
+    pbytes = prep_bytes(B, H, N, d)
+    prep_gbs = pbytes / (kprep["ms_avg"] * 1e-3) / 1e9
+    kernels = {
+        "fwd16": dict(bound="mfma", achieved=round(tf16, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=round(tf16 / PEAK_BF16_TFLOPS, 4), traffic=traffic_for("fwd16"),
+                      kernel="fwd16_kernel<128, bf16, causal> (bf16 fused forward)", ms=k16["ms_avg"],
+                      units_per_launch=f"{F:.4e} flop (4*B*H*N^2*d/2)"),
+        "fwd8": dict(bound="mfma", achieved=round(tf8, 2), peak=PEAK_8BIT_TFLOPS, unit="TFLOP/s",
+                     frac=round(tf8 / PEAK_8BIT_TFLOPS, 4), traffic=traffic_for("fwd8"),
+                     kernel="fwd8_kernel<128, causal> (INT8 QK^T, FP8 PV fused forward)", ms=k8["ms_avg"],
+                     units_per_launch=f"{F:.4e} flop (4*B*H*N^2*d/2)"),
+        "prep8": dict(bound="hbm", achieved=round(prep_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(prep_gbs / PEAK_HBM_GBS, 4), traffic=traffic_for("prep8"),
+                      kernel="sage8 colstats + finalize + quant (three launches)", ms=kprep["ms_avg"],
+                      units_per_launch=f"{pbytes} bytes (9 per element of Q/K/V)"),
+    }
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    roof = {kk: kernels[dom][kk] for kk in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")}
+    roof["ms_avg"] = kernels[dom]["ms"]
 
     out = {
         "metric": METRIC,
@@ -174,39 +282,75 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{cfg['name']}: B={B} H={H} N={N} d={d} causal bf16 in/out",
-                   "batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": causal},
-        "roofline": {"bound": "mfma", "achieved": round(bf16_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(bf16_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "fwd16_kernel<128,bf16,causal>",
-                     "ms_avg": round(bf16_avg, 4), "ms_median": round(bf16_ms[K // 2], 4)},
-        "paths": {"bf16": {"ms": round(bf16_avg, 4), "tflops": round(bf16_tflops, 2),
-                           "frac_of_peak": round(bf16_tflops / PEAK_BF16_TFLOPS, 4)}},
+        "dtype": "bf16 + int8/fp8(e4m3)",
+        "data": "synthetic (seeded N(0,1) Q/K/V, no dataset)",
+        "config": {"workload": f"{cfg['name']}: B={B} H={H} N={N} d={d} causal, bf16 in/out; "
+                               "step = bf16 forward + 8-bit prep + 8-bit forward",
+                   "batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": causal,
+                   "cache_flush": False},
+        "roofline": roof,
+        "kernels": {n: {kk: vv for kk, vv in kv.items()} for n, kv in kernels.items()},
+        "per_kernel_ms": {"fwd16": k16, "prep8": kprep, "fwd8": k8},
+        "paths": {
+            "bf16": {"tflops": round(tf16, 2), "frac_of_peak": round(tf16 / PEAK_BF16_TFLOPS, 4)},
+            "sage8": {"tflops_attention": round(tf8, 2), "frac_of_8bit_peak": round(tf8 / PEAK_8BIT_TFLOPS, 4),
+                      "tflops_prep_plus_attention": round(tf8_e2e, 2),
+                      "speedup_vs_bf16_attention": round(tf8 / tf16, 3),
+                      "speedup_vs_bf16_end_to_end": round(tf8_e2e / tf16, 3)},
+        },
     }
 
     if not args.no_extra:
-        extra = {}
-        for cid in (3, 5):
-            c2, i2 = workloads.config_inputs(cid)
-            q2, k2, v2 = (i2[n].to(dev) for n in ("q", "k", "v"))
-            b2 = i2["bias"].to(dev) if i2["bias"] is not None else None
-            F2 = workloads.flops(c2["B"], c2["H"], c2["N"], c2["d"], c2["causal"])
+        out["workloads"] = extra_workloads(attn, workloads, stream, dev)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores)")
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def extra_workloads(attn, workloads, stream, dev):
+    """The long-context, 8-bit-outlier and DiT-gated workloads at full size:
+    10 timed launches per path after 2 warm-ups."""
+    import torch
+    extra = {}
+    for cid in (3, 4, 5):
+        c2, i2 = workloads.config_inputs(cid)
+        log(f"workload {c2['name']}")
+        q2, k2, v2 = (i2[n].to(dev) for n in ("q", "k", "v"))
+        b2 = i2["bias"].to(dev) if i2["bias"] is not None else None
+        del i2
+        F2 = workloads.flops(c2["B"], c2["H"], c2["N"], c2["d"], c2["causal"])
+        res = {}
+        if cid != 4:
             fn = lambda: attn.fwd(q2, k2, v2, causal=c2["causal"], bias=b2)  # noqa: E731
             for _ in range(2):
                 fn()
-            avg, med, mn = _time_launches(fn, 10, stream)
-            extra[f"{c2['name']} bf16"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4),
-                                           "tflops": round(F2 / (avg * 1e-3) / 1e12, 2),
-                                           "frac_of_peak": round(F2 / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-            del q2, k2, v2, b2
-            torch.cuda.empty_cache()
-        out["workloads"] = extra
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+            st = _stats(_time_launches(fn, 10, stream))
+            tf = F2 / (st["ms_avg"] * 1e-3) / 1e12
+            res["bf16"] = {**st, "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        ws = attn.sage8_prep(q2, k2, v2).workspace
+        prep = attn.Sage8Prepared(ws, tuple(q2.shape), q2.dtype)
+        fp = lambda: attn.sage8_prep(q2, k2, v2, workspace=ws)  # noqa: E731
+        f8 = lambda: attn.fwd_sage8(prep, causal=c2["causal"], bias=b2)  # noqa: E731
+        for _ in range(2):
+            fp()
+            f8()
+        sp = _stats(_time_launches(fp, 10, stream))
+        s8 = _stats(_time_launches(f8, 10, stream))
+        tf8 = F2 / (s8["ms_avg"] * 1e-3) / 1e12
+        tfe = F2 / ((s8["ms_avg"] + sp["ms_avg"]) * 1e-3) / 1e12
+        res["sage8"] = {"attention": {**s8, "tflops": round(tf8, 2), "frac_of_8bit_peak": round(tf8 / PEAK_8BIT_TFLOPS, 4)},
+                        "prep": {**sp, "GBs": round(prep_bytes(*q2.shape) / (sp["ms_avg"] * 1e-3) / 1e9, 1)},
+                        "tflops_prep_plus_attention": round(tfe, 2)}
+        if "bf16" in res:
+            res["sage8"]["speedup_vs_bf16_attention"] = round(tf8 / res["bf16"]["tflops"], 3)
+            res["sage8"]["speedup_vs_bf16_end_to_end"] = round(tfe / res["bf16"]["tflops"], 3)
+        extra[f"{c2['name']}: B={c2['B']} H={c2['H']} N={c2['N']} d={c2['d']} "
+              f"{'causal' if c2['causal'] else 'non-causal'}{' +gate bias' if b2 is not None else ''}"] = res
+        del q2, k2, v2, b2, ws, prep
+        torch.cuda.empty_cache()
+    return extra
 
 
 if __name__ == "__main__":

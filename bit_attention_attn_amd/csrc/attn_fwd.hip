@@ -5,15 +5,13 @@
 // with a running maximum and running sum; one fused kernel that writes only
 // the final result) without forming the N x N score matrix anywhere.
 //
-// Work split: one workgroup of NW waves per (b, h, query tile); each wave
+// Work split: a workgroup of NW waves per (b, h, query tile); each wave
 // owns QS x 32 queries (QS MFMA column tiles, so one K or V operand read from
 // LDS feeds QS matrix instructions).  Two waves share each SIMD (from two
 // workgroups when NW = 4, from one when NW = 8), so one wave's softmax runs
 // on the vector ALU while the other's products run on the matrix cores.
 // Keys and values stream through LDS in blocks of 64; the global loads of a
-// future block are in flight while the current one is computed.  With PIPE
-// the S^T product of block j+1 is issued in the same stretch of code as the
-// softmax of block j, so one wave can also overlap the two by itself.
+// future block are in flight while the current one is computed.
 //
 // Per key block and wave:
 //   S^T = K Q^T (32x32x16 MFMA, fp32 accumulation): one query per lane
@@ -29,13 +27,16 @@
 //       the B operand (the key order inside a lane is a permutation applied
 //       to both operands); V^T is read from the row-major V tile with the
 //       transposing LDS read.
-// The output is normalised once, staged through LDS and written with
-// coalesced 16-byte stores.
+// The output is normalised once and stored straight from the accumulators.
+// The grid is persistent: as many workgroups as fit on the device at once,
+// each looping over work items in a balanced heavy-first order.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
 #include <math.h>
 #include <stdlib.h>
+
+#include <atomic>
 
 namespace attn {
 namespace {
@@ -43,15 +44,14 @@ namespace {
 constexpr int kBN = 64;       // keys per block
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-// Tiling: QS query tiles of 32 per wave, NW waves per workgroup, PIPE as
-// above.  Buffers: without PIPE, block j+1 (K and V) is loaded during block
-// j; with PIPE, K of block j+2 and V of block j+1 are.
-template <int QS, int NW, bool PIPE>
+// Tiling: QS query tiles of 32 per wave, NW waves per workgroup.  Block
+// j+1 (K and V) is loaded during block j into the other of two buffers.
+template <int QS, int NW>
 struct Tiling {
   static constexpr int kWQ = 32 * QS;            // queries per wave
   static constexpr int kBM = NW * kWQ;           // queries per workgroup
   static constexpr int kThreads = 64 * NW;
-  static constexpr int kKbuf = PIPE ? 3 : 2;
+  static constexpr int kKbuf = 2;
   static constexpr int kVbuf = 2;
 };
 
@@ -64,15 +64,16 @@ struct Fwd16Params {
   const float* bias;
   int N;
   int nq;      // query tiles per head
+  int nbh;     // B*H
   int nb;      // ceil(N/64), bias blocks per side
   int ntiles;  // B*H*nq
   float c;     // scale * log2(e), never 0
   int out_f32;
 };
 
-template <int D, int QS, int NW, bool PIPE>
+template <int D, int QS, int NW>
 struct Fwd16Smem {
-  using T = Tiling<QS, NW, PIPE>;
+  using T = Tiling<QS, NW>;
   // Padded rows.  K: 16 bytes of padding, so the 16-byte operand reads of 16
   // consecutive rows fall on distinct banks.  V: the transposing reads touch
   // 4 consecutive rows x 64 bytes per half wave; a row stride of 288 bytes
@@ -82,15 +83,13 @@ struct Fwd16Smem {
   static constexpr int kVRow = D == 128 ? D + 16 : D + 32;
   static constexpr int kKTile = kBN * kKRow;
   static constexpr int kVTile = kBN * kVRow;
-  static constexpr int kLoop = T::kKbuf * kKTile + T::kVbuf * kVTile;
-  static constexpr int kStage = NW * T::kWQ * (D + 4) * 2;  // fp32 output staging, 16-bit units
-  static constexpr int kElems = kLoop > kStage ? kLoop : kStage;
+  static constexpr int kElems = T::kKbuf * kKTile + T::kVbuf * kVTile;
 };
 
-template <int D, bool BF16, bool CAUSAL, int QS, int NW, bool PIPE>
+template <int D, bool BF16, bool CAUSAL, int QS, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
-  using TL = Tiling<QS, NW, PIPE>;
-  using S = Fwd16Smem<D, QS, NW, PIPE>;
+  using TL = Tiling<QS, NW>;
+  using S = Fwd16Smem<D, QS, NW>;
   constexpr int kWQ = TL::kWQ, kBM = TL::kBM, kThreads = TL::kThreads;
   constexpr int kKbuf = TL::kKbuf, kVbuf = TL::kVbuf;
   constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
@@ -108,10 +107,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, p.ntiles);
-  const int bh = tile / p.nq;
-  int qt = tile - bh * p.nq;
-  if (CAUSAL) qt = p.nq - 1 - qt;  // heaviest tiles first
+  // Persistent loop over (b, h, query tile) work items.  Workgroups are
+  // handed to the 8 XCDs round-robin, so workgroup w runs on XCD w % 8; the
+  // items are split into 8 contiguous queues (head-major, so the few heads an
+  // XCD works on at a time keep their keys and values in its L2), and queue
+  // w % 8 is served by the n workgroups of that XCD: in round k, slot s takes
+  // item k*n + s, or k*n + n-1-s in odd rounds, which balances the
+  // heavy-first causal tiles across slots.
+  const int G = gridDim.x, w = blockIdx.x;
+  const bool split = (p.ntiles & 7) == 0 && (G & 7) == 0;
+  const int nslot = split ? G >> 3 : G;
+  const int slot = split ? w >> 3 : w;
+  const int qlen = split ? p.ntiles >> 3 : p.ntiles;
+  const int qbase = split ? (w & 7) * qlen : 0;
+  for (int round = 0;; ++round) {
+  const int jq = round * nslot + ((round & 1) ? nslot - 1 - slot : slot);
+  if (jq >= qlen) break;
+  const int item = qbase + jq;
+  const int bh = item / p.nq;
+  const int tq = item - bh * p.nq;
+  const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles of a head first
   const int N = p.N;
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kWQ;
@@ -275,8 +290,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   // scores are +-inf, so c*S is -inf and P is 0 (c is never 0: the host
   // passes the smallest normal float for a zero scale).  The row sum adds
   // the rounded P values the product uses.
-  auto exp_pv = [&](int buf, f32x16_t (&s)[2][QS], const float (&kc)[QS]) {
-    u32x4_t pb[4][QS];
+  u32x4_t pb[4][QS];
+  auto softmax_p = [&](f32x16_t (&s)[2][QS], const float (&kc)[QS]) {
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       float lsum = 0.f;
@@ -295,6 +310,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
       }
       l_run[qs] += lsum;
     }
+  };
+  auto pv = [&](int buf) {
     const uint16_t* Vs = vbase_lds + buf * kVTile + vkey * kVRow + vcol;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -310,140 +327,94 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
     }
   };
 
-  if constexpr (!PIPE) {
-    // ---- block j+1 loads while block j computes
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  __syncthreads();
+  f32x16_t sc[2][QS];
+  // ---- block j+1 loads while block j computes
+  for (int j = 0; j < nkb; ++j) {
+    const bool more = j + 1 < nkb;
+    if (more) {
+      load_k(j + 1);
+      load_v(j + 1);
+    }
+    if (wave_has_rows && j <= wave_last) {
+      qk(j & 1, sc);
+      if (needs_mask(j)) apply_mask(j, sc);
+      float kc[QS];
+      block_max(j, sc, kc);
+      softmax_p(sc, kc);
+      pv(j & 1);
+    }
+    if (more) {
+      store_k((j + 1) & 1);
+      store_v((j + 1) & 1);
+    }
     __syncthreads();
-    f32x16_t sc[2][QS];
-    for (int j = 0; j < nkb; ++j) {
-      const bool more = j + 1 < nkb;
-      if (more) {
-        load_k(j + 1);
-        load_v(j + 1);
-      }
-      if (wave_has_rows && j <= wave_last) {
-        qk(j & 1, sc);
-        if (needs_mask(j)) apply_mask(j, sc);
-        float kc[QS];
-        block_max(j, sc, kc);
-        exp_pv(j & 1, sc, kc);
-      }
-      if (more) {
-        store_k((j + 1) & 1);
-        store_v((j + 1) & 1);
-      }
-      __syncthreads();
-    }
-  } else {
-    // ---- pipelined: in iteration j, S of block j+1 is computed next to the
-    // softmax and P V of block j.  K of block j+2 and V of block j+1 load
-    // meanwhile; K buffers rotate over 3, V over 2.  A buffer is overwritten
-    // only after the barrier that follows its last read.
-    load_k(0);
-    store_k(0);
-    if (nkb > 1) {
-      load_k(1);
-      store_k(1);
-    }
-    load_v(0);
-    store_v(0);
-    __syncthreads();
-    f32x16_t sa[2][QS], sb[2][QS];
-    if (wave_has_rows) qk(0, sa);
-    auto step = [&](int j, f32x16_t (&s_cur)[2][QS], f32x16_t (&s_nxt)[2][QS]) {
-      const bool kmore = j + 2 < nkb, vmore = j + 1 < nkb;
-      if (kmore) load_k(j + 2);
-      if (vmore) load_v(j + 1);
-      const bool act = wave_has_rows && j <= wave_last;
-      if (act && needs_mask(j)) apply_mask(j, s_cur);
-      if (wave_has_rows && j + 1 <= wave_last) qk((j + 1) % kKbuf, s_nxt);
-      if (act) {
-        float kc[QS];
-        block_max(j, s_cur, kc);
-        exp_pv(j % kVbuf, s_cur, kc);
-      }
-      if (kmore) store_k((j + 2) % kKbuf);
-      if (vmore) store_v((j + 1) % kVbuf);
-      __syncthreads();
-    };
-    int j = 0;
-    for (; j + 1 < nkb; j += 2) {
-      step(j, sa, sb);
-      step(j + 1, sb, sa);
-    }
-    if (j < nkb) step(j, sa, sb);
   }
 
-  // ---- epilogue: normalise, LSE, stage through LDS, coalesced stores
-  float inv[QS];
+  // ---- epilogue: normalise, LSE, stores straight from the accumulators
+  // (lane (l32, hf) holds d = 32dt + 8g + 4hf .. +3 of query qw0 + 32qs + l32)
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
     const float l_tot = xor32_sum(l_run[qs]);
-    inv[qs] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int qi = qw0 + 32 * qs + l32;
-    if (p.lse != nullptr && hf == 0 && qi < N)
-      p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-
-  if (p.out_f32) {
-    constexpr int kSt = D + 4;  // floats per staged row
-    float* st = reinterpret_cast<float*>(smem) + wave * kWQ * kSt;
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
+    if (qi < N) {
+      if (p.lse != nullptr && hf == 0)
+        p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      const size_t orow = head + (size_t)qi * D;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * dt + 8 * g + 4 * hf;
-          const float iv = inv[qs];
-          f32x4_t w = {o[dt][qs][4 * g] * iv, o[dt][qs][4 * g + 1] * iv, o[dt][qs][4 * g + 2] * iv,
-                       o[dt][qs][4 * g + 3] * iv};
-          *(f32x4_t*)(st + (32 * qs + l32) * kSt + d) = w;
+          const f32x4_t w4 = {o[dt][qs][4 * g] * inv, o[dt][qs][4 * g + 1] * inv, o[dt][qs][4 * g + 2] * inv,
+                              o[dt][qs][4 * g + 3] * inv};
+          if (p.out_f32) {
+            *(f32x4_t*)(reinterpret_cast<float*>(p.o) + orow + d) = w4;
+          } else {
+            *(u32x2_t*)(reinterpret_cast<uint16_t*>(p.o) + orow + d) =
+                u32x2_t{pack2<BF16>(w4[0], w4[1]), pack2<BF16>(w4[2], w4[3])};
+          }
         }
-    __syncthreads();
-    float* O = reinterpret_cast<float*>(p.o) + head;
-    constexpr int kCh = D / 4;  // 16-byte chunks per row
-#pragma unroll
-    for (int it = 0; it < kWQ * kCh / 64; ++it) {
-      const int idx = lane + 64 * it;
-      const int row = idx / kCh, ch = idx % kCh;
-      const int q = qw0 + row;
-      if (q < N) *(f32x4_t*)(O + (size_t)q * D + 4 * ch) = *(const f32x4_t*)(st + row * kSt + 4 * ch);
-    }
-  } else {
-    constexpr int kSt = D + 8;  // 16-bit elements per staged row
-    uint16_t* st = smem + wave * kWQ * kSt;
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * dt + 8 * g + 4 * hf;
-          const float iv = inv[qs];
-          u32x2_t w = {pack2<BF16>(o[dt][qs][4 * g] * iv, o[dt][qs][4 * g + 1] * iv),
-                       pack2<BF16>(o[dt][qs][4 * g + 2] * iv, o[dt][qs][4 * g + 3] * iv)};
-          *(u32x2_t*)(st + (32 * qs + l32) * kSt + d) = w;
-        }
-    __syncthreads();
-    uint16_t* O = reinterpret_cast<uint16_t*>(p.o) + head;
-    constexpr int kCh = D / 8;
-#pragma unroll
-    for (int it = 0; it < kWQ * kCh / 64; ++it) {
-      const int idx = lane + 64 * it;
-      const int row = idx / kCh, ch = idx % kCh;
-      const int q = qw0 + row;
-      if (q < N) *(u32x4_t*)(O + (size_t)q * D + 8 * ch) = *(const u32x4_t*)(st + row * kSt + 8 * ch);
     }
   }
+  }  // work items
 }
 
-template <int D, bool BF16, bool CAUSAL, int QS, int NW, bool PIPE>
+// Grid for a persistent launch: the number of workgroups of this kernel that
+// are resident at once on the current device (CUs x workgroups per CU),
+// rounded down to a multiple of 8 (one slot per XCD), at most the number of
+// work items.  Cached per kernel and device.
+int persistent_grid(const void* kernel, int threads, int items) {
+  struct Entry { const void* k; int dev; int slots; };
+  static Entry cache[64];
+  static std::atomic<int> used{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int slots = 0;
+  const int n = used.load(std::memory_order_acquire);
+  for (int i = 0; i < n && i < 64; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev) slots = cache[i].slots;
+  if (slots == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    slots = per_cu * cus;
+    if (slots >= 8) slots &= ~7;
+    if (slots <= 0) return -1;
+    const int i = used.fetch_add(1, std::memory_order_acq_rel);
+    if (i < 64) cache[i] = Entry{kernel, dev, slots};
+  }
+  return items < slots ? items : slots;
+}
+
+template <int D, bool BF16, bool CAUSAL, int QS, int NW>
 hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
-  using TL = Tiling<QS, NW, PIPE>;
+  using TL = Tiling<QS, NW>;
   Fwd16Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -454,6 +425,7 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   p.N = a.N;
   p.nq = (a.N + TL::kBM - 1) / TL::kBM;
   p.nb = (a.N + 63) / 64;
+  p.nbh = a.B * a.H;
   p.ntiles = a.B * a.H * p.nq;
   // c = scale*log2(e).  A zero scale is passed as the smallest normal float:
   // masked scores are +-inf and inf*0 would be NaN, while any finite score
@@ -461,18 +433,26 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   p.c = (float)((double)a.scale * 1.4426950408889634);
   if (p.c == 0.f) p.c = 1.17549435e-38f;
   p.out_f32 = a.out_kind == kOutF32;
-  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW, PIPE>), dim3(p.ntiles), dim3(TL::kThreads), 0,
-                     stream, p);
+  // Causal tiles differ in cost, so a persistent grid with the balanced
+  // heavy-first order pays (measured +7% at 4x32x4096, d = 128); equal-cost
+  // non-causal tiles run one workgroup per item (persistent was 5% slower).
+  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW>),
+                                            TL::kThreads, p.ntiles)
+                          : p.ntiles;
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW>), dim3(grid), dim3(TL::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 // Tiling per head dimension.  ATTN_FWD16_TILING selects another variant, to
-// compare them on the GPU.  Measured on MI355X (TFLOPS):
-//   d = 128 (prefill 4x32x4096 / long-context 1x32x32768, causal):
-//     QS1 NW8 (default) 688 / 1076; QS1 NW4 688 / 1003; QS1 NW8 PIPE 653 /
-//     1030; QS1 NW4 PIPE 497 / 634 (LDS allows one workgroup per CU).
-//   d = 64 (DiT-gated 2x24x16384, bias): QS2 NW4 (default) 923; QS1 NW4 854;
-//     QS1 NW8 PIPE 780; QS2 NW4 PIPE 583 (spills).
+// compare them on the GPU.  Measured on MI355X (TFLOPS; prefill 4x32x4096 /
+// long-context 1x32x32768, causal, d = 128; DiT-gated 2x24x16384, d = 64):
+//   d = 128: QS1 NW8 (default) 743 / 1085; QS1 NW4 688 / 1003.  Tried and
+//     dropped: software-pipelined S of block j+1 next to the softmax of block j
+//     (653 / 1030); two wave groups in ping-pong phases (596 / 950: a product
+//     phase has one matrix-issuing wave per SIMD, LDS waits are exposed);
+//     waves staggered by one product (701 / 983, and register spills).
+//   d = 64: QS2 NW4 (default) 936-950; QS1 NW4 854.
 int tiling_override() {
   static const int v = [] {
     const char* e = getenv("ATTN_FWD16_TILING");
@@ -485,17 +465,11 @@ template <bool BF16, bool CAUSAL>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   const int t = tiling_override();
   if (a.d == 64) {
-    switch (t) {
-      case 1: return launch_impl<64, BF16, CAUSAL, 1, 4, false>(a, stream);
-      case 2: return launch_impl<64, BF16, CAUSAL, 1, 8, true>(a, stream);
-      default: return launch_impl<64, BF16, CAUSAL, 2, 4, false>(a, stream);
-    }
+    if (t == 1) return launch_impl<64, BF16, CAUSAL, 1, 4>(a, stream);
+    return launch_impl<64, BF16, CAUSAL, 2, 4>(a, stream);
   }
-  switch (t) {
-    case 1: return launch_impl<128, BF16, CAUSAL, 1, 4, false>(a, stream);
-    case 2: return launch_impl<128, BF16, CAUSAL, 1, 8, true>(a, stream);
-    default: return launch_impl<128, BF16, CAUSAL, 1, 8, false>(a, stream);
-  }
+  if (t == 1) return launch_impl<128, BF16, CAUSAL, 1, 4>(a, stream);
+  return launch_impl<128, BF16, CAUSAL, 1, 8>(a, stream);
 }
 
 }  // namespace

@@ -110,12 +110,49 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Workgroup -> work item: consecutive work items are placed on the same XCD
-// (hardware hands workgroups to the 8 XCDs round-robin), so the query tiles
-// of one head share that XCD's L2 while they stream the same keys/values.
-__device__ __forceinline__ int xcd_remap(int wg, int n) {
-  if ((n & 7) != 0) return wg;
-  return (wg & 7) * (n >> 3) + (wg >> 3);
+// Work items (b*h, query tile) of a (possibly persistent) grid.  Workgroups
+// are handed to the 8 XCDs round-robin, so workgroup w runs on XCD w % 8.
+// When B*H is a multiple of 8, XCD x owns the heads x, x+8, ... (so a head's
+// keys and values stay in one L2) and its queue is served by the n
+// workgroups on it: in round k, slot s takes queue entry k*n + s, or
+// k*n + n-1-s in odd rounds.  When the workgroups loop over several causal
+// items, the entries run over tile rank first (heaviest tiles of all the
+// XCD's heads, then the next rank...), so the costs fall monotonically and
+// the alternating order balances the slots; otherwise the entries run head
+// by head (the few heads in flight keep their keys and values in L2), which
+// with one workgroup per item is the plain XCD-grouped order.
+struct WorkQueue {
+  int nslot, slot, qlen, xcd, heads;  // heads per queue (0: one global queue)
+};
+__device__ __forceinline__ WorkQueue work_queue(int nbh, int nq) {
+  const int G = gridDim.x, w = blockIdx.x;
+  const bool split = (nbh & 7) == 0 && (G & 7) == 0;
+  WorkQueue q;
+  q.nslot = split ? G >> 3 : G;
+  q.slot = split ? w >> 3 : w;
+  q.heads = split ? nbh >> 3 : 0;
+  q.qlen = (split ? q.heads : nbh) * nq;
+  q.xcd = w & 7;
+  return q;
+}
+// Returns false when the workgroup is done; else the head bh and the tile
+// rank r (0 = first in order; causal callers process tile nq-1-r).
+template <bool CAUSAL>
+__device__ __forceinline__ bool work_item(const WorkQueue& q, int round, int nq, int& bh, int& r) {
+  const int j = round * q.nslot + ((round & 1) ? q.nslot - 1 - q.slot : q.slot);
+  if (j >= q.qlen) return false;
+  if (q.heads == 0) {  // one global queue, head-major
+    bh = j / nq;
+    r = j - bh * nq;
+  } else if (CAUSAL && q.nslot < q.qlen) {  // persistent: rank-major over the XCD's heads
+    r = j / q.heads;
+    bh = q.xcd + 8 * (j - r * q.heads);
+  } else {  // head-major over the XCD's heads
+    const int hl = j / nq;
+    r = j - hl * nq;
+    bh = q.xcd + 8 * hl;
+  }
+  return true;
 }
 
 }  // namespace attn

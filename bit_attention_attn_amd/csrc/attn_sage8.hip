@@ -292,6 +292,7 @@ struct Fwd8Params {
   const float* bias;
   int N, np, nblk;
   int nq;      // query tiles per head
+  int nbh;     // B*H
   int nb;      // ceil(N/64), bias blocks per side
   int ntiles;  // B*H*nq
   float c;     // scale * log2(e), never 0
@@ -326,7 +327,7 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
+__global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   using S = Fwd8Smem<D>;
   constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
   constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
@@ -342,10 +343,13 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, p.ntiles);
-  const int bh = tile / p.nq;
-  int qt = tile - bh * p.nq;
-  if (CAUSAL) qt = p.nq - 1 - qt;
+  // Loop over (b, h, query tile) work items (work_queue: per-XCD queues,
+  // balanced heavy-first order when the grid is persistent).
+  const WorkQueue wq = work_queue(p.nbh, p.nq);
+  for (int round = 0;; ++round) {
+  int bh, tq;
+  if (!work_item<CAUSAL>(wq, round, p.nq, bh, tq)) break;
+  const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
   const int N = p.N;
   const int q0 = qt * kBM8;
   const int qw0 = q0 + wave * 32;
@@ -516,11 +520,11 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
       p.lse[(size_t)bh * N + qi] =
           l_tot > 0.f ? (m_run + __log2f(l_tot) - kPlog + c * (sqw * dot)) * kLn2 : -INFINITY;
   }
-  if (qi >= N) return;
   // lane (l32, hf) holds d = 32dt + 8g + 4hf + u of query qi: 16-byte (fp32)
   // or 8-byte (fp16 / bf16) stores straight from the accumulators
   const float* svh = p.sv + (size_t)bh * D;
   const size_t orow = ((size_t)bh * N + qi) * D;
+  if (qi < N)
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -537,6 +541,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd8_kernel(Fwd8Params p) {
         *(u32x2_t*)(reinterpret_cast<uint16_t*>(p.o) + orow + d) = u32x2_t{pack2<false>(w[0], w[1]), pack2<false>(w[2], w[3])};
       }
     }
+  }  // work items
 }
 
 template <int D, bool CAUSAL>
@@ -559,11 +564,18 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   p.np = L.nblk * kQB;
   p.nq = (a.N + kBM8 - 1) / kBM8;
   p.nb = (a.N + 63) / 64;
+  p.nbh = a.B * a.H;
   p.ntiles = a.B * a.H * p.nq;
   p.c = (float)((double)a.scale * 1.4426950408889634);
   if (p.c == 0.f) p.c = 1.17549435e-38f;
   p.out_kind = a.out_kind;
-  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(p.ntiles), dim3(kThreads8), 0, stream, p);
+  // persistent grid for causal shapes (tiles differ in cost), one workgroup
+  // per tile otherwise
+  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL>), kThreads8,
+                                            p.ntiles)
+                          : p.ntiles;
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }
 

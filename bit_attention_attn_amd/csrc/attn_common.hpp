@@ -110,6 +110,16 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer access: base and size in scalar registers, a per-lane byte
+// offset and a uniform byte offset; loads past `bytes` return zeros.  The
+// third descriptor word selects 32-bit data (required for untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Work items (b*h, query tile) of a (possibly persistent) grid.  Workgroups
 // are handed to the 8 XCDs round-robin, so workgroup w runs on XCD w % 8.
 // When B*H is a multiple of 8, XCD x owns the heads x, x+8, ... (so a head's

@@ -141,25 +141,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   const bool wave_has_rows = qw0 < N;
 
   // ---- loader: a 64 x D tile is 64*D/8 chunks of 16 bytes, staged through
-  // registers; key rows past N read row N-1 (masked later), so every load is
-  // unconditional.
+  // registers.  Chunk tid + i*threads of block kb sits at byte
+  // 16*tid + (kb*64*D*2 + 16*i*threads) of the head: a buffer load with one
+  // per-lane offset and a uniform one; key rows past N read zeros (masked
+  // later), so every load is unconditional.
   constexpr int kNst = kBN * kCpr / kThreads;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V, (uint32_t)N * D * 2);
+  const uint32_t voff = 16u * tid;
   u32x4_t kst[kNst], vst[kNst];
   auto load_k = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
-      const int key = min(kb * kBN + row, N - 1);
-      kst[i] = *(const u32x4_t*)(K + (size_t)key * D + ch * 8);
-    }
+    for (int i = 0; i < kNst; ++i) kst[i] = buffer_load16(krs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
   };
   auto load_v = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
-      const int key = min(kb * kBN + row, N - 1);
-      vst[i] = *(const u32x4_t*)(V + (size_t)key * D + ch * 8);
-    }
+    for (int i = 0; i < kNst; ++i) vst[i] = buffer_load16(vrs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
   };
   auto store_k = [&](int buf) {
     uint16_t* ks = kbase_lds + buf * kKTile;

@@ -370,15 +370,19 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   const int wave_last = CAUSAL ? min(nkb - 1, qw0 / kQB) : nkb - 1;
   const bool wave_has_rows = qw0 < N;
 
-  // loader: K tile 64*D bytes and V tile D*64 bytes, 16-byte chunks
+  // loader: K tile 64*D bytes and V tile D*64 bytes, 16-byte chunks; chunk
+  // tid + i*threads of block kb is at byte 16*tid + (kb*64*D + 16*i*threads)
+  // of the head (buffer loads: one per-lane offset, a uniform one)
   constexpr int kNld = kQB * D / 16 / kThreads8;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kq, (uint32_t)p.np * D);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vq, (uint32_t)p.np * D);
+  const uint32_t voff = 16u * tid;
   u32x4_t kst[kNld], vst[kNld];
   auto load_kv = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < kNld; ++i) {
-      const int idx = tid + i * kThreads8;
-      kst[i] = *(const u32x4_t*)(Kq + (size_t)kb * kQB * D + idx * 16);
-      vst[i] = *(const u32x4_t*)(Vq + (size_t)kb * kQB * D + idx * 16);
+      kst[i] = buffer_load16(krs, voff, kb * kQB * D + 16 * i * kThreads8);
+      vst[i] = buffer_load16(vrs, voff, kb * kQB * D + 16 * i * kThreads8);
     }
   };
   auto store_kv = [&](int buf) {

@@ -9,8 +9,9 @@
 // Preparation (HBM-bound, three kernels):
 //   colstats  per 256-token chunk of each (b,h): fp64 column sums of K and
 //             fp32 column absmax of V.
-//   finalize  per (b,h): kmean = (sum of chunk sums) / N rounded once to
-//             fp32; V scale = absmax/448 and its inverse 448/absmax (1 if 0).
+//   finalize  per (b,h), 256 threads: kmean = (sum of chunk sums) / N rounded
+//             once to fp32; V scale = absmax/448 and its inverse 448/absmax
+//             (1 if 0).
 //   quant     per 64-row block: Q and K - kmean to INT8 with one fp32 scale
 //             per block (scale = absmax/127, code = rne(x * (127/absmax)),
 //             clamp +-127); V to e4m3 (code = e4m3_rne(v * inv)), written
@@ -138,21 +139,49 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
   }
 }
 
-// ---- finalize: grid B*H, D threads --------------------------------------
+// ---- finalize: grid B*H, 256 threads.  Thread (g, c) adds the partials of
+// chunks g, g + 256/D, ... for channel c with two independent accumulators,
+// then the groups combine through LDS.  The fp64 partials are sums of fp16 /
+// bf16 values, which fp64 adds exactly at these magnitudes, so the order of
+// the additions does not change kmean.
 template <int D>
-__global__ __launch_bounds__(D) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
+__global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
                                                     int nchunk, int N, float* __restrict__ kmean,
                                                     float* __restrict__ sv, float* __restrict__ vinv) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  double s = 0.0;
-  float m = 0.f;
-  for (int ch = 0; ch < nchunk; ++ch) {
-    s += kpart[((size_t)bh * nchunk + ch) * D + c];
-    m = fmaxf(m, vpart[((size_t)bh * nchunk + ch) * D + c]);
+  constexpr int kG = 256 / D;
+  __shared__ double ssum[kG][D];
+  __shared__ float smax[kG][D];
+  const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
+  const double* kp = kpart + (size_t)bh * nchunk * D + c;
+  const float* vp = vpart + (size_t)bh * nchunk * D + c;
+  double s0 = 0.0, s1 = 0.0;
+  float m0 = 0.f, m1 = 0.f;
+  int ch = g;
+  for (; ch + kG < nchunk; ch += 2 * kG) {
+    s0 += kp[(size_t)ch * D];
+    s1 += kp[(size_t)(ch + kG) * D];
+    m0 = fmaxf(m0, vp[(size_t)ch * D]);
+    m1 = fmaxf(m1, vp[(size_t)(ch + kG) * D]);
   }
-  kmean[(size_t)bh * D + c] = (float)(s / (double)N);
-  sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
-  vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
+  if (ch < nchunk) {
+    s0 += kp[(size_t)ch * D];
+    m0 = fmaxf(m0, vp[(size_t)ch * D]);
+  }
+  ssum[g][c] = s0 + s1;
+  smax[g][c] = fmaxf(m0, m1);
+  __syncthreads();
+  if (g == 0) {
+    double s = 0.0;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      s += ssum[i][c];
+      m = fmaxf(m, smax[i][c]);
+    }
+    kmean[(size_t)bh * D + c] = (float)(s / (double)N);
+    sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
+  }
 }
 
 // Block-wide max of a non-negative float over 256 threads (4 waves).
@@ -261,7 +290,7 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
   hipLaunchKernelGGL((sage8_colstats<D, BF16>), dim3(L.nchunk, bh), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N,
                      reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk);
-  hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3(D), 0, stream,
+  hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3(256), 0, stream,
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
                      reinterpret_cast<float*>(w + L.vinv));

@@ -107,12 +107,17 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
     acc[e] = 0.0;
     mx[e] = 0.f;
   }
+  // buffer loads: rows past N read zeros, which change neither the sums nor
+  // the absolute maxima, so the row loop has a fixed trip count
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k + head, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v + head, (uint32_t)N * D * 2);
+  const uint32_t voff = 16u * tid;  // row rg, chunk ch of a pass
   const int n0 = chunk * kChunk;
-  for (int r = rg; r < kChunk; r += kRows) {
-    const int n = n0 + r;
-    if (n >= N) break;
-    const u32x4_t kx = *(const u32x4_t*)(k + head + (size_t)n * D + ch * 8);
-    const u32x4_t vx = *(const u32x4_t*)(v + head + (size_t)n * D + ch * 8);
+#pragma unroll
+  for (int i = 0; i < kChunk / kRows; ++i) {
+    const uint32_t soff = (uint32_t)(n0 + i * kRows) * D * 2;
+    const u32x4_t kx = buffer_load16(krs, voff, soff);
+    const u32x4_t vx = buffer_load16(vrs, voff, soff);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint16_t kb = (uint16_t)(kx[e >> 1] >> (16 * (e & 1)));

@@ -46,12 +46,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 539997696,
-              "sha256": "8b5e33c5d06b06cbf6436c656a7dd63dc19253a52bcadf57f96b5741368794ce"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 338315008,
-             "sha256": "556d3a81c37ec833abfe1121213cd6dd7b04eabffe50f91310d7fd57b980f724"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880664576,
-              "sha256": "556d3a81c37ec833abfe1121213cd6dd7b04eabffe50f91310d7fd57b980f724"},
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 681654374,
+              "sha256": "77ffcc7c4d3ff892ab77661578637498400c46cd324031bb1ccb7e5c9556f956"},
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 336086855,
+             "sha256": "cb55c4ee7984d54f45e182019a6962e67c12076cb20db95bb4bef2e40e9a5b42"},
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880731966,
+              "sha256": "cb55c4ee7984d54f45e182019a6962e67c12076cb20db95bb4bef2e40e9a5b42"},
 }
 
 

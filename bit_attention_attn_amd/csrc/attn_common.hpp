@@ -122,46 +122,35 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
 
 // Work items (b*h, query tile) of a (possibly persistent) grid.  Workgroups
 // are handed to the 8 XCDs round-robin, so workgroup w runs on XCD w % 8.
-// When B*H is a multiple of 8, XCD x owns the heads x, x+8, ... (so a head's
-// keys and values stay in one L2) and its queue is served by the n
-// workgroups on it: in round k, slot s takes queue entry k*n + s, or
-// k*n + n-1-s in odd rounds.  When the workgroups loop over several causal
-// items, the entries run over tile rank first (heaviest tiles of all the
-// XCD's heads, then the next rank...), so the costs fall monotonically and
-// the alternating order balances the slots; otherwise the entries run head
-// by head (the few heads in flight keep their keys and values in L2), which
-// with one workgroup per item is the plain XCD-grouped order.
+// When B*H is a multiple of 8, XCD x owns the heads x, x+8, ... (a head's
+// keys and values stay in one L2) and serves them head by head, tiles in
+// order (heaviest first for causal callers), with the n workgroups on it as
+// slots: in round k, slot s takes queue entry k*n + s, or k*n + n-1-s in odd
+// rounds.  This pairs entries e and 2n-1-e; when 2n is a multiple of the
+// tiles per head those two tiles cost the same together for every pair, so
+// the slots are balanced (the host makes the grid persistent only then).
+// With one workgroup per item it is the plain XCD-grouped order.
 struct WorkQueue {
-  int nslot, slot, qlen, xcd, heads;  // heads per queue (0: one global queue)
+  int nslot, slot, qlen, xcd, split;
 };
 __device__ __forceinline__ WorkQueue work_queue(int nbh, int nq) {
   const int G = gridDim.x, w = blockIdx.x;
-  const bool split = (nbh & 7) == 0 && (G & 7) == 0;
   WorkQueue q;
-  q.nslot = split ? G >> 3 : G;
-  q.slot = split ? w >> 3 : w;
-  q.heads = split ? nbh >> 3 : 0;
-  q.qlen = (split ? q.heads : nbh) * nq;
+  q.split = (nbh & 7) == 0 && (G & 7) == 0;
+  q.nslot = q.split ? G >> 3 : G;
+  q.slot = q.split ? w >> 3 : w;
+  q.qlen = (q.split ? nbh >> 3 : nbh) * nq;
   q.xcd = w & 7;
   return q;
 }
 // Returns false when the workgroup is done; else the head bh and the tile
-// rank r (0 = first in order; causal callers process tile nq-1-r).
-template <bool CAUSAL>
+// position r within the head (causal callers process tile nq-1-r).
 __device__ __forceinline__ bool work_item(const WorkQueue& q, int round, int nq, int& bh, int& r) {
   const int j = round * q.nslot + ((round & 1) ? q.nslot - 1 - q.slot : q.slot);
   if (j >= q.qlen) return false;
-  if (q.heads == 0) {  // one global queue, head-major
-    bh = j / nq;
-    r = j - bh * nq;
-  } else if (CAUSAL && q.nslot < q.qlen) {  // persistent: rank-major over the XCD's heads
-    r = j / q.heads;
-    bh = q.xcd + 8 * (j - r * q.heads);
-  } else {  // head-major over the XCD's heads
-    const int hl = j / nq;
-    r = j - hl * nq;
-    bh = q.xcd + 8 * hl;
-  }
+  const int hl = j / nq;
+  r = j - hl * nq;
+  bh = q.split ? q.xcd + 8 * hl : hl;
   return true;
 }
 

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   const WorkQueue wq = work_queue(p.nbh, p.nq);
   for (int round = 0;; ++round) {
   int bh, tq;
-  if (!work_item<CAUSAL>(wq, round, p.nq, bh, tq)) break;
+  if (!work_item(wq, round, p.nq, bh, tq)) break;
   const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
   const int N = p.N;
   const int q0 = qt * kBM;
@@ -391,10 +391,11 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   if (p.c == 0.f) p.c = 1.17549435e-38f;
   p.out_f32 = a.out_kind == kOutF32;
   // Causal tiles differ in cost, so a persistent grid with the balanced
-  // heavy-first order pays (measured +7% at 4x32x4096, d = 128); equal-cost
-  // non-causal tiles run one workgroup per item (persistent was 5% slower).
+  // heavy-first order pays where it applies (measured +7% at 4x32x4096,
+  // d = 128); equal-cost non-causal tiles run one workgroup per item
+  // (persistent was 5% slower).
   const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW>),
-                                            TL::kThreads, p.ntiles)
+                                            TL::kThreads, p.nbh, p.nq)
                           : p.ntiles;
   if (grid <= 0) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW>), dim3(grid), dim3(TL::kThreads), 0, stream, p);
@@ -431,12 +432,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Cached per kernel and device.  Returns the item count itself (one workgroup
-// per item) beyond 8 rounds.
-int persistent_grid(const void* kernel, int threads, int items) {
+// Cached per kernel and device.
+int persistent_grid(const void* kernel, int threads, int nbh, int nq) {
   struct Entry { const void* k; int dev; int slots; };
   static Entry cache[64];
   static std::atomic<int> used{0};
+  const int items = nbh * nq;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   int slots = 0;
@@ -453,13 +454,12 @@ int persistent_grid(const void* kernel, int threads, int items) {
     const int i = used.fetch_add(1, std::memory_order_acq_rel);
     if (i < 64) cache[i] = Entry{kernel, dev, slots};
   }
-  // Persistent only while the tail matters: with many rounds per workgroup
-  // the hardware's own dispatch already balances, and workgroups that drift
-  // apart over many items lose L2 locality (measured: 8-bit forward,
-  // 1x32x32768 causal, 10.7 rounds: 1466 vs 1693 TFLOPS with one workgroup
-  // per item; 4x32x4096, 5.3 rounds: 1141 vs 1080).
-  if (items > 8 * slots) return items;
-  return items < slots ? items : slots;
+  // Persistent only when the alternating order of the per-XCD queues
+  // balances exactly (2 x slots per XCD a multiple of the tiles per head,
+  // heads spread evenly over the XCDs) and there is more than one round;
+  // else one workgroup per item, where the hardware dispatch balances.
+  const bool balanced = (nbh & 7) == 0 && slots % 8 == 0 && (2 * (slots / 8)) % nq == 0;
+  return (balanced && items > slots) ? slots : items;
 }
 
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream) {

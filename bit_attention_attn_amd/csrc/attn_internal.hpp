@@ -23,11 +23,12 @@ struct FwdArgs {
   int out_kind;       // OutKind
 };
 
-// Grid for a persistent launch: the number of workgroups of `kernel` that are
-// resident at once on the current device (CUs x workgroups per CU), rounded
-// down to a multiple of 8, at most `items`; `items` itself when that would
-// take more than 8 rounds; -1 on a HIP error.
-int persistent_grid(const void* kernel, int threads, int items);
+// Grid for a launch over nbh * nq (head, query tile) items: the number of
+// workgroups of `kernel` resident at once on the current device (CUs x
+// workgroups per CU, a multiple of 8) when the persistent per-XCD queues
+// balance exactly and there is more than one round, else nbh * nq (one
+// workgroup per item); -1 on a HIP error.
+int persistent_grid(const void* kernel, int threads, int nbh, int nq);
 
 // 16-bit path (fp16 when bf16 == false).
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream);

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   const WorkQueue wq = work_queue(p.nbh, p.nq);
   for (int round = 0;; ++round) {
   int bh, tq;
-  if (!work_item<CAUSAL>(wq, round, p.nq, bh, tq)) break;
+  if (!work_item(wq, round, p.nq, bh, tq)) break;
   const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
   const int N = p.N;
   const int q0 = qt * kBM8;
@@ -610,7 +610,7 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   // persistent grid for causal shapes (tiles differ in cost), one workgroup
   // per tile otherwise
   const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL>), kThreads8,
-                                            p.ntiles)
+                                            p.nbh, p.nq)
                           : p.ntiles;
   if (grid <= 0) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads8), 0, stream, p);

@@ -310,17 +310,21 @@ def main():
 
 
 def extra_workloads(attn, workloads, stream, dev):
-    """The long-context, 8-bit-outlier and DiT-gated workloads at full size:
-    10 timed launches per path after 2 warm-ups."""
+    """The long-context, 8-bit-outlier, DiT-gated and block-sparse DiT
+    workloads at full size: 10 timed launches per path after 2 warm-ups."""
     import torch
     extra = {}
-    for cid in (3, 4, 5):
+    for cid in (3, 4, 5, 6):
         c2, i2 = workloads.config_inputs(cid)
         log(f"workload {c2['name']}")
         q2, k2, v2 = (i2[n].to(dev) for n in ("q", "k", "v"))
         b2 = i2["bias"].to(dev) if i2["bias"] is not None else None
+        # block-sparse gates: count the FLOPs of the (query block, key block)
+        # pairs that are not gated off (the ones the kernels compute)
+        sparse = c2.get("gate_keep") is not None
+        F2 = (workloads.active_flops(i2["bias"], c2["N"], c2["d"], c2["causal"]) if sparse
+              else workloads.flops(c2["B"], c2["H"], c2["N"], c2["d"], c2["causal"]))
         del i2
-        F2 = workloads.flops(c2["B"], c2["H"], c2["N"], c2["d"], c2["causal"])
         res = {}
         if cid != 4:
             fn = lambda: attn.fwd(q2, k2, v2, causal=c2["causal"], bias=b2)  # noqa: E731
@@ -346,8 +350,11 @@ def extra_workloads(attn, workloads, stream, dev):
         if "bf16" in res:
             res["sage8"]["speedup_vs_bf16_attention"] = round(tf8 / res["bf16"]["tflops"], 3)
             res["sage8"]["speedup_vs_bf16_end_to_end"] = round(tfe / res["bf16"]["tflops"], 3)
+        if sparse:
+            res["flops_counted"] = f"{F2:.4e} (gated-on block pairs only, {c2['gate_keep']} of the off-diagonal kept)"
         extra[f"{c2['name']}: B={c2['B']} H={c2['H']} N={c2['N']} d={c2['d']} "
-              f"{'causal' if c2['causal'] else 'non-causal'}{' +gate bias' if b2 is not None else ''}"] = res
+              f"{'causal' if c2['causal'] else 'non-causal'}{' +gate bias' if b2 is not None else ''}"
+              f"{' (block-sparse)' if sparse else ''}"] = res
         del q2, k2, v2, b2, ws, prep
         torch.cuda.empty_cache()
     return extra

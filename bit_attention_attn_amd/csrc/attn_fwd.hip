@@ -311,32 +311,56 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
     }
   };
 
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  __syncthreads();
+  // ---- block-sparse skip: a key block whose gate is 0 (bias -inf) for every
+  // query block of this tile adds nothing to any of its rows, so it is
+  // neither loaded nor computed; a wave skips blocks gated off for its own
+  // query block.  Without a bias every block is active.
+  const int qb_lo = q0 / kBN, qb_hi = min((q0 + kBM - 1) / kBN, p.nb - 1);
+  const float* bias_head = p.bias ? p.bias + (size_t)bh * p.nb * p.nb : nullptr;
+  auto tile_active = [&](int j) {
+    if (bias_head == nullptr) return true;
+    for (int qb = qb_lo; qb <= qb_hi; ++qb)
+      if (bias_head[(size_t)qb * p.nb + j] != -INFINITY) return true;
+    return false;
+  };
+  auto next_active = [&](int j) {
+    ++j;
+    while (j < nkb && !tile_active(j)) ++j;
+    return j;
+  };
+
   f32x16_t sc[2][QS];
-  // ---- block j+1 loads while block j computes
-  for (int j = 0; j < nkb; ++j) {
-    const bool more = j + 1 < nkb;
+  int jc = next_active(-1), buf = 0;
+  if (jc < nkb) {
+    load_k(jc);
+    load_v(jc);
+    store_k(0);
+    store_v(0);
+  }
+  __syncthreads();
+  // ---- the next active block loads while the current one computes
+  while (jc < nkb) {
+    const int jn = next_active(jc);
+    const bool more = jn < nkb;
     if (more) {
-      load_k(j + 1);
-      load_v(j + 1);
+      load_k(jn);
+      load_v(jn);
     }
-    if (wave_has_rows && j <= wave_last) {
-      qk(j & 1, sc);
-      if (needs_mask(j)) apply_mask(j, sc);
+    if (wave_has_rows && jc <= wave_last && !(bias_row && bias_row[jc] == -INFINITY)) {
+      qk(buf, sc);
+      if (needs_mask(jc)) apply_mask(jc, sc);
       float kc[QS];
-      block_max(j, sc, kc);
+      block_max(jc, sc, kc);
       softmax_p(sc, kc);
-      pv(j & 1);
+      pv(buf);
     }
     if (more) {
-      store_k((j + 1) & 1);
-      store_v((j + 1) & 1);
+      store_k(buf ^ 1);
+      store_v(buf ^ 1);
     }
     __syncthreads();
+    jc = jn;
+    buf ^= 1;
   }
 
   // ---- epilogue: normalise, LSE, stores straight from the accumulators

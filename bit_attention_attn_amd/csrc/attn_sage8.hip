@@ -441,14 +441,33 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   const float* bias_row = p.bias ? p.bias + ((size_t)bh * p.nb + (size_t)qb64) * p.nb : nullptr;
   const float* skrow = p.sk + (size_t)bh * p.nblk;
 
-  load_kv(0);
-  store_kv(0);
+  // block-sparse skip: a key block gated off (bias -inf) for every query
+  // block of this tile is neither loaded nor computed; a wave skips blocks
+  // gated off for its own query block.  Without a bias every block is active.
+  const int qb_lo = q0 / kQB, qb_hi = min((q0 + kBM8 - 1) / kQB, p.nb - 1);
+  const float* bias_head = p.bias ? p.bias + (size_t)bh * p.nb * p.nb : nullptr;
+  auto tile_active = [&](int jj) {
+    if (bias_head == nullptr) return true;
+    for (int qb = qb_lo; qb <= qb_hi; ++qb)
+      if (bias_head[(size_t)qb * p.nb + jj] != -INFINITY) return true;
+    return false;
+  };
+  auto next_active = [&](int jj) {
+    ++jj;
+    while (jj < nkb && !tile_active(jj)) ++jj;
+    return jj;
+  };
+  int j = next_active(-1), buf = 0;
+  if (j < nkb) {
+    load_kv(j);
+    store_kv(0);
+  }
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < nkb;
-    if (more) load_kv(j + 1);
-    if (wave_has_rows && j <= wave_last) {
+  while (j < nkb) {
+    const int jn = next_active(j);
+    const bool more = jn < nkb;
+    if (more) load_kv(jn);
+    if (wave_has_rows && j <= wave_last && !(bias_row && bias_row[j] == -INFINITY)) {
       // ---- S^T = Kq Qq^T on top of the offset, exact
       const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
       i32x16_t si[2];
@@ -533,8 +552,10 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
         o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, o[dt], 0, 0, 0, 0, 0, 0);
       }
     }
-    if (more) store_kv((j + 1) & 1);
+    if (more) store_kv(buf ^ 1);
     __syncthreads();
+    j = jn;
+    buf ^= 1;
   }
 
   // ---- epilogue: O = acc * sv[d] / l; LSE = (m + log2 l - kPlog) ln 2 plus

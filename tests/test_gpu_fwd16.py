@@ -85,7 +85,7 @@ def test_workload1_tiny_exact_all_rows():
     assert o.dtype == torch.float32 and o.shape == (1, 2, 256, 64)
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3, 5])
+@pytest.mark.parametrize("cfg_id", [2, 3, 5, 6])
 def test_full_size_workloads_sampled_rows(cfg_id):
     cfg, inp = workloads.config_inputs(cfg_id)
     rows = workloads.parity_rows(cfg["B"], cfg["H"], cfg["N"], seed=cfg_id)
@@ -160,3 +160,41 @@ def test_negative_and_zero_scale():
     for scale in (-0.2, 0.0):
         _run_and_check(inp, True, scale, label=f"scale={scale}")
         _run_and_check(inp, False, scale, label=f"scale={scale}")
+
+
+# ---- block-sparse gates: key blocks with bias -inf are skipped, which must
+# give exactly what the definition gives (those blocks weigh 0)
+
+@pytest.mark.parametrize("N", [200, 700])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("keep", [0.1, 0.5])
+def test_block_sparse_gates(N, d, causal, keep):
+    inp = workloads.make_inputs(1, 2, N, d, "bf16", seed=N + d + int(10 * keep), gate=True, gate_keep=keep)
+    _run_and_check(inp, causal, 1 / math.sqrt(d), label=f"sparse N={N} d={d} keep={keep}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_inactive_tiles(d, causal):
+    """Key block 2 gated off for every query block (skipped by whole tiles),
+    query blocks 4..7 of head 1 gated off everywhere (rows 256..511 give
+    O = 0, LSE = -inf, a whole workgroup with nothing to do), and the
+    causal diagonal gated off for query block 9."""
+    B, H, N = 1, 2, 1000
+    inp = workloads.make_inputs(B, H, N, d, "bf16", seed=77 + d, gate=True)
+    bias = inp["bias"]
+    bias[:, :, :, 2] = float("-inf")
+    bias[0, 1, 4:8, :] = float("-inf")
+    bias[0, 0, 9, 9] = float("-inf")
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = attn.fwd(q, k, v, causal=causal, bias=bias.to(DEV), out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    assert (o[0, 1, 256:512] == 0).all() and torch.isneginf(lse[0, 1, 256:512]).all()
+    o_ref, l_ref = oracle.attn_full(*(inp[n].float().numpy() for n in ("q", "k", "v")), causal=causal,
+                                    scale=1 / math.sqrt(d), bias=bias.numpy())
+    got, got_l = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(fin, np.isfinite(got_l))
+    assert np.abs(got - o_ref).max() <= MAX_ABS and np.abs(got - o_ref).mean() <= MEAN_ABS
+    assert np.abs(got_l[fin] - l_ref[fin]).max() <= 2e-3

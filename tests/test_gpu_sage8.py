@@ -231,3 +231,33 @@ def test_workload_sampled_rows(cfg_id):
     rows = workloads.parity_rows(B, H, N, seed=cfg_id, n_random=24)
     _check(inp, cfg["causal"], 1 / math.sqrt(d), rows=rows, out_dtype=torch.bfloat16,
            label=f"workload {cfg['name']}")
+
+
+# ---------------------------------------------------- block-sparse gates
+
+@pytest.mark.parametrize("N", [200, 700])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_gates(N, d, causal):
+    """Key blocks gated off (bias -inf) are skipped: results still match the
+    fp32 model and the exact attention."""
+    inp = workloads.make_inputs(1, 2, N, d, "bf16", seed=5 * N + d, gate=True, gate_keep=0.25)
+    _check(inp, causal, 1 / math.sqrt(d), label=f"sparse N={N} d={d}")
+
+
+def test_block_sparse_inactive_tiles():
+    """Key block 2 off for every query block; query blocks 4..7 of head 1
+    off everywhere (O = 0, LSE = -inf)."""
+    inp = workloads.make_inputs(1, 2, 1000, 128, "bf16", seed=91, gate=True)
+    inp["bias"][:, :, :, 2] = -math.inf
+    inp["bias"][0, 1, 4:8, :] = -math.inf
+    _, _, o, lse, _, _ = _check(inp, True, 1 / math.sqrt(128), label="sparse inactive", check_oracle=False)
+    assert (o[0, 1, 256:512] == 0).all()
+    assert torch.isneginf(lse[0, 1, 256:512]).all()
+
+
+def test_workload_dit_sparse_sampled_rows():
+    cfg, inp = workloads.config_inputs(6)
+    rows = workloads.parity_rows(cfg["B"], cfg["H"], cfg["N"], seed=6, n_random=24)
+    _check(inp, cfg["causal"], 1 / math.sqrt(cfg["d"]), rows=rows, out_dtype=torch.bfloat16,
+           label="workload dit-sparse")

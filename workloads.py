@@ -47,6 +47,10 @@ CONFIGS = {
             out="same", paths=("sage8",), outliers=True),
     5: dict(name="dit-gated", B=2, H=24, N=16384, d=64, causal=False, dtype="bf16",
             out="same", paths=("bf16", "sage8"), gate_bias=True),
+    # block-sparse variant of the DiT shape: each query block keeps its own
+    # key block and the top quarter of the others by gate logit
+    6: dict(name="dit-sparse", B=2, H=24, N=16384, d=64, causal=False, dtype="bf16",
+            out="same", paths=("bf16", "sage8"), gate_bias=True, gate_keep=0.25),
 }
 
 _TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
@@ -62,14 +66,21 @@ def flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     return f / 2 if causal else f
 
 
-def gate_bias(g: torch.Tensor) -> torch.Tensor:
+def gate_bias(g: torch.Tensor, keep=None) -> torch.Tensor:
     """Log-gate bias from raw gate logits g [B,H,nb,nb]: off-diagonal entries
     of each row are log(softmax(g over the other key blocks)), the diagonal is
-    log(1) = 0.  Computed in fp64, returned in fp32."""
+    log(1) = 0.  With keep (a fraction in (0, 1]) only the top
+    ceil(keep*(nb-1)) off-diagonal blocks of each row by g keep their gate
+    (softmax over the kept ones); the others are gated off, bias -inf
+    (block-sparse selection).  Computed in fp64, returned in fp32."""
     g = g.to(torch.float64)
     nb = g.shape[-1]
     eye = torch.eye(nb, dtype=torch.bool)
     masked = g.masked_fill(eye, float("-inf"))
+    if keep is not None and nb > 1:
+        kcount = max(1, math.ceil(keep * (nb - 1)))
+        thresh = torch.topk(masked, kcount, dim=-1).values[..., -1:]
+        masked = masked.masked_fill(masked < thresh, float("-inf"))
     if nb > 1:
         out = masked - torch.logsumexp(masked, dim=-1, keepdim=True)
     else:
@@ -79,7 +90,7 @@ def gate_bias(g: torch.Tensor) -> torch.Tensor:
 
 
 def make_inputs(B, H, N, d, dtype="bf16", seed=0, outliers=False, gate=False,
-                randn_scale=1.0):
+                randn_scale=1.0, gate_keep=None):
     """Draw Q, K, V (and optional bias) on the CPU.  Returns a dict with torch
     CPU tensors q, k, v in ``dtype`` and bias (fp32 or None)."""
     gen = torch.Generator("cpu").manual_seed(int(seed))
@@ -106,16 +117,17 @@ def make_inputs(B, H, N, d, dtype="bf16", seed=0, outliers=False, gate=False,
     if gate:
         nb = (N + BIAS_BLOCK - 1) // BIAS_BLOCK
         g = torch.randn((B, H, nb, nb), generator=gen, dtype=torch.float32) * math.sqrt(2.0)
-        bias = gate_bias(g)
+        bias = gate_bias(g, gate_keep)
     tdt = torch_dtype(dtype)
     return dict(q=q.to(tdt), k=k.to(tdt), v=v.to(tdt), bias=bias)
 
 
 def config_inputs(cfg_id: int):
-    """Inputs of workload cfg_id (1..5) with its seed; returns (cfg, inputs)."""
+    """Inputs of workload cfg_id (1..6) with its seed; returns (cfg, inputs)."""
     cfg = CONFIGS[cfg_id]
     inp = make_inputs(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["dtype"], seed=cfg_id,
-                      outliers=cfg.get("outliers", False), gate=cfg.get("gate_bias", False))
+                      outliers=cfg.get("outliers", False), gate=cfg.get("gate_bias", False),
+                      gate_keep=cfg.get("gate_keep"))
     return cfg, inp
 
 
@@ -157,3 +169,18 @@ def error_metrics(got: np.ndarray, ref: np.ndarray) -> dict:
         cos=float(np.dot(got, ref) / denom) if denom > 0 else 1.0,
         rel_l1=float(diff.sum() / max(np.abs(ref).sum(), 1e-300)),
     )
+
+
+def active_flops(bias: torch.Tensor, N: int, d: int, causal: bool) -> float:
+    """FLOPs of the (query block, key block) pairs whose gate is not 0 (bias
+    finite): 4*d per visible score, the causal diagonal counted by its
+    visible half-plus-diagonal."""
+    nb = bias.shape[-1]
+    sizes = torch.tensor([min(64, N - 64 * i) for i in range(nb)], dtype=torch.float64)
+    pair = sizes[:, None] * sizes[None, :]
+    if causal:
+        tri = torch.tril(torch.ones(nb, nb, dtype=torch.float64), diagonal=-1)
+        diag = torch.diag(sizes * (sizes + 1) / 2)
+        pair = pair * tri + diag
+    live = torch.isfinite(bias).to(torch.float64)
+    return float(4.0 * d * (live * pair).sum())

@@ -22,7 +22,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 attn_status check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (d != 64 && d != 96 && d != 128) return ATTN_ERR_HEADDIM;
   const int64_t elems = (int64_t)B * H * N * d;
   if (elems >= kMaxElems) return ATTN_ERR_SHAPE;
   return ATTN_OK;
@@ -147,7 +147,7 @@ const char* attn_status_str(int status) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: B, H, N must be >= 1 and each tensor < 2^31 elements";
-    case ATTN_ERR_HEADDIM: return "ATTN_ERR_HEADDIM: head dimension must be 64 or 128";
+    case ATTN_ERR_HEADDIM: return "ATTN_ERR_HEADDIM: head dimension must be 64, 96 or 128";
     case ATTN_ERR_DTYPE: return "ATTN_ERR_DTYPE: unsupported input/output dtype";
     case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: pointer not aligned (tensors 16 B, workspace 256 B)";
     case ATTN_ERR_ARG: return "ATTN_ERR_ARG: invalid argument (causal must be 0/1, scale finite)";

@@ -80,7 +80,8 @@ struct Fwd16Smem {
   // (d = 128) or 192 bytes (d = 64) spreads them over the banks (measured
   // on gfx950: 107 B/clk/CU against 62 B/clk/CU at a 272-byte stride).
   static constexpr int kKRow = D + 8;
-  static constexpr int kVRow = D == 128 ? D + 16 : D + 32;
+  // V rows of 288 bytes at d = 128 and 96, 192 bytes at d = 64
+  static constexpr int kVRow = D == 64 ? D + 32 : 144;
   static constexpr int kKTile = kBN * kKRow;
   static constexpr int kVTile = kBN * kVRow;
   static constexpr int kElems = T::kKbuf * kKTile + T::kVbuf * kVTile;
@@ -450,6 +451,8 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     if (t == 1) return launch_impl<64, BF16, CAUSAL, 1, 4>(a, stream);
     return launch_impl<64, BF16, CAUSAL, 2, 4>(a, stream);
   }
+  // d = 96: a 64 x 96 tile is 768 16-byte chunks, which 4 waves split evenly
+  if (a.d == 96) return launch_impl<96, BF16, CAUSAL, 1, 4>(a, stream);
   if (t == 1) return launch_impl<128, BF16, CAUSAL, 1, 4>(a, stream);
   return launch_impl<128, BF16, CAUSAL, 1, 8>(a, stream);
 }

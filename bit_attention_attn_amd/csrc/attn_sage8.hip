@@ -38,6 +38,10 @@ namespace {
 
 constexpr int kQB = 64;        // rows per INT8 scale block (and keys per block)
 constexpr int kChunk = 256;    // tokens per column-statistics chunk
+// threads of the preparation kernels: a multiple of the 16-byte chunks per
+// row (D/8), so every thread keeps one chunk column (192 at d = 96)
+template <int D>
+constexpr int prep_threads() { return D == 96 ? 192 : 256; }
 constexpr float kTau8 = 2.0f;  // lazy-rescale threshold of the 8-bit path (log2 units)
 // log2(448) - kTau8: P^ = e4m3(2^(t - m + kPlog)) stays <= 448
 constexpr float kPlog = 6.807354922057604f;
@@ -88,13 +92,13 @@ __device__ __forceinline__ float in_to_f32(uint16_t x) {
   }
 }
 
-// ---- colstats: grid (nchunk, B*H), 256 threads --------------------------
+// ---- colstats: grid (nchunk, B*H), prep_threads<D>() threads --------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                       int N, double* __restrict__ kpart,
                                                       float* __restrict__ vpart, int nchunk) {
-  constexpr int kCpr = D / 8;          // 16-byte chunks per row
-  constexpr int kRows = 256 / kCpr;    // rows per pass
+  constexpr int kCpr = D / 8;                        // 16-byte chunks per row
+  constexpr int kRows = prep_threads<D>() / kCpr;    // rows per pass
   __shared__ double ssum[kRows][D];
   __shared__ float smax[kRows][D];
   const int chunk = blockIdx.x, bh = blockIdx.y;
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
   }
 }
 
-// ---- finalize: grid B*H, 256 threads.  Thread (g, c) adds the partials of
+// ---- finalize: grid B*H, (256/D)*D threads.  Thread (g, c) adds the partials of
 // chunks g, g + 256/D, ... for channel c with two independent accumulators,
 // then the groups combine through LDS.  The fp64 partials are sums of fp16 /
 // bf16 values, which fp64 adds exactly at these magnitudes, so the order of
@@ -153,7 +157,7 @@ template <int D>
 __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
                                                     int nchunk, int N, float* __restrict__ kmean,
                                                     float* __restrict__ sv, float* __restrict__ vinv) {
-  constexpr int kG = 256 / D;
+  constexpr int kG = 256 / D;  // chunk groups; the block has kG * D threads
   __shared__ double ssum[kG][D];
   __shared__ float smax[kG][D];
   const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
@@ -189,15 +193,19 @@ __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__
   }
 }
 
-// Block-wide max of a non-negative float over 256 threads (4 waves).
-__device__ __forceinline__ float block_max256(float x, float* red) {
+// Block-wide max of a non-negative float over NW waves.
+template <int NW>
+__device__ __forceinline__ float block_max(float x, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = x;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
+  return m;
 }
 
 __device__ __forceinline__ uint32_t q8(float y, float inv) {
@@ -206,7 +214,7 @@ __device__ __forceinline__ uint32_t q8(float y, float inv) {
   return (uint32_t)((int)r & 0xFF);
 }
 
-// ---- quant: grid (nblk, B*H), 256 threads --------------------------------
+// ---- quant: grid (nblk, B*H), prep_threads<D>() threads --------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, int N, int np, int nblk,
@@ -214,9 +222,10 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
                                                    int8_t* __restrict__ qq, int8_t* __restrict__ kq,
                                                    uint8_t* __restrict__ vq, float* __restrict__ sq,
                                                    float* __restrict__ sk) {
+  constexpr int kThreads = prep_threads<D>();
   constexpr int kCpr = D / 8;
-  constexpr int kRows = 256 / kCpr;      // rows per pass
-  constexpr int kPass = kQB / kRows;     // passes over the 64-row block
+  constexpr int kRows = kThreads / kCpr;  // rows per pass
+  constexpr int kPass = kQB / kRows;      // passes over the 64-row block
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t vt[D][kQB];  // transposed, permuted V codes
   const int blk = blockIdx.x, bh = blockIdx.y;
@@ -257,8 +266,8 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
       vt[ch * 8 + e][key_pos(r)] = (uint8_t)code;
     }
   }
-  aq = block_max256(aq, red);
-  ak = block_max256(ak, red);
+  aq = block_max<kThreads / 64>(aq, red);
+  ak = block_max<kThreads / 64>(ak, red);
   const float inv_q = aq > 0.f ? __fdiv_rn(127.0f, aq) : 1.0f;
   const float inv_k = ak > 0.f ? __fdiv_rn(127.0f, ak) : 1.0f;
   if (tid == 0) {
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   __syncthreads();
   // V tile: D rows of 64 bytes, contiguous per block -> 16-byte stores
   uint8_t* vdst = vq + headp + (size_t)blk * kQB * D;
-  for (int idx = tid; idx < D * kQB / 16; idx += 256) {
+  for (int idx = tid; idx < D * kQB / 16; idx += kThreads) {
     const int row = idx / (kQB / 16), c16 = idx % (kQB / 16);
     *(u32x4_t*)(vdst + row * kQB + c16 * 16) = *(const u32x4_t*)(&vt[row][c16 * 16]);
   }
@@ -292,14 +301,14 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
   char* w = static_cast<char*>(ws);
   const int bh = B * H;
   const int np = L.nblk * kQB;
-  hipLaunchKernelGGL((sage8_colstats<D, BF16>), dim3(L.nchunk, bh), dim3(256), 0, stream,
+  hipLaunchKernelGGL((sage8_colstats<D, BF16>), dim3(L.nchunk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N,
                      reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk);
-  hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3(256), 0, stream,
+  hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3((256 / D) * D), 0, stream,
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
                      reinterpret_cast<float*>(w + L.vinv));
-  hipLaunchKernelGGL((sage8_quant<D, BF16>), dim3(L.nblk, bh), dim3(256), 0, stream,
+  hipLaunchKernelGGL((sage8_quant<D, BF16>), dim3(L.nblk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), N, np, L.nblk,
                      reinterpret_cast<const float*>(w + L.kmean), reinterpret_cast<const float*>(w + L.vinv),
@@ -407,7 +416,8 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   // loader: K tile 64*D bytes and V tile D*64 bytes, 16-byte chunks; chunk
   // tid + i*threads of block kb is at byte 16*tid + (kb*64*D + 16*i*threads)
   // of the head (buffer loads: one per-lane offset, a uniform one)
-  constexpr int kNld = kQB * D / 16 / kThreads8;
+  constexpr int kChunks = kQB * D / 16;  // 16-byte chunks per tile
+  constexpr int kNld = (kChunks + kThreads8 - 1) / kThreads8;
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kq, (uint32_t)p.np * D);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vq, (uint32_t)p.np * D);
   const uint32_t voff = 16u * tid;
@@ -415,6 +425,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   auto load_kv = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < kNld; ++i) {
+      if (kChunks % kThreads8 != 0 && tid + i * kThreads8 >= kChunks) continue;
       kst[i] = buffer_load16(krs, voff, kb * kQB * D + 16 * i * kThreads8);
       vst[i] = buffer_load16(vrs, voff, kb * kQB * D + 16 * i * kThreads8);
     }
@@ -423,6 +434,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
 #pragma unroll
     for (int i = 0; i < kNld; ++i) {
       const int idx = tid + i * kThreads8;
+      if (kChunks % kThreads8 != 0 && idx >= kChunks) continue;
       const int kr = idx / (D / 16), kc = idx % (D / 16);
       *(u32x4_t*)(kl + buf * kKTile + kr * kKRow + kc * 16) = kst[i];
       const int vr = idx / (kQB / 16), vc = idx % (kQB / 16);
@@ -644,12 +656,15 @@ hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool b
                              void* ws, hipStream_t stream) {
   if (d == 64) return bf16 ? prep_impl<64, true>(q, k, v, B, H, N, ws, stream)
                            : prep_impl<64, false>(q, k, v, B, H, N, ws, stream);
+  if (d == 96) return bf16 ? prep_impl<96, true>(q, k, v, B, H, N, ws, stream)
+                           : prep_impl<96, false>(q, k, v, B, H, N, ws, stream);
   return bf16 ? prep_impl<128, true>(q, k, v, B, H, N, ws, stream)
               : prep_impl<128, false>(q, k, v, B, H, N, ws, stream);
 }
 
 hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? fwd8_impl<64, true>(ws, a, stream) : fwd8_impl<64, false>(ws, a, stream);
+  if (a.d == 96) return a.causal ? fwd8_impl<96, true>(ws, a, stream) : fwd8_impl<96, false>(ws, a, stream);
   return a.causal ? fwd8_impl<128, true>(ws, a, stream) : fwd8_impl<128, false>(ws, a, stream);
 }
 

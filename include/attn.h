@@ -23,7 +23,7 @@
  *
  * Conventions for every entry point:
  *  - Tensors are contiguous [B,H,N,d], d innermost, in device memory, with
- *    16-byte aligned base pointers.  d must be 64 or 128; B, H, N >= 1;
+ *    16-byte aligned base pointers.  d must be 64, 96 or 128; B, H, N >= 1;
  *    B*H*N*d must fit in 2^31 elements per tensor.
  *  - The caller owns every buffer.  The library allocates no device memory,
  *    keeps no mutable state between calls and is safe to call from several
@@ -53,7 +53,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,      /* a required pointer is NULL                   */
     ATTN_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 elts */
-    ATTN_ERR_HEADDIM = 3,   /* d is not 64 or 128                           */
+    ATTN_ERR_HEADDIM = 3,   /* d is not 64, 96 or 128                       */
     ATTN_ERR_DTYPE = 4,     /* unsupported input/output dtype combination   */
     ATTN_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned             */
     ATTN_ERR_ARG = 6,       /* scale not finite, causal not 0/1, ...        */

@@ -48,7 +48,7 @@ def test_fwd_validation(name, dt):
     assert _fwd(fn, B=0, out=dt) == E_SHAPE
     assert _fwd(fn, N=0, out=dt) == E_SHAPE
     assert _fwd(fn, H=-1, out=dt) == E_SHAPE
-    assert _fwd(fn, d=96, out=dt) == E_HEADDIM
+    assert _fwd(fn, d=80, out=dt) == E_HEADDIM
     assert _fwd(fn, d=256, out=dt) == E_HEADDIM
     assert _fwd(fn, B=1 << 10, H=1 << 10, N=1 << 10, d=128, out=dt) == E_SHAPE  # 2^37 elements
     assert _fwd(fn, causal=2, out=dt) == E_ARG
@@ -63,14 +63,15 @@ def test_fwd_validation(name, dt):
 
 def test_sage8_validation():
     L = attn.lib()
-    assert L.attn_sage8_workspace_size(1, 1, 64, 96) == 0
+    assert L.attn_sage8_workspace_size(1, 1, 64, 80) == 0
+    assert L.attn_sage8_workspace_size(1, 1, 64, 96) > 0
     assert L.attn_sage8_workspace_size(0, 1, 64, 64) == 0
     need = L.attn_sage8_workspace_size(1, 2, 100, 64)
     assert need >= 3 * 2 * 128 * 64  # three 8-bit tensors padded to 128 rows
     prep = L.attn_k_smooth_quant
     assert prep(None, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need, None) == E_NULL
     assert prep(FAKE, FAKE, FAKE, F32, 1, 2, 100, 64, FAKE, need, None) == E_DTYPE
-    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 96, FAKE, need, None) == E_HEADDIM
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 80, FAKE, need, None) == E_HEADDIM
     assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, None, need, None) == E_WS
     assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need - 1, None) == E_WS
     assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE + 16, need, None) == E_ALIGN

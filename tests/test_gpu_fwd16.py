@@ -54,7 +54,7 @@ SWEEP_N = [1, 17, 63, 64, 65, 127, 128, 129, 200, 256, 300]
 
 
 @pytest.mark.parametrize("N", SWEEP_N)
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_small_sweep_bf16(N, d, causal, with_bias):
@@ -63,7 +63,7 @@ def test_small_sweep_bf16(N, d, causal, with_bias):
 
 
 @pytest.mark.parametrize("N", [1, 65, 200, 256])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("out", ["same", "f32"])
 def test_small_sweep_f16(N, d, causal, out):
@@ -166,7 +166,7 @@ def test_negative_and_zero_scale():
 # give exactly what the definition gives (those blocks weigh 0)
 
 @pytest.mark.parametrize("N", [200, 700])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("keep", [0.1, 0.5])
 def test_block_sparse_gates(N, d, causal, keep):
@@ -174,7 +174,7 @@ def test_block_sparse_gates(N, d, causal, keep):
     _run_and_check(inp, causal, 1 / math.sqrt(d), label=f"sparse N={N} d={d} keep={keep}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_inactive_tiles(d, causal):
     """Key block 2 gated off for every query block (skipped by whole tiles),

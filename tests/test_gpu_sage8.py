@@ -94,7 +94,7 @@ PREP_N = [1, 63, 64, 65, 200, 256, 300, 1000]
 
 
 @pytest.mark.parametrize("N", PREP_N)
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_prep_bit_exact(N, d, dtype):
     inp = workloads.make_inputs(2, 2, N, d, dtype, seed=7 * N + d, outliers=(N % 2 == 0))
@@ -138,7 +138,7 @@ FWD_N = [1, 17, 64, 65, 127, 128, 129, 200, 300]
 
 
 @pytest.mark.parametrize("N", FWD_N)
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_small_sweep(N, d, causal, with_bias):
@@ -236,7 +236,7 @@ def test_workload_sampled_rows(cfg_id):
 # ---------------------------------------------------- block-sparse gates
 
 @pytest.mark.parametrize("N", [200, 700])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_gates(N, d, causal):
     """Key blocks gated off (bias -inf) are skipped: results still match the

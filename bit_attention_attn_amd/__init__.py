@@ -8,6 +8,8 @@ raised.
 
     fwd(q, k, v, causal=False, scale=None, bias=None, out_dtype=None,
         return_lse=False)                       # fp16 / bf16 path
+    fwd_strided(q, k, v, ...)                   # same, any layout with d contiguous
+    fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...)  # packed sequences
     prep = sage8_prep(q, k, v)                  # 8-bit preparation
     fwd_sage8(prep, causal=False, ...)          # 8-bit forward
     sageattn(q, k, v, causal=False, ...)        # both 8-bit steps
@@ -24,8 +26,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "sage8_prep", "fwd_sage8", "sageattn", "AttnError", "Sage8Prepared",
-           "sage8_workspace_views", "lib", "LIB_PATH", "status_str"]
+__all__ = ["fwd", "fwd_strided", "fwd_varlen", "sage8_prep", "fwd_sage8", "sageattn", "AttnError",
+           "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH", "status_str"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
@@ -55,6 +57,11 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_fwd_f16", "attn_fwd_bf16"):
         fn = getattr(L, name)
         fn.argtypes = fwd_args
+        fn.restype = i
+    ll_p = ctypes.POINTER(ctypes.c_longlong)
+    for name in ("attn_fwd_strided_f16", "attn_fwd_strided_bf16"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, ll_p, vp, i, f, i, vp]
         fn.restype = i
     L.attn_sage8_workspace_size.argtypes = [i, i, i, i]
     L.attn_sage8_workspace_size.restype = sz
@@ -125,6 +132,74 @@ def fwd(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse
                 float(scale), _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(q.device))
     if st != 0:
         raise AttnError(st, fn.__name__)
+    return (o, lse) if return_lse else o
+
+
+def _strided_call(q, k, v, o, lse, B, H, N, d, strides, cu, causal, scale, out_dtype):
+    fn = lib().attn_fwd_strided_bf16 if q.dtype == torch.bfloat16 else lib().attn_fwd_strided_f16
+    arr = (ctypes.c_longlong * 12)(*[int(x) for x in strides])
+    with torch.cuda.device(q.device):
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, arr, _ptr(cu), int(bool(causal)),
+                float(scale), _DTYPE_CODE.get(out_dtype, -1), _stream(q.device))
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+
+
+def _check_views(ts, ndim):
+    for name, t in zip(("q", "k", "v"), ts):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != ndim or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a {ndim}-D CUDA (HIP) tensor with the last dimension contiguous")
+    q = ts[0]
+    if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must share one dtype: float16 or bfloat16")
+    if any(t.device != q.device for t in ts):
+        raise ValueError("q, k, v must be on one device")
+
+
+def fwd_strided(q, k, v, causal=False, scale=None, out_dtype=None, return_lse=False):
+    """Fused attention forward on logical [B,H,N,d] tensors of any layout
+    with d contiguous (e.g. x.transpose(1, 2) of a [B,N,H,d] tensor, or
+    views of a fused QKV projection).  O has q's layout (empty_like); LSE is
+    [B,H,N] fp32."""
+    _check_views((q, k, v), 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same logical shape")
+    B, H, N, d = q.shape
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q, dtype=out_dtype)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    strides = []
+    for t in (q, k, v, o):
+        strides += [t.stride(0), t.stride(1), t.stride(2)]
+    _strided_call(q, k, v, o, lse, B, H, N, d, strides, None, causal, scale, out_dtype)
+    return (o, lse) if return_lse else o
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False):
+    """Fused attention forward on packed sequences: q, k, v [total,H,d] (d
+    contiguous), cu_seqlens int32 [B+1] on the device (sequence b is tokens
+    cu_seqlens[b] .. cu_seqlens[b+1]-1, attending only within itself),
+    max_seqlen the longest length.  O is [total,H,d] like q; LSE is
+    [B,H,max_seqlen] fp32."""
+    _check_views((q, k, v), 3)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    total, H, d = q.shape
+    B = cu_seqlens.numel() - 1
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q, dtype=out_dtype)
+    lse = torch.empty((B, H, max_seqlen), dtype=torch.float32, device=q.device) if return_lse else None
+    strides = []
+    for t in (q, k, v, o):
+        strides += [0, t.stride(1), t.stride(0)]
+    _strided_call(q, k, v, o, lse, B, H, int(max_seqlen), d, strides, cu_seqlens, causal, scale, out_dtype)
     return (o, lse) if return_lse else o
 
 

@@ -76,6 +76,39 @@ attn_status fwd16(bool bf16, const void* q, const void* k, const void* v, void* 
   return ATTN_OK;
 }
 
+attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                          int H, int N, int d, const long long* strides, const int* cu_seqlens, int causal,
+                          float scale, int out_dtype, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || strides == nullptr) return ATTN_ERR_NULL;
+  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, nullptr);
+  if (s != ATTN_OK) return s;
+  const int in_dtype = bf16 ? ATTN_DTYPE_BF16 : ATTN_DTYPE_F16;
+  if (out_dtype != in_dtype && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens != nullptr && !aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
+  // every stride non-negative and a multiple of 8 elements (16-byte rows),
+  // token strides at least d; a head's rows must be addressable with 32-bit
+  // byte offsets
+  for (int t = 0; t < 4; ++t) {
+    for (int i = 0; i < 3; ++i) {
+      const long long st = strides[3 * t + i];
+      if (st < 0 || st > (1LL << 31)) return ATTN_ERR_ARG;
+      if (st % 8 != 0) return ATTN_ERR_ALIGN;
+    }
+    if (strides[3 * t + 2] < d) return ATTN_ERR_ARG;
+    if ((long long)N * strides[3 * t + 2] * 2 >= (1LL << 32)) return ATTN_ERR_SHAPE;
+  }
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  attn::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, d, causal, scale,
+                  out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16)};
+  a.general = true;
+  for (int i = 0; i < 12; ++i) a.strides[i] = strides[i];
+  a.cu = cu_seqlens;
+  if (attn::launch_fwd16(a, bf16, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,6 +123,18 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
                           int N, int d, int causal, float scale, const float* bias, int out_dtype,
                           void* stream) {
   return fwd16(true, q, k, v, o, lse, B, H, N, d, causal, scale, bias, out_dtype, stream);
+}
+
+attn_status attn_fwd_strided_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                 int N, int d, const long long* strides, const int* cu_seqlens, int causal,
+                                 float scale, int out_dtype, void* stream) {
+  return fwd16_strided(false, q, k, v, o, lse, B, H, N, d, strides, cu_seqlens, causal, scale, out_dtype, stream);
+}
+
+attn_status attn_fwd_strided_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                  int N, int d, const long long* strides, const int* cu_seqlens, int causal,
+                                  float scale, int out_dtype, void* stream) {
+  return fwd16_strided(true, q, k, v, o, lse, B, H, N, d, strides, cu_seqlens, causal, scale, out_dtype, stream);
 }
 
 size_t attn_sage8_workspace_size(int B, int H, int N, int d) {

@@ -120,6 +120,74 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8) that waits for every outstanding vector memory
+// operation and for nothing else.  Placed after a kernel's prologue loads, it
+// tells the compiler's wait tracking that those loads are done, so no wait on
+// them is left inside the main loop (where, the counter being in order, it
+// would also wait for the loads that prefetch the next block).
+constexpr int kWaitVm0 = 0x0F70;
+
+// Block-sparse gating by a per-head [nb x nb] block bias (fp32, natural-log
+// units; -inf gates a 64 x 64 block off).  A workgroup tile spans kRows
+// query blocks starting at qb_lo; a key block is visited when its bias is
+// not -inf for at least one of them.  The gate holds a chunk of 64 key
+// blocks: a bit mask of the visited ones (one ballot per query block) and,
+// in lane i, the bias of key block cb + i for the wave's own query block, so
+// stepping to the next block costs a few scalar instructions and one lane
+// read; a new chunk is read once per 64 key blocks.  Reads go through a
+// buffer resource: reads past the head return 0 and are masked out.
+template <int kRows>
+struct BlockGate {
+  __amdgpu_buffer_rsrc_t rs;
+  int nb, nkb, qb_lo, rw;
+  int cb;         // first key block of the chunk held (a multiple of 64)
+  uint64_t rest;  // visited blocks of the chunk not yet returned (bit i: cb + i)
+  float wv;       // lane i: bias of key block cb + i for query block qb_lo + rw
+
+  // head: this head's bias; nkb: key blocks of the tile; rw: the wave's
+  // query block within the tile
+  __device__ __forceinline__ BlockGate(const float* head, int nb_, int qb_lo_, int nkb_, int rw_)
+      : nb(nb_), nkb(nkb_), qb_lo(qb_lo_), rw(rw_), cb(0), rest(0), wv(-INFINITY) {
+    rs = buffer_rsrc(head, (uint32_t)nb * (uint32_t)nb * 4u);
+  }
+  __device__ void load_chunk(int c) {
+    const int lane = threadIdx.x & 63;
+    cb = c;
+    rest = 0;
+    wv = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      if (qb_lo + r >= nb) break;
+      const float x = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (uint32_t)lane,
+                                                      4u * (uint32_t)((qb_lo + r) * nb + c), 0));
+      rest |= __ballot(c + lane < nkb && x != -INFINITY);
+      if (r == rw) wv = x;
+    }
+  }
+  // the next visited key block in increasing order (nkb when none is left);
+  // the chunk held afterwards contains it
+  __device__ __forceinline__ int next() {
+    while (rest == 0) {
+      if (cb + 64 >= nkb) return nkb;
+      load_chunk(cb + 64);
+    }
+    const int t = (int)__builtin_ctzll(rest);
+    rest &= rest - 1;
+    return cb + t;
+  }
+  // the first visited key block (nkb when none)
+  __device__ __forceinline__ int first() {
+    load_chunk(0);
+    return next();
+  }
+  // the wave's bias of key block j, which the chunk held must contain
+  __device__ __forceinline__ float wave_bias(int j) const {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), j - cb));
+  }
+};
+
 // Work items (b*h, query tile) of a (possibly persistent) grid.  Workgroups
 // are handed to the 8 XCDs round-robin, so workgroup w runs on XCD w % 8.
 // When B*H is a multiple of 8, XCD x owns the heads x, x+8, ... (a head's

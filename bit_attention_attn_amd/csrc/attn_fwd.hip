@@ -61,7 +61,6 @@ struct Fwd16Params {
   const uint16_t* v;
   void* o;
   float* lse;
-  const float* bias;
   int N;
   int nq;      // query tiles per head
   int nbh;     // B*H
@@ -69,6 +68,12 @@ struct Fwd16Params {
   int ntiles;  // B*H*nq
   float c;     // scale * log2(e), never 0
   int out_f32;
+  // general layout (strided entry point only): element strides (batch, head,
+  // token) of q, k, v, o with d contiguous, and optional packed sequences
+  // (cu: sequence b holds tokens cu[b] .. cu[b+1]-1; N is the longest)
+  int H;
+  const int* cu;
+  int64_t qs[3], ks[3], vs[3], os[3];
 };
 
 template <int D, int QS, int NW>
@@ -87,8 +92,17 @@ struct Fwd16Smem {
   static constexpr int kElems = T::kKbuf * kKTile + T::kVbuf * kVTile;
 };
 
-template <int D, bool BF16, bool CAUSAL, int QS, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
+// Kernel variants by input layout: contiguous without a bias (the plain loop
+// over key blocks), contiguous with a block bias (adds the block-sparse skip)
+// and the general strided / packed-sequence layout (no bias).
+enum Mode { kDense = 0, kBias = 1, kGen = 2 };
+
+// The block bias comes as its own restrict argument: its reads, uniform and
+// never written by the kernel, then compile to scalar loads, which do not
+// share the in-order vector-load counter with the K/V prefetch.
+template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, const float* __restrict__ bias) {
+  constexpr bool GEN = MODE == kGen, HAS_BIAS = MODE == kBias;
   using TL = Tiling<QS, NW>;
   using S = Fwd16Smem<D, QS, NW>;
   constexpr int kWQ = TL::kWQ, kBM = TL::kBM, kThreads = TL::kThreads;
@@ -115,13 +129,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
   const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
-  const int N = p.N;
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kWQ;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Q = p.q + head;
-  const uint16_t* __restrict__ K = p.k + head;
-  const uint16_t* __restrict__ V = p.v + head;
+  // this head's row 0 (elements) and row strides; the dense layout is
+  // [B,H,N,d] contiguous
+  int N = p.N;
+  int64_t qoff, koff, voff0, ooff;
+  int qsn = D, ksn = D, vsn = D, osn = D;
+  if constexpr (GEN) {
+    const int b = bh / p.H, h = bh - b * p.H;
+    int64_t t0 = 0;
+    if (p.cu != nullptr) {
+      t0 = p.cu[b];
+      N = max(0, min(p.cu[b + 1] - p.cu[b], p.N));
+    }
+    qoff = (p.cu ? t0 * p.qs[2] : b * p.qs[0]) + h * p.qs[1];
+    koff = (p.cu ? t0 * p.ks[2] : b * p.ks[0]) + h * p.ks[1];
+    voff0 = (p.cu ? t0 * p.vs[2] : b * p.vs[0]) + h * p.vs[1];
+    ooff = (p.cu ? t0 * p.os[2] : b * p.os[0]) + h * p.os[1];
+    qsn = (int)p.qs[2];
+    ksn = (int)p.ks[2];
+    vsn = (int)p.vs[2];
+    osn = (int)p.os[2];
+    if (q0 >= N) continue;  // this sequence is shorter than the tile start
+  } else {
+    qoff = koff = voff0 = ooff = (int64_t)bh * N * D;
+  }
+  const uint16_t* __restrict__ Q = p.q + qoff;
+  const uint16_t* __restrict__ K = p.k + koff;
+  const uint16_t* __restrict__ V = p.v + voff0;
 
   // Q^T as the B operand of S^T = K Q^T: for query sub-tile qs the lane holds
   // Q[qw0 + 32qs + l32][16kk + 8hf .. +7].  Rows past N read row N-1 (their
@@ -130,7 +166,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
     const int row = min(qw0 + 32 * qs + l32, N - 1);
-    const uint16_t* src = Q + (size_t)row * D + 8 * hf;
+    const uint16_t* src = Q + (size_t)row * qsn + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) qf[qs][kk] = *(const u32x4_t*)(src + 16 * kk);
   }
@@ -146,18 +182,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   // 16*tid + (kb*64*D*2 + 16*i*threads) of the head: a buffer load with one
   // per-lane offset and a uniform one; key rows past N read zeros (masked
   // later), so every load is unconditional.
+  // (general layout: key rows ksn / vsn elements apart, so each chunk has its
+  // own per-lane offset and the block offset is kb*64 rows)
   constexpr int kNst = kBN * kCpr / kThreads;
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K, (uint32_t)N * ksn * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V, (uint32_t)N * vsn * 2);
   const uint32_t voff = 16u * tid;
+  uint32_t kvo[kNst], vvo[kNst];
+  if constexpr (GEN) {
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      kvo[i] = (uint32_t)(row * ksn * 2 + ch * 16);
+      vvo[i] = (uint32_t)(row * vsn * 2 + ch * 16);
+    }
+  }
   u32x4_t kst[kNst], vst[kNst];
   auto load_k = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) kst[i] = buffer_load16(krs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+    for (int i = 0; i < kNst; ++i) {
+      if constexpr (GEN) kst[i] = buffer_load16(krs, kvo[i], (uint32_t)(kb * kBN) * ksn * 2);
+      else kst[i] = buffer_load16(krs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+    }
   };
   auto load_v = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) vst[i] = buffer_load16(vrs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+    for (int i = 0; i < kNst; ++i) {
+      if constexpr (GEN) vst[i] = buffer_load16(vrs, vvo[i], (uint32_t)(kb * kBN) * vsn * 2);
+      else vst[i] = buffer_load16(vrs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+    }
   };
   auto store_k = [&](int buf) {
     uint16_t* ks = kbase_lds + buf * kKTile;
@@ -189,8 +242,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   const float c = p.c;
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
-  const int qb64 = min(qw0 / kBN, p.nb - 1);
-  const float* bias_row = p.bias ? p.bias + ((size_t)bh * p.nb + (size_t)qb64) * p.nb : nullptr;
 
   // transposing-read coordinates for the V^T operand: this lane addresses row
   // 16kk + vkey (and +8) at column 32dt + vcol
@@ -234,8 +285,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
 
   // ---- block maximum and lazy rescale of the running state; returns the
   // exponent offsets kc = bias - m (log2 units) of the block
-  auto block_max = [&](int j, f32x16_t (&s)[2][QS], float (&kc)[QS]) {
-    const float bl = bias_row ? bias_row[j] * kLog2e : 0.f;
+  auto block_max = [&](f32x16_t (&s)[2][QS], float (&kc)[QS], float braw) {
+    const float bl = HAS_BIAS ? braw * kLog2e : 0.f;
     float m_blk[QS];
     bool need_any = false;
 #pragma unroll
@@ -312,46 +363,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
     }
   };
 
-  // ---- block-sparse skip: a key block whose gate is 0 (bias -inf) for every
-  // query block of this tile adds nothing to any of its rows, so it is
-  // neither loaded nor computed; a wave skips blocks gated off for its own
-  // query block.  Without a bias every block is active.
-  const int qb_lo = q0 / kBN, qb_hi = min((q0 + kBM - 1) / kBN, p.nb - 1);
-  const float* bias_head = p.bias ? p.bias + (size_t)bh * p.nb * p.nb : nullptr;
-  auto tile_active = [&](int j) {
-    if (bias_head == nullptr) return true;
-    for (int qb = qb_lo; qb <= qb_hi; ++qb)
-      if (bias_head[(size_t)qb * p.nb + j] != -INFINITY) return true;
-    return false;
-  };
-  auto next_active = [&](int j) {
-    ++j;
-    while (j < nkb && !tile_active(j)) ++j;
-    return j;
-  };
+  // ---- block-sparse skip (with a bias only): a key block whose gate is 0
+  // (bias -inf) for every query block of this tile adds nothing to any of
+  // its rows, so it is neither loaded nor computed; a wave skips blocks gated
+  // off for its own query block.  The bias values a step needs are read a
+  // step ahead, so their latency hides behind a block's products.
+  constexpr int kRows = kBM / kBN;  // 64-query blocks per tile (2 or 4)
+  const int rw = wave * kWQ / kBN;  // this wave's query block in the tile
+  BlockGate<kRows> gate(HAS_BIAS ? bias + (size_t)bh * p.nb * p.nb : bias, p.nb, q0 / kBN, nkb, rw);
 
   f32x16_t sc[2][QS];
-  int jc = next_active(-1), buf = 0;
-  if (jc < nkb) {
-    load_k(jc);
-    load_v(jc);
-    store_k(0);
-    store_v(0);
-  }
-  __syncthreads();
-  // ---- the next active block loads while the current one computes
-  while (jc < nkb) {
-    const int jn = next_active(jc);
+  // ---- one key block: the next active block (jn) loads while block jc,
+  // staged in buffer buf, computes; braw is this wave's bias of block jc
+  auto step = [&](int jc, int jn, int buf, float braw) {
     const bool more = jn < nkb;
     if (more) {
       load_k(jn);
       load_v(jn);
     }
-    if (wave_has_rows && jc <= wave_last && !(bias_row && bias_row[jc] == -INFINITY)) {
+    if (wave_has_rows && jc <= wave_last && (!HAS_BIAS || braw != -INFINITY)) {
       qk(buf, sc);
       if (needs_mask(jc)) apply_mask(jc, sc);
       float kc[QS];
-      block_max(jc, sc, kc);
+      block_max(sc, kc, braw);
       softmax_p(sc, kc);
       pv(buf);
     }
@@ -360,8 +394,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
       store_v(buf ^ 1);
     }
     __syncthreads();
-    jc = jn;
-    buf ^= 1;
+  };
+  // The first block is staged unconditionally (a valid block even when every
+  // block is gated off), and its loads are issued after the Q loads (the
+  // scheduling barrier): its wait for the global loads then also covers Q,
+  // so no wait on Q lands inside the loop, where (the counter being in
+  // order) it would also wait for the next block's prefetch every iteration.
+  int j0 = 0;
+  if constexpr (HAS_BIAS) j0 = gate.first();
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(min(j0, nkb - 1));
+  load_v(min(j0, nkb - 1));
+  store_k(0);
+  store_v(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if constexpr (HAS_BIAS) {
+    // the wave's bias of block jc, then the next visited block (a wave whose
+    // query block is past the last one has no rows and ignores its bias)
+    int jc = j0;
+    float wb = jc < nkb ? gate.wave_bias(jc) : -INFINITY;
+    int jn = gate.next();
+    for (int buf = 0; jc < nkb; buf ^= 1) {
+      const float wb_next = jn < nkb ? gate.wave_bias(jn) : -INFINITY;
+      step(jc, jn, buf, wb);
+      const int jnn = gate.next();
+      jc = jn;
+      jn = jnn;
+      wb = wb_next;
+    }
+  } else {
+    // every block is active (the plain counted loop schedules measurably
+    // better than the general one)
+    for (int j = 0; j < nkb; ++j) step(j, j + 1, j & 1, 0.f);
   }
 
   // ---- epilogue: normalise, LSE, stores straight from the accumulators
@@ -373,8 +438,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
     const int qi = qw0 + 32 * qs + l32;
     if (qi < N) {
       if (p.lse != nullptr && hf == 0)
-        p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot)) * kLn2 : -INFINITY;
-      const size_t orow = head + (size_t)qi * D;
+        p.lse[(size_t)bh * p.N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      const size_t orow = (size_t)ooff + (size_t)qi * osn;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -394,7 +459,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p) {
   }  // work items
 }
 
-template <int D, bool BF16, bool CAUSAL, int QS, int NW>
+template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE>
 hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   using TL = Tiling<QS, NW>;
   Fwd16Params p;
@@ -403,7 +468,6 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   p.v = static_cast<const uint16_t*>(a.v);
   p.o = a.o;
   p.lse = a.lse;
-  p.bias = a.bias;
   p.N = a.N;
   p.nq = (a.N + TL::kBM - 1) / TL::kBM;
   p.nb = (a.N + 63) / 64;
@@ -415,15 +479,26 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   p.c = (float)((double)a.scale * 1.4426950408889634);
   if (p.c == 0.f) p.c = 1.17549435e-38f;
   p.out_f32 = a.out_kind == kOutF32;
+  p.H = a.H;
+  p.cu = a.cu;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = a.strides[i];
+    p.ks[i] = a.strides[3 + i];
+    p.vs[i] = a.strides[6 + i];
+    p.os[i] = a.strides[9 + i];
+  }
   // Causal tiles differ in cost, so a persistent grid with the balanced
   // heavy-first order pays where it applies (measured +7% at 4x32x4096,
   // d = 128); equal-cost non-causal tiles run one workgroup per item
   // (persistent was 5% slower).
-  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW>),
-                                            TL::kThreads, p.nbh, p.nq)
-                          : p.ntiles;
+  // (packed sequences of different lengths: one workgroup per tile; the
+  // balance argument of the persistent queues assumes equal heads)
+  const int grid = (CAUSAL && !(MODE == kGen && a.cu))
+                       ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE>),
+                                         TL::kThreads, p.nbh, p.nq)
+                       : p.ntiles;
   if (grid <= 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW>), dim3(grid), dim3(TL::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE>), dim3(grid), dim3(TL::kThreads), 0, stream, p, a.bias);
   return hipGetLastError();
 }
 
@@ -444,17 +519,23 @@ int tiling_override() {
   return v;
 }
 
-template <bool BF16, bool CAUSAL>
+template <bool BF16, bool CAUSAL, int MODE>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   const int t = tiling_override();
   if (a.d == 64) {
-    if (t == 1) return launch_impl<64, BF16, CAUSAL, 1, 4>(a, stream);
-    return launch_impl<64, BF16, CAUSAL, 2, 4>(a, stream);
+    if (t == 1) return launch_impl<64, BF16, CAUSAL, 1, 4, MODE>(a, stream);
+    return launch_impl<64, BF16, CAUSAL, 2, 4, MODE>(a, stream);
   }
   // d = 96: a 64 x 96 tile is 768 16-byte chunks, which 4 waves split evenly
-  if (a.d == 96) return launch_impl<96, BF16, CAUSAL, 1, 4>(a, stream);
-  if (t == 1) return launch_impl<128, BF16, CAUSAL, 1, 4>(a, stream);
-  return launch_impl<128, BF16, CAUSAL, 1, 8>(a, stream);
+  if (a.d == 96) return launch_impl<96, BF16, CAUSAL, 1, 4, MODE>(a, stream);
+  if (t == 1) return launch_impl<128, BF16, CAUSAL, 1, 4, MODE>(a, stream);
+  return launch_impl<128, BF16, CAUSAL, 1, 8, MODE>(a, stream);
+}
+
+template <bool BF16, bool CAUSAL>
+hipError_t launch_g(const FwdArgs& a, hipStream_t stream) {
+  if (a.general) return launch_d<BF16, CAUSAL, kGen>(a, stream);
+  return a.bias ? launch_d<BF16, CAUSAL, kBias>(a, stream) : launch_d<BF16, CAUSAL, kDense>(a, stream);
 }
 
 }  // namespace
@@ -490,8 +571,8 @@ int persistent_grid(const void* kernel, int threads, int nbh, int nq) {
 }
 
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream) {
-  if (bf16) return a.causal ? launch_d<true, true>(a, stream) : launch_d<true, false>(a, stream);
-  return a.causal ? launch_d<false, true>(a, stream) : launch_d<false, false>(a, stream);
+  if (bf16) return a.causal ? launch_g<true, true>(a, stream) : launch_g<true, false>(a, stream);
+  return a.causal ? launch_g<false, true>(a, stream) : launch_g<false, false>(a, stream);
 }
 
 }  // namespace attn

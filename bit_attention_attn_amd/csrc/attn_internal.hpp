@@ -21,6 +21,11 @@ struct FwdArgs {
   int causal;
   float scale;
   int out_kind;       // OutKind
+  // general layout (16-bit strided entry point): element strides (batch,
+  // head, token) of q, k, v, o; cu (nullable, device) packs sequences
+  bool general = false;
+  int64_t strides[12] = {};
+  const int* cu = nullptr;
 };
 
 // Grid for a launch over nbh * nq (head, query tile) items: the number of

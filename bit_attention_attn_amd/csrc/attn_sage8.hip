@@ -327,12 +327,10 @@ struct Fwd8Params {
   const int8_t* kq;
   const uint8_t* vq;
   const float* sq;
-  const float* sk;
   const float* sv;
   const float* kmean;
   void* o;
   float* lse;
-  const float* bias;
   int N, np, nblk;
   int nq;      // query tiles per head
   int nbh;     // B*H
@@ -369,8 +367,13 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
+// BIAS: a block bias is given (adds the block-sparse skip).  The bias and
+// the K block scales come as their own restrict arguments: their reads,
+// uniform and never written by the kernel, then compile to scalar loads,
+// which do not share the in-order vector-load counter with the K/V prefetch.
+template <int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const float* __restrict__ bias,
+                                                            const float* __restrict__ sk) {
   using S = Fwd8Smem<D>;
   constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
   constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
@@ -449,37 +452,29 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   const float c = p.c;
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
-  const int qb64 = min(qw0 / kQB, p.nb - 1);
-  const float* bias_row = p.bias ? p.bias + ((size_t)bh * p.nb + (size_t)qb64) * p.nb : nullptr;
-  const float* skrow = p.sk + (size_t)bh * p.nblk;
+  // K block scales, read one step ahead (through a buffer resource, so the
+  // read of the block after the last returns 0 and its wait falls in with
+  // the prefetch's)
+  const __amdgpu_buffer_rsrc_t skrs = buffer_rsrc(sk + (size_t)bh * p.nblk, (uint32_t)p.nblk * 4u);
+  auto sk_at = [&](int jj) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(skrs, 0u, 4u * (uint32_t)jj, 0));
+  };
 
-  // block-sparse skip: a key block gated off (bias -inf) for every query
-  // block of this tile is neither loaded nor computed; a wave skips blocks
-  // gated off for its own query block.  Without a bias every block is active.
-  const int qb_lo = q0 / kQB, qb_hi = min((q0 + kBM8 - 1) / kQB, p.nb - 1);
-  const float* bias_head = p.bias ? p.bias + (size_t)bh * p.nb * p.nb : nullptr;
-  auto tile_active = [&](int jj) {
-    if (bias_head == nullptr) return true;
-    for (int qb = qb_lo; qb <= qb_hi; ++qb)
-      if (bias_head[(size_t)qb * p.nb + jj] != -INFINITY) return true;
-    return false;
-  };
-  auto next_active = [&](int jj) {
-    ++jj;
-    while (jj < nkb && !tile_active(jj)) ++jj;
-    return jj;
-  };
-  int j = next_active(-1), buf = 0;
-  if (j < nkb) {
-    load_kv(j);
-    store_kv(0);
-  }
-  __syncthreads();
-  while (j < nkb) {
-    const int jn = next_active(j);
+  // ---- block-sparse skip (with a bias only): a key block gated off (bias
+  // -inf) for every query block of this tile is neither loaded nor computed;
+  // a wave skips blocks gated off for its own query block.  The bias values
+  // a step needs are read a step ahead.
+  constexpr int kRows = kBM8 / kQB;  // 64-query blocks per tile
+  const int rw = wave * 32 / kQB;    // this wave's query block in the tile
+  BlockGate<kRows> gate(BIAS ? bias + (size_t)bh * p.nb * p.nb : bias, p.nb, q0 / kQB, nkb, rw);
+
+  // ---- one key block: the next active block (jn) loads while block jc,
+  // staged in buffer buf, computes; braw is this wave's bias of block jc and
+  // skc the scale of its K block
+  auto step = [&](int jc, int jn, int buf, float braw, float skc) {
     const bool more = jn < nkb;
     if (more) load_kv(jn);
-    if (wave_has_rows && j <= wave_last && !(bias_row && bias_row[j] == -INFINITY)) {
+    if (wave_has_rows && jc <= wave_last && (!BIAS || braw != -INFINITY)) {
       // ---- S^T = Kq Qq^T on top of the offset, exact
       const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
       i32x16_t si[2];
@@ -497,12 +492,12 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
         }
       // s = kMagic + S_int; base 2: t = S_int * f + bias*log2(e)
       //                               = s * f + g,  g = bias*log2(e) - kMagic * f
-      const float f = (sqw * skrow[j]) * c;
+      const float f = (sqw * skc) * c;
       f32x16_t s[2];
 #pragma unroll
       for (int T = 0; T < 2; ++T) s[T] = __builtin_bit_cast(f32x16_t, si[T]);
-      if ((CAUSAL && j == wave_last) || (j + 1) * kQB > N) {
-        const int kb0 = j * kQB, qi = qw0 + l32;
+      if ((CAUSAL && jc == wave_last) || (jc + 1) * kQB > N) {
+        const int kb0 = jc * kQB, qi = qw0 + l32;
 #pragma unroll
         for (int T = 0; T < 2; ++T)
 #pragma unroll
@@ -512,7 +507,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
             s[T][r] = m ? sent : s[T][r];
           }
       }
-      const float bl = bias_row ? bias_row[j] * kLog2e : 0.f;
+      const float bl = BIAS ? braw * kLog2e : 0.f;
       const float g = fmaf(-kMagic, f, bl);
       float a0;
       if (pos) {
@@ -566,8 +561,43 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
     }
     if (more) store_kv(buf ^ 1);
     __syncthreads();
-    j = jn;
-    buf ^= 1;
+  };
+  // The first block is staged unconditionally (a valid block even when every
+  // block is gated off), after the Q loads (the scheduling barrier): its wait
+  // for the global loads then also covers Q, so no wait on Q lands inside the
+  // loop, where (the counter being in order) it would also wait for the next
+  // block's prefetch every iteration.
+  int j0 = 0;
+  if constexpr (BIAS) j0 = gate.first();
+  __builtin_amdgcn_sched_barrier(0);
+  load_kv(min(j0, nkb - 1));
+  store_kv(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if constexpr (BIAS) {
+    // the wave's bias of block jc, then the next visited block (a wave whose
+    // query block is past the last one has no rows and ignores its bias)
+    int jc = j0;
+    float wb = jc < nkb ? gate.wave_bias(jc) : -INFINITY;
+    float skc = sk_at(jc);
+    int jn = gate.next();
+    for (int buf = 0; jc < nkb; buf ^= 1) {
+      const float wb_next = jn < nkb ? gate.wave_bias(jn) : -INFINITY;
+      const float sk_next = sk_at(jn);
+      step(jc, jn, buf, wb, skc);
+      const int jnn = gate.next();
+      jc = jn;
+      jn = jnn;
+      wb = wb_next;
+      skc = sk_next;
+    }
+  } else {
+    float skc = sk_at(0);
+    for (int j = 0; j < nkb; ++j) {
+      const float sk_next = sk_at(j + 1);
+      step(j, j + 1, j & 1, 0.f, skc);
+      skc = sk_next;
+    }
   }
 
   // ---- epilogue: O = acc * sv[d] / l; LSE = (m + log2 l - kPlog) ln 2 plus
@@ -615,7 +645,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p) {
   }  // work items
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   const Sage8Layout L = sage8_layout(a.B, a.H, a.N, D);
   const char* w = static_cast<const char*>(ws);
@@ -624,12 +654,10 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   p.kq = reinterpret_cast<const int8_t*>(w + L.kq);
   p.vq = reinterpret_cast<const uint8_t*>(w + L.vq);
   p.sq = reinterpret_cast<const float*>(w + L.sq);
-  p.sk = reinterpret_cast<const float*>(w + L.sk);
   p.sv = reinterpret_cast<const float*>(w + L.sv);
   p.kmean = reinterpret_cast<const float*>(w + L.kmean);
   p.o = a.o;
   p.lse = a.lse;
-  p.bias = a.bias;
   p.N = a.N;
   p.nblk = L.nblk;
   p.np = L.nblk * kQB;
@@ -642,11 +670,12 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   p.out_kind = a.out_kind;
   // persistent grid for causal shapes (tiles differ in cost), one workgroup
   // per tile otherwise
-  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL>), kThreads8,
+  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS>), kThreads8,
                                             p.nbh, p.nq)
                           : p.ntiles;
   if (grid <= 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads8), 0, stream, p);
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, BIAS>), dim3(grid), dim3(kThreads8), 0, stream, p, a.bias,
+                     reinterpret_cast<const float*>(w + L.sk));
   return hipGetLastError();
 }
 
@@ -662,10 +691,18 @@ hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool b
               : prep_impl<128, false>(q, k, v, B, H, N, ws, stream);
 }
 
+namespace {
+template <int D>
+hipError_t fwd8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  if (a.bias) return a.causal ? fwd8_impl<D, true, true>(ws, a, stream) : fwd8_impl<D, false, true>(ws, a, stream);
+  return a.causal ? fwd8_impl<D, true, false>(ws, a, stream) : fwd8_impl<D, false, false>(ws, a, stream);
+}
+}  // namespace
+
 hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return a.causal ? fwd8_impl<64, true>(ws, a, stream) : fwd8_impl<64, false>(ws, a, stream);
-  if (a.d == 96) return a.causal ? fwd8_impl<96, true>(ws, a, stream) : fwd8_impl<96, false>(ws, a, stream);
-  return a.causal ? fwd8_impl<128, true>(ws, a, stream) : fwd8_impl<128, false>(ws, a, stream);
+  if (a.d == 64) return fwd8_d<64>(ws, a, stream);
+  if (a.d == 96) return fwd8_d<96>(ws, a, stream);
+  return fwd8_d<128>(ws, a, stream);
 }
 
 }  // namespace attn

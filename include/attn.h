@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
     ATTN_OK = 0,
@@ -92,6 +92,36 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                           float* lse, int B, int H, int N, int d, int causal,
                           float scale, const float* bias, int out_dtype,
                           void* stream);
+
+/*
+ * attn_fwd_strided_f16 / attn_fwd_strided_bf16 -- the same forward on
+ * tensors of any layout with d contiguous, and on packed sequences of
+ * different lengths (the drop-in layouts of the SageAttention page's
+ * integration section and of a scaled-dot-product-attention call: e.g.
+ * [B,N,H,d] token-major tensors, or q/k/v as views of one fused projection).
+ *
+ *  strides    host array of 12 element strides: for q, k, v, o in turn the
+ *             (batch, head, token) strides; d is contiguous.  Each stride is
+ *             >= 0 and a multiple of 8 elements (16-byte rows), each token
+ *             stride >= d, and N * token stride * 2 < 2^32 bytes.
+ *  cu_seqlens nullable device int32 [B+1]: packed sequences.  Sequence b is
+ *             tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of the token axis
+ *             (the batch strides are then unused) and attends only within
+ *             itself; N is the longest length.  The values are read on the
+ *             device and not validated: they must be non-decreasing with
+ *             every length <= N (longer lengths are clamped to N).
+ *  lse        nullable fp32 [B,H,N] (row b,h,i for i < the sequence length).
+ *  Other arguments as attn_fwd_f16 / attn_fwd_bf16; there is no block bias
+ *  on this entry point.  The arithmetic is that of attn_fwd_f16/bf16.
+ */
+attn_status attn_fwd_strided_f16(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int B, int H, int N, int d,
+                                 const long long* strides, const int* cu_seqlens,
+                                 int causal, float scale, int out_dtype, void* stream);
+attn_status attn_fwd_strided_bf16(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int B, int H, int N, int d,
+                                  const long long* strides, const int* cu_seqlens,
+                                  int causal, float scale, int out_dtype, void* stream);
 
 /*
  * attn_sage8_workspace_size -- bytes of device workspace that

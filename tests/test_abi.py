@@ -26,11 +26,12 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = attn.lib()
     names = _declared_functions()
-    assert {"attn_fwd_f16", "attn_fwd_bf16", "attn_sage8_workspace_size", "attn_k_smooth_quant",
+    assert {"attn_fwd_f16", "attn_fwd_bf16", "attn_fwd_strided_f16", "attn_fwd_strided_bf16",
+            "attn_sage8_workspace_size", "attn_k_smooth_quant", "attn_sage8_workspace_layout",
             "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 1
+    assert L.attn_abi_version() == 2
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -92,3 +93,29 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.fwd(q, q, q)
+
+
+def _strided(fn, strides, q=FAKE, o=FAKE, cu=None, B=1, H=2, N=64, d=64, causal=0, out=BF16):
+    arr = None if strides is None else (ctypes.c_longlong * 12)(*strides)
+    return fn(q, FAKE, FAKE, o, None, B, H, N, d, arr, cu, causal, 0.125, out, None)
+
+
+@pytest.mark.parametrize("name,dt", [("attn_fwd_strided_bf16", BF16), ("attn_fwd_strided_f16", F16)])
+def test_strided_validation(name, dt):
+    fn = getattr(attn.lib(), name)
+    # a [B,N,H,d] token-major layout: batch N*H*d, head d, token H*d
+    good = [64 * 2 * 64, 64, 2 * 64] * 4
+    assert _strided(fn, None, out=dt) == E_NULL
+    assert _strided(fn, good, q=None, out=dt) == E_NULL
+    assert _strided(fn, good, d=80, out=dt) == E_HEADDIM
+    assert _strided(fn, good, out=F16 if dt == BF16 else BF16) == E_DTYPE
+    bad = list(good); bad[4] = -64
+    assert _strided(fn, bad, out=dt) == E_ARG          # negative stride
+    bad = list(good); bad[7] = 68
+    assert _strided(fn, bad, out=dt) == E_ALIGN        # rows not 16-byte aligned
+    bad = list(good); bad[11] = 32
+    assert _strided(fn, bad, out=dt) == E_ARG          # token stride < d
+    bad = list(good); bad[2] = 1 << 28
+    assert _strided(fn, bad, N=1 << 12, out=dt) == E_SHAPE  # byte offsets beyond 32 bits
+    assert _strided(fn, good, cu=FAKE + 2, out=dt) == E_ALIGN
+    assert _strided(fn, good, causal=3, out=dt) == E_ARG

@@ -245,6 +245,15 @@ def test_block_sparse_gates(N, d, causal):
     _check(inp, causal, 1 / math.sqrt(d), label=f"sparse N={N} d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_chunk_boundaries(d, causal):
+    """Tiles over more than 64 key blocks: the skip steps through the gates 64
+    key blocks at a time (the gate patterns of the 16-bit test)."""
+    inp, rows = workloads.chunk_gate_inputs(d, seed=250 + d + causal)
+    _check(inp, causal, 1 / math.sqrt(d), rows=rows, label=f"sparse chunks d={d}")
+
+
 def test_block_sparse_inactive_tiles():
     """Key block 2 off for every query block; query blocks 4..7 of head 1
     off everywhere (O = 0, LSE = -inf)."""

@@ -149,6 +149,27 @@ def parity_rows(B, H, N, seed=0, n_random=48, heads=None):
     return np.asarray(rows, dtype=np.int64)
 
 
+def chunk_gate_inputs(d, seed, dtype="bf16"):
+    """B=2, H=2, N=64*150 (150 key blocks) with random gates (keep 0.3) plus
+    two gate patterns across runs of 64 key blocks: (0,0) key blocks 60..130
+    off for every query block (64 consecutive blocks and their edges), (0,1)
+    only key blocks 0, 63, 64, 127, 128, 149 on.  Returns the inputs and the
+    rows (b,h,i) to check: block edges, random rows and rows next to those
+    runs."""
+    N = 64 * 150
+    inp = make_inputs(2, 2, N, d, dtype, seed=seed, gate=True, gate_keep=0.3)
+    bias = inp["bias"]
+    bias[0, 0, :, 60:131] = float("-inf")
+    on = torch.zeros(150, dtype=torch.bool)
+    on[[0, 63, 64, 127, 128, 149]] = True
+    bias[0, 1] = bias[0, 1].masked_fill(~on, float("-inf"))
+    bias[0, 1, :, 0] = 0.0
+    rows = parity_rows(2, 2, N, seed=seed, n_random=16, heads=[0, 1])
+    extra = [(b, h, i) for b in range(2) for h in range(2)
+             for i in (63 * 64 + 5, 64 * 64, 127 * 64 + 63, 128 * 64, 131 * 64 + 1, N - 1)]
+    return inp, np.unique(np.concatenate([rows, np.asarray(extra, dtype=np.int64)]), axis=0)
+
+
 def gather_rows(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
     """Pick rows (b,h,i) of a [B,H,N,d] tensor (any device) as fp64 numpy."""
     idx = torch.as_tensor(rows, dtype=torch.long, device=t.device)

@@ -452,13 +452,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   const float c = p.c;
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
-  // K block scales, read one step ahead (through a buffer resource, so the
-  // read of the block after the last returns 0 and its wait falls in with
-  // the prefetch's)
-  const __amdgpu_buffer_rsrc_t skrs = buffer_rsrc(sk + (size_t)bh * p.nblk, (uint32_t)p.nblk * 4u);
-  auto sk_at = [&](int jj) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(skrs, 0u, 4u * (uint32_t)jj, 0));
-  };
+  const float* skrow = sk + (size_t)bh * p.nblk;  // K block scales (scalar reads)
 
   // ---- block-sparse skip (with a bias only): a key block gated off (bias
   // -inf) for every query block of this tile is neither loaded nor computed;
@@ -469,9 +463,8 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   BlockGate<kRows> gate(BIAS ? bias + (size_t)bh * p.nb * p.nb : bias, p.nb, q0 / kQB, nkb, rw);
 
   // ---- one key block: the next active block (jn) loads while block jc,
-  // staged in buffer buf, computes; braw is this wave's bias of block jc and
-  // skc the scale of its K block
-  auto step = [&](int jc, int jn, int buf, float braw, float skc) {
+  // staged in buffer buf, computes; braw is this wave's bias of block jc
+  auto step = [&](int jc, int jn, int buf, float braw) {
     const bool more = jn < nkb;
     if (more) load_kv(jn);
     if (wave_has_rows && jc <= wave_last && (!BIAS || braw != -INFINITY)) {
@@ -492,7 +485,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
         }
       // s = kMagic + S_int; base 2: t = S_int * f + bias*log2(e)
       //                               = s * f + g,  g = bias*log2(e) - kMagic * f
-      const float f = (sqw * skc) * c;
+      const float f = (sqw * skrow[jc]) * c;
       f32x16_t s[2];
 #pragma unroll
       for (int T = 0; T < 2; ++T) s[T] = __builtin_bit_cast(f32x16_t, si[T]);
@@ -579,25 +572,17 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
     // query block is past the last one has no rows and ignores its bias)
     int jc = j0;
     float wb = jc < nkb ? gate.wave_bias(jc) : -INFINITY;
-    float skc = sk_at(jc);
     int jn = gate.next();
     for (int buf = 0; jc < nkb; buf ^= 1) {
       const float wb_next = jn < nkb ? gate.wave_bias(jn) : -INFINITY;
-      const float sk_next = sk_at(jn);
-      step(jc, jn, buf, wb, skc);
+      step(jc, jn, buf, wb);
       const int jnn = gate.next();
       jc = jn;
       jn = jnn;
       wb = wb_next;
-      skc = sk_next;
     }
   } else {
-    float skc = sk_at(0);
-    for (int j = 0; j < nkb; ++j) {
-      const float sk_next = sk_at(j + 1);
-      step(j, j + 1, j & 1, 0.f, skc);
-      skc = sk_next;
-    }
+    for (int j = 0; j < nkb; ++j) step(j, j + 1, j & 1, 0.f);
   }
 
   // ---- epilogue: O = acc * sv[d] / l; LSE = (m + log2 l - kPlog) ln 2 plus
@@ -607,15 +592,19 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int qi = qw0 + l32;
   if (p.lse != nullptr) {
+    // the Q codes are read again here rather than kept from the prologue,
+    // so no register has to survive the main loop for this
     const float* kmh = p.kmean + (size_t)bh * D;
     float dot = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < kKS; ++kk)
+    for (int kk = 0; kk < kKS; ++kk) {
+      const u32x4_t qc = *(const u32x4_t*)(Qq + (size_t)(qw0 + l32) * D + 32 * kk + 16 * hf);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int code = (int)(int8_t)(qf[kk][e >> 2] >> (8 * (e & 3)));
+        const int code = (int)(int8_t)(qc[e >> 2] >> (8 * (e & 3)));
         dot = fmaf((float)code, kmh[32 * kk + 16 * hf + e], dot);
       }
+    }
     dot = xor32_sum(dot);
     if (hf == 0 && qi < N)
       p.lse[(size_t)bh * N + qi] =

@@ -13,6 +13,10 @@ Functions (each cites what it follows in the C source):
                         attention formula of the section on standard
                         attention; bias: page 5, "SAS", log-form gate).
 * ``row_probs``      -- the probability row P of one query (same passage).
+* ``attn_bwd``       -- fp64 gradients dQ, dK, dV and of the block bias for
+                        a given dO (page 3, "FlashAttention", glossary: the
+                        backward pass recomputes instead of storing; page 5,
+                        "SAS": the gate's gradient through the softmax).
 * ``sage8_kmean``, ``sage8_quant_int8``, ``sage8_quant_v`` -- the 8-bit
                         preparation steps (page 1, "SageAttention",
                         "claim vs reality": K smoothing, INT8 Q/K, FP8).
@@ -52,6 +56,9 @@ def _load():
     lib.attn_oracle_row_probs.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64,
                                           _int, _dbl, _i64, _i64, _i64, _ptr]
     lib.attn_oracle_row_probs.restype = _int
+    lib.attn_oracle_bwd.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64,
+                                    _int, _dbl, _ptr, _ptr, _ptr, _ptr, _int]
+    lib.attn_oracle_bwd.restype = _int
     lib.attn_oracle_max_threads.argtypes = []
     lib.attn_oracle_max_threads.restype = _int
     lib.sage8_e4m3_encode.argtypes = [_dbl]
@@ -124,6 +131,30 @@ def attn_full(q, k, v, causal=False, scale=None, bias=None, nthreads=0):
     rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
     o, l = attn_rows(q, k, v, rows, causal=causal, scale=scale, bias=bias, nthreads=nthreads)
     return o.reshape(B, H, N, d), l.reshape(B, H, N)
+
+
+def attn_bwd(q, k, v, dout, causal=False, scale=None, bias=None, nthreads=0):
+    """fp64 gradients of sum(dout * O) for O = attention(q, k, v): returns
+    (dq, dk, dv [B,H,N,d], dbias [B,H,nb,nb] or None when bias is None).
+    All forward quantities are recomputed from the inputs."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, N, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nb = (N + 63) // 64
+    if bias is not None:
+        bias = _f32(bias)
+        assert bias.shape == (B, H, nb, nb), bias.shape
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(q.shape, dtype=np.float64)
+    dv = np.zeros(q.shape, dtype=np.float64)
+    db = np.zeros((B, H, nb, nb), dtype=np.float64) if bias is not None else None
+    rc = _load().attn_oracle_bwd(_p(q), _p(k), _p(v), _p(dout), _p(bias), B, H, N, d, int(bool(causal)),
+                                 float(scale), _p(dq), _p(dk), _p(dv), _p(db), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_bwd failed with code {rc}")
+    return dq, dk, dv, db
 
 
 def row_probs(q, k, b, h, i, causal=False, scale=None, bias=None):

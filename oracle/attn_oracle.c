@@ -162,3 +162,106 @@ int attn_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Gradients of the attention above (page 3, "FlashAttention", the glossary
+ * paragraph: the backward pass recomputes the small intermediate quantities
+ * instead of storing the score matrix; page 5, "SAS": the log-form gate sits
+ * inside the softmax so that the loss's gradient reaches it).  For a loss L
+ * with dO = dL/dO, per row (b,h,i), with P the probability row of the
+ * definition above and s the (scaled, biased) score row:
+ *
+ *   dV[j]  += P_ij * dO_i                      (O_i = sum_j P_ij V_j)
+ *   dp_ij   = dO_i . V_j                       (dL/dP_ij)
+ *   ds_ij   = P_ij * (dp_ij - sum_k P_ik dp_ik)  (softmax Jacobian: dL/ds_ij)
+ *   dQ_i   += scale * ds_ij * K_j,   dK_j += scale * ds_ij * Q_i
+ *   dbias[b,h,i/64,j/64] += ds_ij               (the bias enters s unscaled)
+ *
+ * Everything in fp64 from the exact input values; the forward quantities
+ * are recomputed here, nothing is taken from a GPU run.  Outputs are fp64
+ * [B,H,N,d] (dq, dk, dv) and [B,H,nb,nb] (dbias, nullable), overwritten.
+ * OpenMP runs over (b,h) heads.  Returns 0 on success.
+ */
+int attn_oracle_bwd(const float* q, const float* k, const float* v,
+                    const float* dout, const float* bias, int64_t B,
+                    int64_t H, int64_t N, int64_t d, int causal, double scale,
+                    double* dq, double* dk, double* dv, double* dbias,
+                    int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B <= 0 || H <= 0 ||
+        N <= 0 || d <= 0)
+        return 1;
+    const int64_t nb = (N + ORACLE_BIAS_BLOCK - 1) / ORACLE_BIAS_BLOCK;
+    memset(dq, 0, (size_t)(B * H * N * d) * sizeof(double));
+    memset(dk, 0, (size_t)(B * H * N * d) * sizeof(double));
+    memset(dv, 0, (size_t)(B * H * N * d) * sizeof(double));
+    if (dbias)
+        memset(dbias, 0, (size_t)(B * H * nb * nb) * sizeof(double));
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)N * sizeof(double));
+        double* dp = (double*)malloc((size_t)N * sizeof(double));
+        if (!s || !dp) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            if (!s || !dp)
+                continue;
+            const int64_t b = bh / H, h = bh % H;
+            const float* kb = k + bh * N * d;
+            const float* vb = v + bh * N * d;
+            for (int64_t i = 0; i < N; ++i) {
+                const double m = row_scores(q, k, bias, H, N, d, causal, scale, b, h, i, s);
+                if (m == -INFINITY)
+                    continue; /* no visible key: O = 0, no gradient */
+                double l = 0.0;
+                for (int64_t j = 0; j < N; ++j) {
+                    s[j] = exp(s[j] - m); /* s now holds unnormalised P */
+                    l += s[j];
+                }
+                const float* doi = dout + (bh * N + i) * d;
+                const float* qi = q + (bh * N + i) * d;
+                double pdp = 0.0; /* sum_k P_ik dp_ik */
+                for (int64_t j = 0; j < N; ++j) {
+                    s[j] /= l;
+                    dp[j] = 0.0;
+                    if (s[j] == 0.0)
+                        continue;
+                    const float* vj = vb + j * d;
+                    for (int64_t c = 0; c < d; ++c)
+                        dp[j] += (double)doi[c] * (double)vj[c];
+                    pdp += s[j] * dp[j];
+                }
+                double* dqi = dq + (bh * N + i) * d;
+                for (int64_t j = 0; j < N; ++j) {
+                    const double pj = s[j];
+                    if (pj == 0.0)
+                        continue;
+                    const double dsj = pj * (dp[j] - pdp);
+                    double* dvj = dv + (bh * N + j) * d;
+                    double* dkj = dk + (bh * N + j) * d;
+                    const float* kj = kb + j * d;
+                    for (int64_t c = 0; c < d; ++c) {
+                        dvj[c] += pj * (double)doi[c];
+                        dkj[c] += scale * dsj * (double)qi[c];
+                        dqi[c] += scale * dsj * (double)kj[c];
+                    }
+                    if (dbias)
+                        dbias[(bh * nb + i / ORACLE_BIAS_BLOCK) * nb + j / ORACLE_BIAS_BLOCK] += dsj;
+                }
+            }
+        }
+        free(s);
+        free(dp);
+    }
+    return failed ? 3 : 0;
+}

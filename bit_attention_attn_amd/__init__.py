@@ -26,7 +26,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_strided", "fwd_varlen", "sage8_prep", "fwd_sage8", "sageattn", "AttnError",
+__all__ = ["fwd", "fwd_strided", "fwd_varlen", "bwd", "attention", "sage8_prep", "fwd_sage8", "sageattn", "AttnError",
            "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH", "status_str"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -62,6 +62,12 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_fwd_strided_f16", "attn_fwd_strided_bf16"):
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, ll_p, vp, i, f, i, vp]
+        fn.restype = i
+    L.attn_bwd_workspace_size.argtypes = [i, i, i, i]
+    L.attn_bwd_workspace_size.restype = sz
+    for name in ("attn_bwd_f16", "attn_bwd_bf16"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp, sz, vp]
         fn.restype = i
     L.attn_sage8_workspace_size.argtypes = [i, i, i, i]
     L.attn_sage8_workspace_size.restype = sz
@@ -133,6 +139,64 @@ def fwd(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse
     if st != 0:
         raise AttnError(st, fn.__name__)
     return (o, lse) if return_lse else o
+
+
+def bwd(q, k, v, o, dout, lse, causal=False, scale=None, bias=None, grad_dtype=None, return_dbias=False):
+    """Gradients of the fused forward: given the forward's inputs, its output
+    o (q's dtype, or float32 for an exact row statistic D) and LSE, and
+    dout = dL/dO, returns (dq, dk, dv), plus the fp32 gradient of the
+    [B,H,nb,nb] block bias when return_dbias.  d must be 64 or 128."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    for name, t, dts in (("o", o, (q.dtype, torch.float32)), ("dout", dout, (q.dtype,))):
+        if not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype not in dts or t.device != q.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32 \
+            or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor on q's device")
+    bias = _check_bias(bias, B, H, N, q.device)
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) for _ in range(3))
+    nb = (N + 63) // 64
+    dbias = torch.empty((B, H, nb, nb), dtype=torch.float32, device=q.device) if return_dbias else None
+    wsb = lib().attn_bwd_workspace_size(B, H, N, d)
+    ws = torch.empty((max(wsb, 256),), dtype=torch.uint8, device=q.device)
+    fn = lib().attn_bwd_bf16 if q.dtype == torch.bfloat16 else lib().attn_bwd_f16
+    with torch.cuda.device(q.device):
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE_CODE[o.dtype], _ptr(dout), _ptr(lse), _ptr(dq),
+                _ptr(dk), _ptr(dv),
+                _ptr(dbias), B, H, N, d, int(bool(causal)), float(scale), _ptr(bias),
+                _DTYPE_CODE.get(grad_dtype, -1), _ptr(ws), ws.numel(), _stream(q.device))
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+    return (dq, dk, dv, dbias) if return_dbias else (dq, dk, dv)
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, bias, causal, scale):
+        o, lse = fwd(q, k, v, causal=causal, scale=scale, bias=bias, return_lse=True)
+        ctx.save_for_backward(q, k, v, o, lse, bias)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse, bias = ctx.saved_tensors
+        need_db = bias is not None and ctx.needs_input_grad[3]
+        g = bwd(q, k, v, o, dout.contiguous(), lse, causal=ctx.causal, scale=ctx.scale, bias=bias,
+                return_dbias=need_db)
+        return g[0], g[1], g[2], (g[3] if need_db else None), None, None
+
+
+def attention(q, k, v, causal=False, scale=None, bias=None):
+    """Differentiable fused attention (fp16/bf16, d = 64 or 128): the forward
+    kernel, and the backward kernels for torch.autograd (gradients for q, k,
+    v and the block bias)."""
+    return _Attention.apply(q, k, v, bias, bool(causal), scale)
 
 
 def _strided_call(q, k, v, o, lse, B, H, N, d, strides, cu, causal, scale, out_dtype):

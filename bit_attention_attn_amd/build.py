@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_sage8.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_sage8.hip", "attn_bwd.hip", "attn_bwd_kv.hip"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no packed fp32 VALU instructions in device code.
@@ -35,9 +35,18 @@ def _hipcc():
     return "hipcc"
 
 
+# The key-side backward kernel holds two matrix accumulators of D/32 x 16
+# registers each besides its operands: it keeps them in AGPRs instead.
+NO_VGPR_FORM = {"attn_bwd_kv.hip"}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS]
+    flags = FLAGS
+    if src in NO_VGPR_FORM:
+        i = flags.index("-amdgpu-mfma-vgpr-form")
+        flags = flags[:i - 1] + flags[i + 1:]
+    cmd = [_hipcc(), *flags]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -109,6 +109,36 @@ attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v
   return ATTN_OK;
 }
 
+attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dbias, int B, int H,
+                  int N, int d, int causal, float scale, const float* bias, int grad_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if ((int64_t)B * H * N * d >= kMaxElems) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_ARG;
+  const int in_dtype = bf16 ? ATTN_DTYPE_BF16 : ATTN_DTYPE_F16;
+  if (grad_dtype != in_dtype && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (o_dtype != in_dtype && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_size(B, H, N, d)) return ATTN_ERR_WORKSPACE;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned(ptr, 16)) return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(workspace, 256) || (bias && !aligned(bias, 4)) || (dbias && !aligned(dbias, 4)))
+    return ATTN_ERR_ALIGN;
+  attn_status s = check_device();
+  if (s != ATTN_OK) return s;
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dbias, bias, static_cast<float*>(workspace),
+                  B, H, N, d, causal, scale,
+                  grad_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16),
+                  o_dtype == ATTN_DTYPE_F32};
+  if (attn::launch_bwd16(a, bf16, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +215,28 @@ attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B, in
   if (attn::launch_fwd_sage8(workspace, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  if ((int64_t)B * H * N * d >= kMaxElems) return 0;
+  return ((size_t)B * H * N * sizeof(float) + 255) & ~(size_t)255;
+}
+
+attn_status attn_bwd_f16(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, float* dbias, int B, int H, int N,
+                         int d, int causal, float scale, const float* bias, int grad_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return bwd16(false, q, k, v, o, o_dtype, dout, lse, dq, dk, dv, dbias, B, H, N, d, causal, scale, bias, grad_dtype,
+               workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* dbias, int B, int H, int N,
+                          int d, int causal, float scale, const float* bias, int grad_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return bwd16(true, q, k, v, o, o_dtype, dout, lse, dq, dk, dv, dbias, B, H, N, d, causal, scale, bias, grad_dtype,
+               workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_str(int status) {

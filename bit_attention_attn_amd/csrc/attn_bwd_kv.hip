@@ -1,0 +1,322 @@
+// attn_bwd_kv.hip -- key side of the attention backward (fp16/bf16) on gfx950:
+// dK, dV and the gradient of the 64x64 block bias.
+//
+// The formulas are those of attn_bwd.hip (page 3, "FlashAttention": the
+// backward recomputes P from Q, K and the saved LSE; page 5, "SAS": the
+// log-form gate inside the softmax receives dS summed over its block).
+//
+// A workgroup of 4 waves owns 128 keys of one (b, h); each wave holds its 32
+// keys' K and V rows in registers and streams the query blocks (64 rows of
+// Q and dO, with their LSE and D) through LDS, double-buffered.  Per block,
+// in halves of 32 queries:
+//   S = Q K^T and dP = dO V^T (32x32x16 MFMA; Q and dO rows from LDS, K and
+//       V rows as the B operands), one key per lane column;
+//   P = exp2(c S + bias*log2e - LSE*log2e), dS = P (dP - D), with the LSE
+//       and D of the accumulator's 16 query rows read from LDS;
+//   dV^T += dO^T P and dK^T += Q^T dS: P and dS go from the accumulator
+//       registers into the B operand, dO^T and Q^T come from the row-major
+//       tiles by the transposing LDS read.
+// The block-bias gradient of a (64-query block, 64-key block) pair is the
+// sum of dS over it; the two waves that share a key block each add their
+// half to the zeroed output with one atomic add (two addends on zero, so the
+// result does not depend on their order).
+//
+// The two accumulators (2 x 16 x D/32 registers) plus K, V and the staging
+// registers exceed 256 VGPRs at d = 128, so this file is built without the
+// VGPR-form option: the accumulators live in AGPRs, one wave per SIMD.
+#include "attn_common.hpp"
+#include "attn_internal.hpp"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace attn {
+namespace {
+
+constexpr int kQBk = 64;  // queries per staged block
+constexpr int kNWk = 4;   // waves per workgroup
+constexpr int kBK = 32 * kNWk;  // keys per workgroup
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.f;
+}
+
+struct BwdKParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* delta;
+  void* dk;
+  void* dv;
+  int N;
+  int nkt;  // key tiles per head
+  int nbh;
+  int nb;
+  float c;  // scale * log2(e), never 0
+  float scale;
+  int out_f32;
+};
+
+template <int D, bool BF16, bool CAUSAL, bool HAS_BIAS, bool DBIAS>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const float* __restrict__ bias,
+                                                          float* __restrict__ dbias) {
+  constexpr int kThreads = 64 * kNWk;
+  constexpr int kKS = D / 16;
+  constexpr int kDT = D / 32;
+  constexpr int kCpr = D / 8;
+  // Q and dO rows are read both ways (rows for S and dP, transposing reads
+  // for dK and dV)
+  constexpr int kRow = D == 64 ? D + 32 : D + 16;
+  constexpr int kTile = kQBk * kRow;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * kTile];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][kQBk];  // [buf][lse2, delta][row]
+  uint16_t* const ql = smem;
+  uint16_t* const dl = smem + 2 * kTile;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int N = p.N;
+
+  const WorkQueue wq = work_queue(p.nbh, p.nkt);
+  for (int round = 0;; ++round) {
+  int bh, kt;
+  if (!work_item(wq, round, p.nkt, bh, kt)) break;  // causal: low key tiles (most queries) first
+  const int k0 = kt * kBK;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  const int krow = min(key, N - 1);
+  const size_t head = (size_t)bh * N * D;
+
+  // K and V rows as B operands: lane holds key `key`, d = 16kk + 8hf .. +7
+  u32x4_t kf[kKS], vf[kKS];
+#pragma unroll
+  for (int kk = 0; kk < kKS; ++kk) {
+    kf[kk] = *(const u32x4_t*)(p.k + head + (size_t)krow * D + 16 * kk + 8 * hf);
+    vf[kk] = *(const u32x4_t*)(p.v + head + (size_t)krow * D + 16 * kk + 8 * hf);
+  }
+
+  const int nqb = (N + kQBk - 1) / kQBk;
+  const int jq0 = CAUSAL ? k0 / kQBk : 0;  // earlier queries see none of these keys
+  const bool wave_has_keys = kw0 < N;
+  const int kb = kw0 / 64;  // this wave's 64-key bias block
+
+  // loader: chunk tid + i*threads of the Q (dO) block at byte 16*tid +
+  // jq*64*D*2 + 16*i*threads; rows past N read zeros
+  constexpr int kNst = kQBk * kCpr / kThreads;
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(p.q + head, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(p.dout + head, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t lrs = buffer_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(p.delta + (size_t)bh * N, (uint32_t)N * 4);
+  const uint32_t voff = 16u * tid;
+  u32x4_t qst[kNst], dst[kNst];
+  float sst = 0.f;  // wave 0: LSE of row `lane` of the block; wave 1: its D
+  auto load_q = [&](int jq) {
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      qst[i] = buffer_load16(qrs, voff, jq * kQBk * D * 2 + 16 * i * kThreads);
+      dst[i] = buffer_load16(drs, voff, jq * kQBk * D * 2 + 16 * i * kThreads);
+    }
+    // wave 0 reads the LSE, wave 1 the D of the block's rows (rows past N
+    // read 0 and are masked)
+    const uint32_t o4 = 4u * (uint32_t)(jq * kQBk + lane);
+    if (wave == 0) sst = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, o4, 0u, 0));
+    if (wave == 1) sst = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, o4, 0u, 0));
+  };
+  auto store_q = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kNst; ++i) {
+      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      *(u32x4_t*)(ql + buf * kTile + row * kRow + ch * 8) = qst[i];
+      *(u32x4_t*)(dl + buf * kTile + row * kRow + ch * 8) = dst[i];
+    }
+    // a row with no visible key (LSE = -inf) has P = 0 everywhere
+    if (wave == 0) stat[buf][0][lane] = sst == -INFINITY ? INFINITY : sst * kLog2e;
+    if (wave == 1) stat[buf][1][lane] = sst;
+  };
+
+  f32x16_t dka[kDT], dva[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) dka[dt] = dva[dt] = f32x16_t{};
+  const float c = p.c;
+
+  // transposing-read coordinates (Q^T and dO^T operands)
+  const int g16 = lane >> 4, t16 = lane & 15;
+  const int tq = 4 * hf + (t16 >> 2);
+  const int tcol = 16 * (g16 & 1) + 4 * (t16 & 3);
+
+  // one 32-query half u of staged block jq; returns this lane's sum of dS
+  auto half = [&](int jq, int buf, int u) {
+    const int qs0 = jq * kQBk + 32 * u;
+    const float bl = HAS_BIAS ? bias[((size_t)bh * p.nb + jq) * p.nb + kb] * kLog2e : 0.f;
+    const uint16_t* Qs = ql + buf * kTile + (32 * u + l32) * kRow + 8 * hf;
+    const uint16_t* Ds = dl + buf * kTile + (32 * u + l32) * kRow + 8 * hf;
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      s = mfma32x32x16<BF16>(*(const u32x4_t*)(Qs + 16 * kk), kf[kk], s);
+      dp = mfma32x32x16<BF16>(*(const u32x4_t*)(Ds + 16 * kk), vf[kk], dp);
+    }
+    const bool msk = (CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N || kw0 + 32 > N;
+    float pr[16], ds[16], dsum = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // rows 32u + 8g + 4hf .. +3 of the block
+      const f32x4_t l4 = *(const f32x4_t*)(&stat[buf][0][32 * u + 8 * g + 4 * hf]);
+      const f32x4_t d4 = *(const f32x4_t*)(&stat[buf][1][32 * u + 8 * g + 4 * hf]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float x = exp2_approx(fmaf(s[r], c, bl - l4[e]));
+        if (msk) {
+          const int q = qs0 + 8 * g + 4 * hf + e;
+          if ((CAUSAL && key > q) || q >= N || key >= N) x = 0.f;
+        }
+        pr[r] = x;
+        ds[r] = x * (dp[r] - d4[e]);
+        dsum += ds[r];
+      }
+    }
+    // P and dS in the register order of the B operand: step t holds queries
+    // 32u + 16t + 4hf + {0..3} and 32u + 16t + 8 + 4hf + {0..3}
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4_t pp, pd;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        pp[e >> 1] = pack2<BF16>(pr[8 * t + e], pr[8 * t + e + 1]);
+        pd[e >> 1] = pack2<BF16>(ds[8 * t + e], ds[8 * t + e + 1]);
+      }
+      const int rowt = (32 * u + 16 * t + tq) * kRow + tcol;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+        const uint16_t* dtp = dl + buf * kTile + rowt + 32 * dt;
+        const uint16_t* qtp = ql + buf * kTile + rowt + 32 * dt;
+        const u32x2_t dlo = lds_read_tr16(dtp), dhi = lds_read_tr16(dtp + 8 * kRow);
+        const u32x2_t qlo = lds_read_tr16(qtp), qhi = lds_read_tr16(qtp + 8 * kRow);
+        dva[dt] = mfma32x32x16<BF16>(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, pp, dva[dt]);
+        dka[dt] = mfma32x32x16<BF16>(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, pd, dka[dt]);
+      }
+    }
+    return dsum;
+  };
+
+  if (jq0 < nqb) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(jq0);
+    store_q(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
+  __syncthreads();
+  for (int jq = jq0, buf = 0; jq < nqb; ++jq, buf ^= 1) {
+    const bool more = jq + 1 < nqb;
+    if (more) load_q(jq + 1);
+    float dsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qs0 = jq * kQBk + 32 * u;
+      const bool live = wave_has_keys && qs0 < N && !(CAUSAL && qs0 + 31 < kw0) &&
+                        (!HAS_BIAS || bias[((size_t)bh * p.nb + jq) * p.nb + kb] != -INFINITY);
+      if (live) dsum += half(jq, buf, u);
+    }
+    if constexpr (DBIAS) {
+      // sum over the wave, then one add per wave to the zeroed output
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
+      dsum = xor32_sum(dsum);
+      if (lane == 0 && wave_has_keys) atomicAdd(&dbias[((size_t)bh * p.nb + jq) * p.nb + kb], dsum);
+    }
+    if (more) store_q(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale * dka, dV = dva; lane (l32, hf) holds d =
+  // 32dt + 8g + 4hf .. +3 of key `key`
+  if (key < N) {
+    const size_t orow = head + (size_t)key * D;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hf;
+        const f32x4_t wk = {dka[dt][4 * g] * p.scale, dka[dt][4 * g + 1] * p.scale, dka[dt][4 * g + 2] * p.scale,
+                            dka[dt][4 * g + 3] * p.scale};
+        const f32x4_t wv = {dva[dt][4 * g], dva[dt][4 * g + 1], dva[dt][4 * g + 2], dva[dt][4 * g + 3]};
+        if (p.out_f32) {
+          *(f32x4_t*)(reinterpret_cast<float*>(p.dk) + orow + d) = wk;
+          *(f32x4_t*)(reinterpret_cast<float*>(p.dv) + orow + d) = wv;
+        } else {
+          *(u32x2_t*)(reinterpret_cast<uint16_t*>(p.dk) + orow + d) =
+              u32x2_t{pack2<BF16>(wk[0], wk[1]), pack2<BF16>(wk[2], wk[3])};
+          *(u32x2_t*)(reinterpret_cast<uint16_t*>(p.dv) + orow + d) =
+              u32x2_t{pack2<BF16>(wv[0], wv[1]), pack2<BF16>(wv[2], wv[3])};
+        }
+      }
+  }
+  }  // work items
+}
+
+template <int D, bool BF16, bool CAUSAL, bool HAS_BIAS>
+void launch_kv(const BwdKParams& p, const BwdArgs& a, hipStream_t stream) {
+  const dim3 grid(p.nkt * p.nbh), block(256);
+  if (a.dbias)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, HAS_BIAS, true>), grid, block, 0, stream, p, a.bias,
+                       a.dbias);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, HAS_BIAS, false>), grid, block, 0, stream, p, a.bias,
+                       a.dbias);
+}
+
+template <int D, bool BF16>
+void launch_kv_d(const BwdKParams& p, const BwdArgs& a, hipStream_t stream) {
+  if (a.causal) {
+    if (a.bias) launch_kv<D, BF16, true, true>(p, a, stream);
+    else launch_kv<D, BF16, true, false>(p, a, stream);
+  } else {
+    if (a.bias) launch_kv<D, BF16, false, true>(p, a, stream);
+    else launch_kv<D, BF16, false, false>(p, a, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd16_kv(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  const int nb = (a.N + 63) / 64;
+  if (a.dbias) {
+    const int64_t n = (int64_t)a.B * a.H * nb * nb;
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, stream, a.dbias, n);
+  }
+  BwdKParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.lse = a.lse;
+  p.delta = a.delta;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.N = a.N;
+  p.nkt = (a.N + kBK - 1) / kBK;
+  p.nbh = a.B * a.H;
+  p.nb = nb;
+  p.c = (float)((double)a.scale * 1.4426950408889634);
+  if (p.c == 0.f) p.c = 1.17549435e-38f;
+  p.scale = a.scale;
+  p.out_f32 = a.grad_kind == kOutF32;
+  if (a.d == 64) {
+    if (bf16) launch_kv_d<64, true>(p, a, stream);
+    else launch_kv_d<64, false>(p, a, stream);
+  } else {
+    if (bf16) launch_kv_d<128, true>(p, a, stream);
+    else launch_kv_d<128, false>(p, a, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -100,6 +100,16 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return a + b;
 }
 
+// One fp16 / bf16 value (raw bits) to fp32, exactly.
+template <bool BF16>
+__device__ __forceinline__ float in_to_f32(uint16_t x) {
+  if constexpr (BF16) {
+    return __uint_as_float((uint32_t)x << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+}
+
 // Transposing LDS read of four 16-bit values.  Within each group of 16 lanes,
 // lane 4a+b receives element b of the 8-byte rows addressed by lanes a, a+4,
 // a+8 and a+12 of the group (verified on gfx950).

@@ -38,6 +38,31 @@ int persistent_grid(const void* kernel, int threads, int nbh, int nq);
 // 16-bit path (fp16 when bf16 == false).
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream);
 
+// Backward of the 16-bit path: gradients of a loss L given dO = dL/dO and the
+// forward's O and LSE.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // forward output, input dtype or fp32 (o_f32)
+  const void* dout;   // dL/dO, input dtype
+  const float* lse;   // forward LSE [B,H,N], natural log
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dbias;       // nullable, [B,H,nb,nb], overwritten
+  const float* bias;  // nullable, [B,H,nb,nb]
+  float* delta;       // workspace [B,H,N]: rowsum(dO * O)
+  int B, H, N, d;
+  int causal;
+  float scale;
+  int grad_kind;      // OutKind of dq, dk, dv
+  bool o_f32;         // o holds fp32 values
+};
+hipError_t launch_bwd16(const BwdArgs& a, bool bf16, hipStream_t stream);
+// the key-side kernel (dK, dV, dbias), built without the VGPR-form option
+hipError_t launch_bwd16_kv(const BwdArgs& a, bool bf16, hipStream_t stream);
+
 // 8-bit path.
 struct Sage8Layout {
   // byte offsets inside the workspace, each 256-byte aligned

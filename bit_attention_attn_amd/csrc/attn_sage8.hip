@@ -83,15 +83,6 @@ __device__ __forceinline__ int key_pos(int k) {
   return 32 * h + 16 * T + 4 * g + u;
 }
 
-template <bool BF16>
-__device__ __forceinline__ float in_to_f32(uint16_t x) {
-  if constexpr (BF16) {
-    return __uint_as_float((uint32_t)x << 16);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, x);
-  }
-}
-
 // ---- colstats: grid (nchunk, B*H), prep_threads<D>() threads --------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,

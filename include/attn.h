@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
     ATTN_OK = 0,
@@ -181,6 +181,57 @@ attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v,
 attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B,
                            int H, int N, int d, int causal, float scale,
                            const float* bias, int out_dtype, void* stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd_f16/bf16
+ * need for this shape (one fp32 value per query row, 256-byte rounded; 0
+ * when the shape is invalid for the backward).
+ */
+size_t attn_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * attn_bwd_f16 / attn_bwd_bf16 -- gradients of the fused forward (page 3,
+ * "FlashAttention", the glossary paragraph: the backward pass recomputes the
+ * small intermediates from the inputs instead of storing the score matrix;
+ * page 5, "SAS": the log-form gate inside the softmax is trained through
+ * it).  For a loss L with dout = dL/dO, with P = exp(s - LSE) the exact
+ * probabilities of the forward, D = rowsum(dout * o):
+ *
+ *     dv = P^T dout,  dS = P * (dout v^T - D),
+ *     dq = scale * dS k,  dk = scale * dS^T q,
+ *     dbias[b,h,qb,kb] = sum of dS over the 64 x 64 block (qb, kb).
+ *
+ *  q, k, v    [B,H,N,d] of the forward, fp16 (f16 entry) or bf16.
+ *  o, lse     the forward's output and its LSE (fp32).  o_dtype is q's dtype
+ *             or ATTN_DTYPE_F32.  D is computed from o: with o rounded to
+ *             16 bits each row of dS sums to a small rounding residue
+ *             (below 2^-9 * sum |dout * o| relative to 0) instead of 0, which
+ *             shows in dbias; an fp32 o removes it.
+ *  dout       [B,H,N,d] dL/dO, same dtype as q.
+ *  dq, dk, dv [B,H,N,d] outputs in grad_dtype: the input dtype or
+ *             ATTN_DTYPE_F32.  Fully overwritten.
+ *  dbias      nullable fp32 [B,H,nb,nb], nb = ceil(N/64): the gradient of
+ *             the block bias (also defined when bias is NULL, as the
+ *             gradient at bias = 0).  Fully overwritten.
+ *  causal, scale, bias  as passed to the forward.
+ *  workspace  device buffer of at least attn_bwd_workspace_size bytes,
+ *             256-byte aligned; overwritten.
+ *  d must be 64 or 128.  Products run on the matrix cores with fp32
+ *  accumulation; P and dS are rounded to the input dtype for the products
+ *  that use them.  Rows with LSE = -inf (no visible key) pass no gradient.
+ *  dbias is accumulated with at most two atomic additions per element onto
+ *  zero, so results are identical from run to run.
+ */
+attn_status attn_bwd_f16(const void* q, const void* k, const void* v, const void* o,
+                         int o_dtype, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* dbias, int B, int H, int N, int d, int causal, float scale,
+                         const float* bias, int grad_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                          int o_dtype, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          float* dbias, int B, int H, int N, int d, int causal, float scale,
+                          const float* bias, int grad_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_status_str(int status);

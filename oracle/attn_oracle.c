@@ -220,6 +220,13 @@ int attn_oracle_bwd(const float* q, const float* k, const float* v,
             const float* kb = k + bh * N * d;
             const float* vb = v + bh * N * d;
             for (int64_t i = 0; i < N; ++i) {
+                /* a row with dO_i = 0 contributes nothing (dp = 0, so ds = 0) */
+                const float* doz = dout + (bh * N + i) * d;
+                int64_t nz = 0;
+                for (int64_t c = 0; c < d; ++c)
+                    nz |= (doz[c] != 0.0f);
+                if (!nz)
+                    continue;
                 const double m = row_scores(q, k, bias, H, N, d, causal, scale, b, h, i, s);
                 if (m == -INFINITY)
                     continue; /* no visible key: O = 0, no gradient */

@@ -27,11 +27,12 @@ def test_library_exports_every_declared_function():
     L = attn.lib()
     names = _declared_functions()
     assert {"attn_fwd_f16", "attn_fwd_bf16", "attn_fwd_strided_f16", "attn_fwd_strided_bf16",
+            "attn_bwd_workspace_size", "attn_bwd_f16", "attn_bwd_bf16",
             "attn_sage8_workspace_size", "attn_k_smooth_quant", "attn_sage8_workspace_layout",
             "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 2
+    assert L.attn_abi_version() == 3
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -119,3 +120,31 @@ def test_strided_validation(name, dt):
     assert _strided(fn, bad, N=1 << 12, out=dt) == E_SHAPE  # byte offsets beyond 32 bits
     assert _strided(fn, good, cu=FAKE + 2, out=dt) == E_ALIGN
     assert _strided(fn, good, causal=3, out=dt) == E_ARG
+
+
+def _bwd(fn, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, dbias=None, B=1, H=2, N=100, d=64, causal=0,
+         scale=0.125, grad=BF16, ws=FAKE, wsb=1 << 20, odt=None):
+    return fn(q, FAKE, FAKE, o, grad if odt is None else odt, FAKE, lse, dq, FAKE, FAKE, dbias, B, H, N, d,
+              causal, scale, None, grad, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name,dt", [("attn_bwd_bf16", BF16), ("attn_bwd_f16", F16)])
+def test_bwd_validation(name, dt):
+    L = attn.lib()
+    fn = getattr(L, name)
+    assert L.attn_bwd_workspace_size(1, 2, 100, 64) == 1024  # 200 fp32 rows, rounded to 256 bytes
+    assert L.attn_bwd_workspace_size(1, 2, 100, 96) == 0      # d = 96 has no backward
+    assert _bwd(fn, q=None, grad=dt) == E_NULL
+    assert _bwd(fn, lse=None, grad=dt) == E_NULL
+    assert _bwd(fn, dq=None, grad=dt) == E_NULL
+    assert _bwd(fn, B=0, grad=dt) == E_SHAPE
+    assert _bwd(fn, d=96, grad=dt) == E_HEADDIM
+    assert _bwd(fn, causal=2, grad=dt) == E_ARG
+    assert _bwd(fn, scale=float("nan"), grad=dt) == E_ARG
+    assert _bwd(fn, grad=F16 if dt == BF16 else BF16, odt=dt) == E_DTYPE
+    assert _bwd(fn, grad=dt, odt=F16 if dt == BF16 else BF16) == E_DTYPE
+    assert _bwd(fn, ws=None, grad=dt) == E_WS
+    assert _bwd(fn, wsb=1023, grad=dt) == E_WS
+    assert _bwd(fn, ws=FAKE + 16, grad=dt) == E_ALIGN
+    assert _bwd(fn, o=FAKE + 8, grad=dt) == E_ALIGN
+    assert _bwd(fn, dbias=FAKE + 2, grad=dt) == E_ALIGN

@@ -46,12 +46,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 701084675,
-              "sha256": "cadc96162b91b9e9717cc6e97df1298687ab1d2d10fd1b03687ce683c1011cae"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344987124,
-             "sha256": "11c7fd8611d74f2390558e11cb0ebc949ff54ca4ce362a37d8c0e92286eedbeb"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880724559,
-              "sha256": "11c7fd8611d74f2390558e11cb0ebc949ff54ca4ce362a37d8c0e92286eedbeb"},
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 704988683,
+              "sha256": "a394d17d13525a848762ea47ce3ea79edc382e8cf22656cc4f74fda5c29ae56d"},
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344952343,
+             "sha256": "c904286068ede1d569e6b2e55383086c9abfe1d1e7cf6f4e1a56c79e1044223b"},
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880727617,
+              "sha256": "c904286068ede1d569e6b2e55383086c9abfe1d1e7cf6f4e1a56c79e1044223b"},
 }
 
 
@@ -316,6 +316,7 @@ def main():
 
     if not args.no_extra:
         out["workloads"] = extra_workloads(attn, workloads, stream, dev)
+        out["backward"] = backward_workloads(attn, workloads, stream, dev)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)")
@@ -371,6 +372,38 @@ def extra_workloads(attn, workloads, stream, dev):
         del q2, k2, v2, b2, ws, prep
         torch.cuda.empty_cache()
     return extra
+
+
+def backward_workloads(attn, workloads, stream, dev):
+    """The backward (D, dQ, dK, dV, and the bias gradient where a bias is
+    given) on llm-prefill, long-context and DiT-gated: whole-call times of 10
+    launches after 0.1 s of warm-up.  FLOPs: the five products of the
+    algorithm (S, dP, dV, dQ, dK), 2.5 times the forward's; the kernels
+    compute S and dP twice (once per side), seven products in all."""
+    import torch
+    res = {}
+    for cid in (2, 3, 5):
+        c2 = workloads.CONFIGS[cid]
+        B, H, N, d = c2["B"], c2["H"], c2["N"], c2["d"]
+        log(f"backward {c2['name']}")
+        g = torch.Generator(device=dev).manual_seed(cid)
+        q, k, v, dout = (torch.randn((B, H, N, d), device=dev, dtype=torch.bfloat16, generator=g) for _ in range(4))
+        nb = (N + 63) // 64
+        b = torch.zeros((B, H, nb, nb), device=dev) if c2.get("gate_bias") else None
+        o, lse = attn.fwd(q, k, v, causal=c2["causal"], bias=b, return_lse=True)
+        fn = lambda: attn.bwd(q, k, v, o, dout, lse, causal=c2["causal"], bias=b,  # noqa: E731
+                              return_dbias=b is not None)
+        _warm(fn)
+        st = _stats(_time_launches(fn, 10, stream))
+        F = 2.5 * workloads.flops(B, H, N, d, c2["causal"])
+        tf = F / (st["ms_avg"] * 1e-3) / 1e12
+        res[f"{c2['name']}: B={B} H={H} N={N} d={d} {'causal' if c2['causal'] else 'non-causal'}"
+            f"{' +bias grad' if b is not None else ''}"] = {
+            **st, "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_counted": f"{F:.4e} (5 products, 2.5 x forward)"}
+        del q, k, v, dout, o, lse, b
+        torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

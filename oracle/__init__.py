@@ -69,15 +69,17 @@ def _load():
     lib.sage8_oracle_kmean.restype = _int
     lib.sage8_oracle_quant_int8.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]
     lib.sage8_oracle_quant_int8.restype = _int
+    lib.sage8_oracle_quant_fp8.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]
+    lib.sage8_oracle_quant_fp8.restype = _int
     lib.sage8_oracle_quant_v.argtypes = [_ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]
     lib.sage8_oracle_quant_v.restype = _int
     lib.sage8_oracle_emulate_rows.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                               _i64, _i64, _i64, _i64, _int, _dbl, _i64,
-                                              _int, _ptr, _i64, _ptr, _ptr, _int]
+                                              _int, _ptr, _i64, _ptr, _ptr, _int, _int]
     lib.sage8_oracle_emulate_rows.restype = _int
     lib.sage8_oracle_emulate_rows_fp32.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                                    _i64, _i64, _i64, _i64, _int, ctypes.c_float,
-                                                   _ptr, _i64, _ptr, _ptr, _int]
+                                                   _ptr, _i64, _ptr, _ptr, _int, _int]
     lib.sage8_oracle_emulate_rows_fp32.restype = _int
     _lib = lib
     return lib
@@ -216,6 +218,23 @@ def sage8_quant_int8(x, center=None):
     return codes, scales
 
 
+def sage8_quant_fp8(x, center=None):
+    """Per-64-row-block e4m3 (the FP8-QK variant): returns (codes uint8
+    [B,H,N,d], scales f32 [B,H,nb])."""
+    x = _f32(x)
+    B, H, N, d = x.shape
+    if center is not None:
+        center = _f32(center)
+        assert center.shape == (B, H, d)
+    nb = (N + 63) // 64
+    codes = np.zeros((B, H, N, d), dtype=np.uint8)
+    scales = np.zeros((B, H, nb), dtype=np.float32)
+    rc = _load().sage8_oracle_quant_fp8(_p(x), _p(center), B, H, N, d, _p(codes), _p(scales))
+    if rc != 0:
+        raise RuntimeError(f"sage8_oracle_quant_fp8 failed with code {rc}")
+    return codes, scales
+
+
 def sage8_quant_v(v):
     """Per-channel e4m3: returns (codes uint8 [B,H,N,d], scales f32 [B,H,d])."""
     v = _f32(v)
@@ -228,21 +247,24 @@ def sage8_quant_v(v):
     return codes, scales
 
 
-def sage8_prepare(q, k, v):
-    """All three preparation steps; returns a dict of the quantised data."""
+def sage8_prepare(q, k, v, qk="int8"):
+    """All three preparation steps; returns a dict of the quantised data.
+    qk = "fp8" quantises Q and smoothed K to e4m3 blocks instead of INT8."""
     kmean = sage8_kmean(k)
-    qq, sq = sage8_quant_int8(q)
-    kq, sk = sage8_quant_int8(k, kmean)
+    quant = sage8_quant_fp8 if qk == "fp8" else sage8_quant_int8
+    qq, sq = quant(q)
+    kq, sk = quant(k, kmean)
     vq, sv = sage8_quant_v(v)
-    return dict(kmean=kmean, qq=qq, sq=sq, kq=kq, sk=sk, vq=vq, sv=sv)
+    return dict(kmean=kmean, qq=qq, sq=sq, kq=kq, sk=sk, vq=vq, sv=sv, qk_fp8=qk == "fp8")
 
 
 def sage8_emulate_rows(prep, rows, causal=False, scale=None, bias=None, kv_block=64,
                        p_mode=1, nthreads=0):
     """Blocked 8-bit forward on rows from the quantised data of sage8_prepare.
     Returns (O [nrows,d], LSE [nrows]) in fp64."""
-    qq = np.ascontiguousarray(prep["qq"], dtype=np.int8)
-    kq = np.ascontiguousarray(prep["kq"], dtype=np.int8)
+    fp8 = bool(prep.get("qk_fp8", False))
+    qq = np.ascontiguousarray(prep["qq"], dtype=np.uint8 if fp8 else np.int8)
+    kq = np.ascontiguousarray(prep["kq"], dtype=np.uint8 if fp8 else np.int8)
     vq = np.ascontiguousarray(prep["vq"], dtype=np.uint8)
     sq, sk, sv = _f32(prep["sq"]), _f32(prep["sk"]), _f32(prep["sv"])
     B, H, N, d = qq.shape
@@ -257,7 +279,7 @@ def sage8_emulate_rows(prep, rows, causal=False, scale=None, bias=None, kv_block
     rc = _load().sage8_oracle_emulate_rows(_p(qq), _p(kq), _p(vq), _p(sq), _p(sk), _p(sv),
                                            _p(km), _p(bias), B, H, N, d, int(bool(causal)), float(scale),
                                            int(kv_block), int(p_mode), _p(r), r.shape[0],
-                                           _p(out), _p(lse), int(nthreads))
+                                           _p(out), _p(lse), int(fp8), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"sage8_oracle_emulate_rows failed with code {rc}")
     return out, lse
@@ -267,8 +289,9 @@ def sage8_emulate_rows_fp32(prep, rows, causal=False, scale=None, bias=None, nth
     """Blocked 8-bit forward with the kernel's fp32 decisions (64-key blocks,
     running maximum raised only past +2 in log2 units, P^ = e4m3(448*2^(t-m-2))).
     Returns (O [nrows,d], LSE [nrows]) in fp64."""
-    qq = np.ascontiguousarray(prep["qq"], dtype=np.int8)
-    kq = np.ascontiguousarray(prep["kq"], dtype=np.int8)
+    fp8 = bool(prep.get("qk_fp8", False))
+    qq = np.ascontiguousarray(prep["qq"], dtype=np.uint8 if fp8 else np.int8)
+    kq = np.ascontiguousarray(prep["kq"], dtype=np.uint8 if fp8 else np.int8)
     vq = np.ascontiguousarray(prep["vq"], dtype=np.uint8)
     sq, sk, sv = _f32(prep["sq"]), _f32(prep["sk"]), _f32(prep["sv"])
     B, H, N, d = qq.shape
@@ -283,7 +306,7 @@ def sage8_emulate_rows_fp32(prep, rows, causal=False, scale=None, bias=None, nth
     rc = _load().sage8_oracle_emulate_rows_fp32(_p(qq), _p(kq), _p(vq), _p(sq), _p(sk), _p(sv),
                                                 _p(km), _p(bias), B, H, N, d, int(bool(causal)),
                                                 float(np.float32(scale)), _p(r), r.shape[0],
-                                                _p(out), _p(lse), int(nthreads))
+                                                _p(out), _p(lse), int(fp8), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"sage8_oracle_emulate_rows_fp32 failed with code {rc}")
     return out, lse

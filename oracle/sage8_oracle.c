@@ -161,6 +161,54 @@ int sage8_oracle_quant_int8(const float* x, const float* center, int64_t B,
     return 0;
 }
 
+/* ---- step 2, FP8 variant: per-64-row-block e4m3 Q and smoothed K ------- */
+
+/* The FP8-QK variant (page 2, "FlashAttention-3" bulletin, claim vs reality
+ * section: FP8 for the products needs block-wise dynamic scaling): the same
+ * blocks as step 2, amax over the block (fp32), scale = amax / 448 and
+ * inv = 448 / amax (correctly rounded fp32 divisions; amax = 0 gives 1),
+ * code = e4m3(x * inv) with the product in fp32, round-half-to-even and
+ * saturation at 448.  center (nullable) is subtracted first, as for K in
+ * step 2.  codes [B,H,N,d] (e4m3 bytes), scales [B,H,ceil(N/64)]. */
+int sage8_oracle_quant_fp8(const float* x, const float* center, int64_t B,
+                           int64_t H, int64_t N, int64_t d, uint8_t* codes,
+                           float* scales)
+{
+    if (!x || !codes || !scales || B <= 0 || H <= 0 || N <= 0 || d <= 0)
+        return 1;
+    const int64_t nb = (N + SAGE_QK_BLOCK - 1) / SAGE_QK_BLOCK;
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t blk = 0; blk < nb; ++blk) {
+            const int64_t n0 = blk * SAGE_QK_BLOCK;
+            const int64_t n1 = (n0 + SAGE_QK_BLOCK < N) ? n0 + SAGE_QK_BLOCK : N;
+            float amax = 0.0f;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t c = 0; c < d; ++c) {
+                    float y = x[(bh * N + n) * d + c];
+                    if (center)
+                        y = y - center[bh * d + c];
+                    const float ay = fabsf(y);
+                    if (ay > amax)
+                        amax = ay;
+                }
+            float scale = 1.0f, inv = 1.0f;
+            if (amax > 0.0f) {
+                scale = amax / 448.0f;
+                inv = 448.0f / amax;
+            }
+            scales[bh * nb + blk] = scale;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t c = 0; c < d; ++c) {
+                    float y = x[(bh * N + n) * d + c];
+                    if (center)
+                        y = y - center[bh * d + c];
+                    const float t = y * inv;
+                    codes[(bh * N + n) * d + c] = sage8_e4m3_encode((double)t);
+                }
+        }
+    return 0;
+}
+
 /* ---- step 3: V to e4m3 with a per-channel scale ------------------------- */
 
 /* codes [B,H,N,d] (logical layout), scales [B,H,d]. */
@@ -191,6 +239,34 @@ int sage8_oracle_quant_v(const float* v, int64_t B, int64_t H, int64_t N,
     return 0;
 }
 
+/* Q.K of two quantised rows, exactly: INT8 codes (qk_fp8 = 0) as integers,
+ * or e4m3 codes (qk_fp8 = 1) decoded through dec[]; the e4m3 products and
+ * their sum over d <= 128 terms are exact in fp64. */
+static double qk_dot(const void* qq, const void* kq, int64_t qoff, int64_t koff,
+                     int64_t d, int qk_fp8, const double* dec)
+{
+    if (qk_fp8) {
+        const uint8_t* a = (const uint8_t*)qq + qoff;
+        const uint8_t* b = (const uint8_t*)kq + koff;
+        double acc = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            acc += dec[a[c]] * dec[b[c]];
+        return acc;
+    }
+    const int8_t* a = (const int8_t*)qq + qoff;
+    const int8_t* b = (const int8_t*)kq + koff;
+    int64_t acc = 0;
+    for (int64_t c = 0; c < d; ++c)
+        acc += (int64_t)a[c] * (int64_t)b[c];
+    return (double)acc;
+}
+
+/* The value of quantised Q element idx (before its block scale). */
+static double q_value(const void* qq, int64_t idx, int qk_fp8, const double* dec)
+{
+    return qk_fp8 ? dec[((const uint8_t*)qq)[idx]] : (double)((const int8_t*)qq)[idx];
+}
+
 /* ---- steps 4-5: the blocked 8-bit attention, modelled in fp64 ----------- */
 
 /*
@@ -200,14 +276,14 @@ int sage8_oracle_quant_v(const float* v, int64_t B, int64_t H, int64_t N,
  * (used to pin the blocked algebra against the plain oracle).  out [nrows,d]
  * and lse [nrows] (nullable) are fp64; LSE is in natural-log units.
  */
-int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
+int sage8_oracle_emulate_rows(const void* qq, const void* kq,
                               const uint8_t* vq, const float* sq,
                               const float* sk, const float* sv,
                               const float* kmean, const float* bias, int64_t B, int64_t H,
                               int64_t N, int64_t d, int causal, double scale,
                               int64_t kv_block, int p_mode,
                               const int64_t* rows, int64_t nrows, double* out,
-                              double* lse, int nthreads)
+                              double* lse, int qk_fp8, int nthreads)
 {
     if (!qq || !kq || !vq || !sq || !sk || !sv || !rows || !out || B <= 0 ||
         H <= 0 || N <= 0 || d <= 0 || kv_block <= 0 || nrows < 0)
@@ -243,7 +319,7 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                 continue;
             const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
             const int64_t bh = b * H + h;
-            const int8_t* qi = qq + (bh * N + i) * d;
+            const int64_t qoff = (bh * N + i) * d;
             const double sqi = (double)sq[bh * nqk + i / SAGE_QK_BLOCK];
             double* o = out + r * d;
             for (int64_t c = 0; c < d; ++c)
@@ -254,11 +330,8 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                 const int64_t j1 = (j0 + kv_block < jend) ? j0 + kv_block : jend;
                 double mb = -INFINITY;
                 for (int64_t j = j0; j < j1; ++j) {
-                    const int8_t* kj = kq + (bh * N + j) * d;
-                    int64_t acc = 0;
-                    for (int64_t c = 0; c < d; ++c)
-                        acc += (int64_t)qi[c] * (int64_t)kj[c];
-                    double sj = (double)acc * sqi *
+                    const double acc = qk_dot(qq, kq, qoff, (bh * N + j) * d, d, qk_fp8, vdec);
+                    double sj = acc * sqi *
                                 (double)sk[bh * nqk + j / SAGE_QK_BLOCK] * scale;
                     if (bias)
                         sj += (double)bias[(bh * nbb + i / SAGE_BIAS_BLOCK) * nbb +
@@ -298,7 +371,7 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
                 double shift = 0.0;
                 if (kmean)
                     for (int64_t c = 0; c < d; ++c)
-                        shift += (double)qi[c] * (double)kmean[bh * d + c];
+                        shift += q_value(qq, qoff + c, qk_fp8, vdec) * (double)kmean[bh * d + c];
                 lse[r] = (l > 0.0) ? m + log(l) + scale * sqi * shift : -INFINITY;
             }
         }
@@ -328,14 +401,14 @@ int sage8_oracle_emulate_rows(const int8_t* qq, const int8_t* kq,
  * hardware exp2 is within about one fp32 ulp of that); sums are in fp64.
  * kv_block is 64, as in the kernel.
  */
-int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
+int sage8_oracle_emulate_rows_fp32(const void* qq, const void* kq,
                                    const uint8_t* vq, const float* sq,
                                    const float* sk, const float* sv,
                                    const float* kmean, const float* bias, int64_t B, int64_t H,
                                    int64_t N, int64_t d, int causal,
                                    float scale, const int64_t* rows,
                                    int64_t nrows, double* out, double* lse,
-                                   int nthreads)
+                                   int qk_fp8, int nthreads)
 {
     if (!qq || !kq || !vq || !sq || !sk || !sv || !rows || !out || B <= 0 ||
         H <= 0 || N <= 0 || d <= 0 || nrows < 0)
@@ -351,7 +424,8 @@ int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
     const float log2e_f = 1.4426950408889634f;
     const float tau = 2.0f;
     const float plog = (float)6.807354922057604; /* log2(448) - 2 */
-    const float magic = 12582912.0f;               /* 1.5 * 2^23 */
+    /* INT8 scores leave the matrix unit offset by 1.5 * 2^23; FP8 scores do not */
+    const float magic = qk_fp8 ? 0.0f : 12582912.0f;
     float c = (float)((double)scale * 1.4426950408889634);
     if (c == 0.0f)
         c = 1.17549435e-38f;
@@ -379,7 +453,7 @@ int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
                 continue;
             const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
             const int64_t bh = b * H + h;
-            const int8_t* qi = qq + (bh * N + i) * d;
+            const int64_t qoff = (bh * N + i) * d;
             const float sqi = sq[bh * nqk + i / SAGE_QK_BLOCK];
             double* o = out + r * d;
             for (int64_t cc = 0; cc < d; ++cc)
@@ -395,11 +469,8 @@ int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
                                       : 0.0f;
                 float ext = (f > 0.0f) ? -INFINITY : INFINITY;
                 for (int64_t j = j0; j < j1; ++j) {
-                    const int8_t* kj = kq + (bh * N + j) * d;
-                    int64_t acc = 0;
-                    for (int64_t cc = 0; cc < d; ++cc)
-                        acc += (int64_t)qi[cc] * (int64_t)kj[cc];
-                    s[j - j0] = (float)acc; /* exact: |acc| < 2^24 */
+                    /* exact for INT8 (|acc| < 2^24); one fp32 rounding for FP8 */
+                    s[j - j0] = (float)qk_dot(qq, kq, qoff, (bh * N + j) * d, d, qk_fp8, vdec);
                     if (f > 0.0f ? s[j - j0] > ext : s[j - j0] < ext)
                         ext = s[j - j0];
                 }
@@ -435,7 +506,7 @@ int sage8_oracle_emulate_rows_fp32(const int8_t* qq, const int8_t* kq,
                 double shift = 0.0;
                 if (kmean)
                     for (int64_t cc = 0; cc < d; ++cc)
-                        shift += (double)qi[cc] * (double)kmean[bh * d + cc];
+                        shift += q_value(qq, qoff + cc, qk_fp8, vdec) * (double)kmean[bh * d + cc];
                 lse[r] = (l > 0.0) ? ((double)m + log2(l) - (double)plog) * 0.6931471805599453 +
                                          (double)scale * (double)sqi * shift
                                    : -INFINITY;

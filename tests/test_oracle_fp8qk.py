@@ -1,0 +1,121 @@
+"""Pins of the FP8-QK variant of the 8-bit oracle (CPU only).
+
+The variant (page 2, "FlashAttention-3" bulletin, claim vs reality section:
+FP8 products need block-wise dynamic scaling) quantises Q and mean-centred K
+to e4m3 with one scale per 64-row block (scale = amax / 448) instead of INT8;
+everything after the scores is the 8-bit recipe unchanged.  Pinned here:
+exact round trips of values on the e4m3 grid, the half-step error bound of
+a 3-bit mantissa, the block maximum mapping to +-448, zero blocks, and the
+blocked emulator with e4m3 scores against the plain fp64 oracle on inputs
+the quantisation represents exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+E4M3_FINITE = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def test_fp8_grid_values_round_trip():
+    """Values that are e4m3 codes times a power of two, with each block's
+    largest magnitude exactly 448 times that power, come back code for code."""
+    rng = np.random.default_rng(1)
+    B, H, N, d = 1, 2, 130, 16
+    codes = rng.choice(E4M3_FINITE, size=(B, H, N, d))
+    nb = (N + 63) // 64
+    steps = 2.0 ** rng.integers(-12, -3, (B, H, nb))
+    for b in range(B):
+        for h in range(H):
+            for blk in range(nb):
+                codes[b, h, blk * 64, 0] = 0x7E  # +448
+    x = (oracle.e4m3_decode(codes) * np.repeat(steps, 64, axis=2)[:, :, :N, None]).astype(np.float32)
+    got, scales = oracle.sage8_quant_fp8(x)
+    # +0 and -0 are both zero: compare values, and codes away from zero
+    np.testing.assert_array_equal(oracle.e4m3_decode(got), oracle.e4m3_decode(codes))
+    nz = oracle.e4m3_decode(codes) != 0
+    np.testing.assert_array_equal(got[nz], codes[nz])
+    np.testing.assert_array_equal(scales, steps.astype(np.float32))
+
+
+def test_fp8_error_bound_and_extremes():
+    """|dequantised - x| is at most half an e4m3 step at |x| / scale: 2^-4
+    relative in the normal range (|t| >= 2^-6), 2^-10 absolute below it;
+    each block's largest |x| maps to +-448 exactly."""
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 2, 200, 32)).astype(np.float32) * 3
+    center = rng.standard_normal((2, 2, 32)).astype(np.float32)
+    codes, scales = oracle.sage8_quant_fp8(x, center)
+    y = (x - center[:, :, None, :]).astype(np.float64)
+    s = np.repeat(scales, 64, axis=2)[:, :, :200, None].astype(np.float64)
+    t = np.abs(y) / s
+    ulp = np.where(t >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 3), 2.0 ** -9)
+    err = np.abs(oracle.e4m3_decode(codes) * s - y)
+    assert (err <= 0.5 * ulp * s * (1 + 1e-6)).all()
+    for b in range(2):
+        for h in range(2):
+            for blk in range(4):
+                sl = slice(blk * 64, min(blk * 64 + 64, 200))
+                assert np.abs(oracle.e4m3_decode(codes[b, h, sl])).max() == 448.0
+                amax = np.abs(y[b, h, sl]).max()
+                assert scales[b, h, blk] == np.float32(amax) / np.float32(448)
+
+
+def test_fp8_zero_block():
+    x = np.zeros((1, 1, 70, 8), np.float32)
+    x[0, 0, 64:] = 1.0
+    codes, scales = oracle.sage8_quant_fp8(x)
+    assert scales[0, 0, 0] == 1.0 and (oracle.e4m3_decode(codes[0, 0, :64]) == 0).all()
+    assert (codes[0, 0, 64:] == 0x7E).all()
+
+
+def _lossless_fp8_prep(B, H, N, d, seed):
+    """e4m3 Q/K codes with power-of-two block scales and e4m3 V with
+    power-of-two channel scales: the dequantised values are exact fp32."""
+    rng = np.random.default_rng(seed)
+    nqk = (N + 63) // 64
+    qq = rng.choice(E4M3_FINITE, size=(B, H, N, d))
+    kq = rng.choice(E4M3_FINITE, size=(B, H, N, d))
+    sq = (2.0 ** rng.integers(-11, -8, (B, H, nqk))).astype(np.float32)
+    sk = (2.0 ** rng.integers(-11, -8, (B, H, nqk))).astype(np.float32)
+    vq = rng.choice(E4M3_FINITE, size=(B, H, N, d))
+    sv = (2.0 ** rng.integers(-9, -7, (B, H, d))).astype(np.float32)
+    q = oracle.e4m3_decode(qq) * np.repeat(sq, 64, axis=2)[:, :, :N, None]
+    k = oracle.e4m3_decode(kq) * np.repeat(sk, 64, axis=2)[:, :, :N, None]
+    v = oracle.e4m3_decode(vq) * sv[:, :, None, :]
+    prep = dict(qq=qq, kq=kq, vq=vq, sq=sq, sk=sk, sv=sv, qk_fp8=True)
+    return prep, q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kv_block", [1, 64])
+def test_fp8_emulator_without_p_rounding_equals_oracle(causal, kv_block):
+    """With exact e4m3 inputs and P kept exact, the blocked emulator with
+    e4m3 scores is the plain attention to 1e-12 (a swapped operand, a missing
+    scale or INT8 decoding of the codes fails this)."""
+    prep, q, k, v = _lossless_fp8_prep(1, 2, 150, 16, seed=5)
+    bias = np.random.default_rng(6).normal(0, 1, (1, 2, 3, 3)).astype(np.float32)
+    rows = workloads.parity_rows(1, 2, 150, seed=2, n_random=20)
+    o_ref, l_ref = oracle.attn_rows(q, k, v, rows, causal=causal, scale=0.7, bias=bias)
+    o_emu, l_emu = oracle.sage8_emulate_rows(prep, rows, causal=causal, scale=0.7, bias=bias,
+                                             kv_block=kv_block, p_mode=0)
+    np.testing.assert_allclose(o_emu, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_emu, l_ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_fp32_emulator_tracks_fp64_model():
+    """The kernel-decision model with e4m3 scores (no INT8 offset) stays in
+    the accuracy class of the fp64 model of the recipe."""
+    inp = workloads.make_inputs(1, 2, 300, 128, "bf16", seed=9)
+    q, k, v = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    prep = oracle.sage8_prepare(q, k, v, qk="fp8")
+    assert prep["qq"].dtype == np.uint8 and prep["qk_fp8"]
+    rows = workloads.parity_rows(1, 2, 300, seed=3, n_random=30)
+    o_ref, _ = oracle.attn_rows(q, k, v, rows, causal=True)
+    o64, _ = oracle.sage8_emulate_rows(prep, rows, causal=True)
+    o32, _ = oracle.sage8_emulate_rows_fp32(prep, rows, causal=True)
+    rel64 = np.abs(o64 - o_ref).sum() / np.abs(o_ref).sum()
+    rel32 = np.abs(o32 - o_ref).sum() / np.abs(o_ref).sum()
+    assert abs(rel32 - rel64) < 0.3 * rel64, (rel32, rel64)
+    assert rel64 < 0.08

@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.attn_sage8_workspace_layout.restype = i
     L.attn_fwd_sage8.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
     L.attn_fwd_sage8.restype = i
+    L.attn_k_smooth_quant_fp8qk.argtypes = L.attn_k_smooth_quant.argtypes
+    L.attn_k_smooth_quant_fp8qk.restype = i
+    L.attn_fwd_sage8_fp8qk.argtypes = L.attn_fwd_sage8.argtypes
+    L.attn_fwd_sage8_fp8qk.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_abi_version.argtypes = []
@@ -271,14 +275,19 @@ class Sage8Prepared:
     """Workspace written by the 8-bit preparation, with the shape it was
     prepared for (the forward must use the same shape)."""
 
-    def __init__(self, workspace, shape, in_dtype):
+    def __init__(self, workspace, shape, in_dtype, qk="int8"):
         self.workspace = workspace
         self.shape = tuple(shape)
         self.in_dtype = in_dtype
+        self.qk = qk  # "int8", or "fp8" for the FP8-QK variant
 
 
-def sage8_prep(q, k, v, workspace=None):
-    """K smoothing and 8-bit quantisation of Q, K, V into a device workspace."""
+def sage8_prep(q, k, v, workspace=None, qk="int8"):
+    """K smoothing and 8-bit quantisation of Q, K, V into a device workspace.
+    qk="fp8" quantises Q and K to e4m3 blocks (the FP8-QK variant, d = 64 or
+    128) instead of INT8; fwd_sage8 then uses FP8 scores."""
+    if qk not in ("int8", "fp8"):
+        raise ValueError('qk must be "int8" or "fp8"')
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     L = lib()
@@ -287,12 +296,13 @@ def sage8_prep(q, k, v, workspace=None):
         raise AttnError(2, "attn_sage8_workspace_size")
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    fn = L.attn_k_smooth_quant_fp8qk if qk == "fp8" else L.attn_k_smooth_quant
     with torch.cuda.device(q.device):
-        st = L.attn_k_smooth_quant(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d,
-                                   _ptr(workspace), workspace.numel(), _stream(q.device))
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d,
+                _ptr(workspace), workspace.numel(), _stream(q.device))
     if st != 0:
-        raise AttnError(st, "attn_k_smooth_quant")
-    return Sage8Prepared(workspace, (B, H, N, d), q.dtype)
+        raise AttnError(st, fn.__name__)
+    return Sage8Prepared(workspace, (B, H, N, d), q.dtype, qk)
 
 
 def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtype=None,
@@ -306,18 +316,18 @@ def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtyp
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    fn = lib().attn_fwd_sage8_fp8qk if prep.qk == "fp8" else lib().attn_fwd_sage8
     with torch.cuda.device(dev):
-        st = lib().attn_fwd_sage8(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d,
-                                  int(bool(causal)), float(scale), _ptr(bias),
-                                  _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
+        st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
+                _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
     if st != 0:
-        raise AttnError(st, "attn_fwd_sage8")
+        raise AttnError(st, fn.__name__)
     return (o, lse) if return_lse else o
 
 
-def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False):
+def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False, qk="int8"):
     """8-bit attention in one call (preparation, then the forward)."""
-    prep = sage8_prep(q, k, v)
+    prep = sage8_prep(q, k, v, qk=qk)
     return fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
                      return_lse=return_lse)
 

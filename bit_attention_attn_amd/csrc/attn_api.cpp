@@ -139,6 +139,44 @@ attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const 
   return ATTN_OK;
 }
 
+attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int B, int H, int N, int d,
+                  void* workspace, size_t workspace_bytes, void* stream, bool qk_fp8) {
+  if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
+  attn_status s = check_shape(B, H, N, d);
+  if (s != ATTN_OK) return s;
+  if (qk_fp8 && d == 96) return ATTN_ERR_HEADDIM;
+  if (in_dtype != ATTN_DTYPE_F16 && in_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+  if (workspace_bytes < attn::sage8_layout(B, H, N, d).total) return ATTN_ERR_WORKSPACE;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  if (attn::launch_sage8_prep(q, k, v, in_dtype == ATTN_DTYPE_BF16, B, H, N, d, workspace,
+                              static_cast<hipStream_t>(stream), qk_fp8) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N, int d, int causal, float scale,
+                 const float* bias, int out_dtype, void* stream, bool qk_fp8) {
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
+  if (s != ATTN_OK) return s;
+  if (qk_fp8 && d == 96) return ATTN_ERR_HEADDIM;
+  if (out_dtype != ATTN_DTYPE_F16 && out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32)
+    return ATTN_ERR_DTYPE;
+  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  attn::FwdArgs a{nullptr, nullptr, nullptr, o, lse, bias, B, H, N, d, causal, scale,
+                  out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32
+                                              : (out_dtype == ATTN_DTYPE_BF16 ? attn::kOutBF16 : attn::kOutF16)};
+  if (attn::launch_fwd_sage8(workspace, a, static_cast<hipStream_t>(stream), qk_fp8) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,38 +221,22 @@ int attn_sage8_workspace_layout(int B, int H, int N, int d, size_t* out, int n) 
 
 attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
                                 int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
-  attn_status s = check_shape(B, H, N, d);
-  if (s != ATTN_OK) return s;
-  if (in_dtype != ATTN_DTYPE_F16 && in_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
-  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
-  if (workspace_bytes < attn::sage8_layout(B, H, N, d).total) return ATTN_ERR_WORKSPACE;
-  s = check_device();
-  if (s != ATTN_OK) return s;
-  if (attn::launch_sage8_prep(q, k, v, in_dtype == ATTN_DTYPE_BF16, B, H, N, d, workspace,
-                              static_cast<hipStream_t>(stream)) != hipSuccess)
-    return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return prep8(q, k, v, in_dtype, B, H, N, d, workspace, workspace_bytes, stream, false);
+}
+
+attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
+                                      int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
+  return prep8(q, k, v, in_dtype, B, H, N, d, workspace, workspace_bytes, stream, true);
 }
 
 attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
                            int causal, float scale, const float* bias, int out_dtype, void* stream) {
-  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
-  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
-  if (s != ATTN_OK) return s;
-  if (out_dtype != ATTN_DTYPE_F16 && out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32)
-    return ATTN_ERR_DTYPE;
-  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
-  s = check_device();
-  if (s != ATTN_OK) return s;
-  attn::FwdArgs a{nullptr, nullptr, nullptr, o, lse, bias, B, H, N, d, causal, scale,
-                  out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32
-                                              : (out_dtype == ATTN_DTYPE_BF16 ? attn::kOutBF16 : attn::kOutF16)};
-  if (attn::launch_fwd_sage8(workspace, a, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, stream, false);
+}
+
+attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
+                                 int causal, float scale, const float* bias, int out_dtype, void* stream) {
+  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, stream, true);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int N, int d) {

@@ -72,8 +72,10 @@ struct Sage8Layout {
   int nchunk;  // token chunks of the column reductions
 };
 Sage8Layout sage8_layout(int B, int H, int N, int d);
+// qk_fp8: Q and K in e4m3 blocks (the FP8-QK variant; d = 64 or 128) instead
+// of INT8; the forward must be told the format the preparation wrote.
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H,
-                             int N, int d, void* ws, hipStream_t stream);
-hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream);
+                             int N, int d, void* ws, hipStream_t stream, bool qk_fp8);
+hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream, bool qk_fp8);
 
 }  // namespace attn

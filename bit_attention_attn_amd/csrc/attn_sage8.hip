@@ -205,8 +205,15 @@ __device__ __forceinline__ uint32_t q8(float y, float inv) {
   return (uint32_t)((int)r & 0xFF);
 }
 
+// e4m3 code (round to nearest even) of y * inv, |y * inv| <= 448
+__device__ __forceinline__ uint32_t f8(float y, float inv) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y * inv, 0.f, 0, false) & 0xFF;
+}
+
 // ---- quant: grid (nblk, B*H), prep_threads<D>() threads --------------------------------
-template <int D, bool BF16>
+// QKFP8: Q and smoothed K go to e4m3 with scale amax / 448 per block (the
+// FP8-QK variant) instead of INT8 with amax / 127.
+template <int D, bool BF16, bool QKFP8>
 __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, int N, int np, int nblk,
                                                    const float* __restrict__ kmean, const float* __restrict__ vinv,
@@ -259,20 +266,26 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   }
   aq = block_max<kThreads / 64>(aq, red);
   ak = block_max<kThreads / 64>(ak, red);
-  const float inv_q = aq > 0.f ? __fdiv_rn(127.0f, aq) : 1.0f;
-  const float inv_k = ak > 0.f ? __fdiv_rn(127.0f, ak) : 1.0f;
+  constexpr float kQmax = QKFP8 ? 448.0f : 127.0f;
+  const float inv_q = aq > 0.f ? __fdiv_rn(kQmax, aq) : 1.0f;
+  const float inv_k = ak > 0.f ? __fdiv_rn(kQmax, ak) : 1.0f;
   if (tid == 0) {
-    sq[(size_t)bh * nblk + blk] = aq > 0.f ? __fdiv_rn(aq, 127.0f) : 1.0f;
-    sk[(size_t)bh * nblk + blk] = ak > 0.f ? __fdiv_rn(ak, 127.0f) : 1.0f;
+    sq[(size_t)bh * nblk + blk] = aq > 0.f ? __fdiv_rn(aq, kQmax) : 1.0f;
+    sk[(size_t)bh * nblk + blk] = ak > 0.f ? __fdiv_rn(ak, kQmax) : 1.0f;
   }
+  auto code = [&](float y, float inv) { return QKFP8 ? f8(y, inv) : q8(y, inv); };
 #pragma unroll
   for (int i = 0; i < kPass; ++i) {
     const int r = rg + i * kRows, n = n0 + r;
     u32x2_t wq, wk;
-    wq[0] = q8(xq[i][0], inv_q) | q8(xq[i][1], inv_q) << 8 | q8(xq[i][2], inv_q) << 16 | q8(xq[i][3], inv_q) << 24;
-    wq[1] = q8(xq[i][4], inv_q) | q8(xq[i][5], inv_q) << 8 | q8(xq[i][6], inv_q) << 16 | q8(xq[i][7], inv_q) << 24;
-    wk[0] = q8(xk[i][0], inv_k) | q8(xk[i][1], inv_k) << 8 | q8(xk[i][2], inv_k) << 16 | q8(xk[i][3], inv_k) << 24;
-    wk[1] = q8(xk[i][4], inv_k) | q8(xk[i][5], inv_k) << 8 | q8(xk[i][6], inv_k) << 16 | q8(xk[i][7], inv_k) << 24;
+    wq[0] = code(xq[i][0], inv_q) | code(xq[i][1], inv_q) << 8 | code(xq[i][2], inv_q) << 16 |
+            code(xq[i][3], inv_q) << 24;
+    wq[1] = code(xq[i][4], inv_q) | code(xq[i][5], inv_q) << 8 | code(xq[i][6], inv_q) << 16 |
+            code(xq[i][7], inv_q) << 24;
+    wk[0] = code(xk[i][0], inv_k) | code(xk[i][1], inv_k) << 8 | code(xk[i][2], inv_k) << 16 |
+            code(xk[i][3], inv_k) << 24;
+    wk[1] = code(xk[i][4], inv_k) | code(xk[i][5], inv_k) << 8 | code(xk[i][6], inv_k) << 16 |
+            code(xk[i][7], inv_k) << 24;
     *(u32x2_t*)(qq + headp + (size_t)n * D + ch * 8) = wq;
     *(u32x2_t*)(kq + headp + (size_t)n * D + ch * 8) = wk;
   }
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool QKFP8>
 hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, int N, void* ws,
                      hipStream_t stream) {
   const Sage8Layout L = sage8_layout(B, H, N, D);
@@ -299,7 +312,7 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
                      reinterpret_cast<float*>(w + L.vinv));
-  hipLaunchKernelGGL((sage8_quant<D, BF16>), dim3(L.nblk, bh), dim3(prep_threads<D>()), 0, stream,
+  hipLaunchKernelGGL((sage8_quant<D, BF16, QKFP8>), dim3(L.nblk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), N, np, L.nblk,
                      reinterpret_cast<const float*>(w + L.kmean), reinterpret_cast<const float*>(w + L.vinv),
@@ -362,14 +375,18 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // the K block scales come as their own restrict arguments: their reads,
 // uniform and never written by the kernel, then compile to scalar loads,
 // which do not share the in-order vector-load counter with the K/V prefetch.
-template <int D, bool CAUSAL, bool BIAS>
+// QKFP8: Qq and Kq hold e4m3 codes (the FP8-QK variant) and S^T = Kq Qq^T
+// runs on the FP8 32x32x64 instruction, with no offset on the accumulators.
+template <int D, bool CAUSAL, bool BIAS, bool QKFP8>
 __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const float* __restrict__ bias,
                                                             const float* __restrict__ sk) {
   using S = Fwd8Smem<D>;
   constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
   constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
   constexpr int kDT = D / 32;  // 32-row tiles of O^T
-  constexpr int kKS = D / 32;  // k-steps of the INT8 product (32 per step)
+  constexpr int kKS = D / 32;  // 16-byte Q chunks per lane (INT8: one per 32-deep k-step;
+                               // FP8: two per 64-deep k-step)
+  static_assert(!QKFP8 || D % 64 == 0, "FP8 scores need d a multiple of 64");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::kBytes];
   uint8_t* const kl = smem;               // 2 K tiles
   uint8_t* const vl = smem + 2 * kKTile;  // 2 V tiles
@@ -396,10 +413,14 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   const uint8_t* __restrict__ Vq = p.vq + headp;
 
   // Qq^T as the B operand: lane holds Qq[qw0 + l32][32kk + 16hf .. +15]
-  // (rows up to the padded length are valid zero codes).
+  // (INT8), or bytes 64(kk/2) + 32hf + 16(kk%2) .. +15 (FP8, 32 bytes per
+  // 64-deep step); rows up to the padded length are valid zero codes.
   u32x4_t qf[kKS];
 #pragma unroll
-  for (int kk = 0; kk < kKS; ++kk) qf[kk] = *(const u32x4_t*)(Qq + (size_t)(qw0 + l32) * D + 32 * kk + 16 * hf);
+  for (int kk = 0; kk < kKS; ++kk) {
+    const int col = QKFP8 ? 64 * (kk >> 1) + 32 * hf + 16 * (kk & 1) : 32 * kk + 16 * hf;
+    qf[kk] = *(const u32x4_t*)(Qq + (size_t)(qw0 + l32) * D + col);
+  }
   const float sqw = p.sq[(size_t)bh * p.nblk + qw0 / kQB];
 
   const int kend = CAUSAL ? min(N, q0 + kBM8) : N;
@@ -459,27 +480,47 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
     const bool more = jn < nkb;
     if (more) load_kv(jn);
     if (wave_has_rows && jc <= wave_last && (!BIAS || braw != -INFINITY)) {
-      // ---- S^T = Kq Qq^T on top of the offset, exact
-      const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
-      i32x16_t si[2];
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) si[T][r] = kMagicBits;
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk)
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          const u32x4_t a = *(const u32x4_t*)(Ks + 32 * T * kKRow + 32 * kk);
-          si[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
-                                                        __builtin_bit_cast(i32x4_t, qf[kk]), si[T], 0, 0, 0);
-        }
-      // s = kMagic + S_int; base 2: t = S_int * f + bias*log2(e)
-      //                               = s * f + g,  g = bias*log2(e) - kMagic * f
-      const float f = (sqw * skrow[jc]) * c;
       f32x16_t s[2];
+      if constexpr (QKFP8) {
+        // ---- S^T = Kq Qq^T in fp32 from e4m3 codes (A: 32 bytes of a K
+        // row per 64-deep step, B: the matching 32 bytes of the Q row)
+        const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 32 * hf;
+        s[0] = s[1] = f32x16_t{};
 #pragma unroll
-      for (int T = 0; T < 2; ++T) s[T] = __builtin_bit_cast(f32x16_t, si[T]);
+        for (int kk = 0; kk < kKS / 2; ++kk)
+#pragma unroll
+          for (int T = 0; T < 2; ++T) {
+            const u32x4_t a0 = *(const u32x4_t*)(Ks + 32 * T * kKRow + 64 * kk);
+            const u32x4_t a1 = *(const u32x4_t*)(Ks + 32 * T * kKRow + 64 * kk + 16);
+            const u32x4_t b0 = qf[2 * kk], b1 = qf[2 * kk + 1];
+            const i32x8_t aop = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            const i32x8_t bop = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                 (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+            s[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, s[T], 0, 0, 0, 0, 0, 0);
+          }
+      } else {
+        // ---- S^T = Kq Qq^T on top of the offset, exact
+        const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
+        i32x16_t si[2];
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) si[T][r] = kMagicBits;
+#pragma unroll
+        for (int kk = 0; kk < kKS; ++kk)
+#pragma unroll
+          for (int T = 0; T < 2; ++T) {
+            const u32x4_t a = *(const u32x4_t*)(Ks + 32 * T * kKRow + 32 * kk);
+            si[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
+                                                          __builtin_bit_cast(i32x4_t, qf[kk]), si[T], 0, 0, 0);
+          }
+#pragma unroll
+        for (int T = 0; T < 2; ++T) s[T] = __builtin_bit_cast(f32x16_t, si[T]);
+      }
+      // INT8: s = kMagic + S_int; base 2: t = S_int * f + bias*log2(e)
+      //       = s * f + g,  g = bias*log2(e) - kMagic * f.  FP8: s = S, g = bias*log2(e).
+      const float f = (sqw * skrow[jc]) * c;
       if ((CAUSAL && jc == wave_last) || (jc + 1) * kQB > N) {
         const int kb0 = jc * kQB, qi = qw0 + l32;
 #pragma unroll
@@ -492,7 +533,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
           }
       }
       const float bl = BIAS ? braw * kLog2e : 0.f;
-      const float g = fmaf(-kMagic, f, bl);
+      const float g = QKFP8 ? bl : fmaf(-kMagic, f, bl);
       float a0;
       if (pos) {
         a0 = fmaxf(s[0][0], s[1][0]);
@@ -592,8 +633,9 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
       const u32x4_t qc = *(const u32x4_t*)(Qq + (size_t)(qw0 + l32) * D + 32 * kk + 16 * hf);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int code = (int)(int8_t)(qc[e >> 2] >> (8 * (e & 3)));
-        dot = fmaf((float)code, kmh[32 * kk + 16 * hf + e], dot);
+        const float qv = QKFP8 ? __builtin_amdgcn_cvt_f32_fp8((int)(qc[e >> 2] >> (8 * (e & 3))), 0)
+                               : (float)(int)(int8_t)(qc[e >> 2] >> (8 * (e & 3)));
+        dot = fmaf(qv, kmh[32 * kk + 16 * hf + e], dot);
       }
     }
     dot = xor32_sum(dot);
@@ -625,7 +667,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   }  // work items
 }
 
-template <int D, bool CAUSAL, bool BIAS>
+template <int D, bool CAUSAL, bool BIAS, bool QKFP8>
 hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   const Sage8Layout L = sage8_layout(a.B, a.H, a.N, D);
   const char* w = static_cast<const char*>(ws);
@@ -650,39 +692,50 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   p.out_kind = a.out_kind;
   // persistent grid for causal shapes (tiles differ in cost), one workgroup
   // per tile otherwise
-  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS>), kThreads8,
+  const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), kThreads8,
                                             p.nbh, p.nq)
                           : p.ntiles;
   if (grid <= 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, BIAS>), dim3(grid), dim3(kThreads8), 0, stream, p, a.bias,
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), dim3(grid), dim3(kThreads8), 0, stream, p, a.bias,
                      reinterpret_cast<const float*>(w + L.sk));
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
-                             void* ws, hipStream_t stream) {
-  if (d == 64) return bf16 ? prep_impl<64, true>(q, k, v, B, H, N, ws, stream)
-                           : prep_impl<64, false>(q, k, v, B, H, N, ws, stream);
-  if (d == 96) return bf16 ? prep_impl<96, true>(q, k, v, B, H, N, ws, stream)
-                           : prep_impl<96, false>(q, k, v, B, H, N, ws, stream);
-  return bf16 ? prep_impl<128, true>(q, k, v, B, H, N, ws, stream)
-              : prep_impl<128, false>(q, k, v, B, H, N, ws, stream);
-}
-
 namespace {
-template <int D>
-hipError_t fwd8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
-  if (a.bias) return a.causal ? fwd8_impl<D, true, true>(ws, a, stream) : fwd8_impl<D, false, true>(ws, a, stream);
-  return a.causal ? fwd8_impl<D, true, false>(ws, a, stream) : fwd8_impl<D, false, false>(ws, a, stream);
+template <bool QKFP8>
+hipError_t prep_q(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d, void* ws,
+                  hipStream_t stream) {
+  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8>(q, k, v, B, H, N, ws, stream)
+                           : prep_impl<64, false, QKFP8>(q, k, v, B, H, N, ws, stream);
+  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8>(q, k, v, B, H, N, ws, stream)
+                           : prep_impl<96, false, QKFP8>(q, k, v, B, H, N, ws, stream);
+  return bf16 ? prep_impl<128, true, QKFP8>(q, k, v, B, H, N, ws, stream)
+              : prep_impl<128, false, QKFP8>(q, k, v, B, H, N, ws, stream);
 }
 }  // namespace
 
-hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return fwd8_d<64>(ws, a, stream);
-  if (a.d == 96) return fwd8_d<96>(ws, a, stream);
-  return fwd8_d<128>(ws, a, stream);
+hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
+                             void* ws, hipStream_t stream, bool qk_fp8) {
+  return qk_fp8 ? prep_q<true>(q, k, v, bf16, B, H, N, d, ws, stream)
+                : prep_q<false>(q, k, v, bf16, B, H, N, d, ws, stream);
+}
+
+namespace {
+template <int D, bool QKFP8>
+hipError_t fwd8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  if (a.bias) return a.causal ? fwd8_impl<D, true, true, QKFP8>(ws, a, stream)
+                              : fwd8_impl<D, false, true, QKFP8>(ws, a, stream);
+  return a.causal ? fwd8_impl<D, true, false, QKFP8>(ws, a, stream) : fwd8_impl<D, false, false, QKFP8>(ws, a, stream);
+}
+}  // namespace
+
+hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream, bool qk_fp8) {
+  if (qk_fp8) return a.d == 64 ? fwd8_d<64, true>(ws, a, stream) : fwd8_d<128, true>(ws, a, stream);
+  if (a.d == 64) return fwd8_d<64, false>(ws, a, stream);
+  if (a.d == 96) return fwd8_d<96, false>(ws, a, stream);
+  return fwd8_d<128, false>(ws, a, stream);
 }
 
 }  // namespace attn

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
     ATTN_OK = 0,
@@ -181,6 +181,29 @@ attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v,
 attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B,
                            int H, int N, int d, int causal, float scale,
                            const float* bias, int out_dtype, void* stream);
+
+/*
+ * attn_k_smooth_quant_fp8qk / attn_fwd_sage8_fp8qk -- the FP8-QK variant of
+ * the 8-bit path: Q and the mean-centred K go to FP8 e4m3 with one scale
+ * per 64-row block (scale = amax/448, code = e4m3_rne(x * (448/amax)); a
+ * zero amax gives scale 1), the block-wise dynamic scaling that page 2
+ * ("FlashAttention-3" bulletin, claim vs reality section) says FP8 products
+ * need, and S = Q K^T runs on the FP8 matrix instruction in fp32.  K mean,
+ * V, P and the two-level P V product are as in attn_k_smooth_quant /
+ * attn_fwd_sage8, so the pair differs from the INT8 recipe only in the
+ * number format of the first product.  The workspace (same size and
+ * layout; Qq and Kq hold e4m3 bytes) must be written by
+ * attn_k_smooth_quant_fp8qk for attn_fwd_sage8_fp8qk and by
+ * attn_k_smooth_quant for attn_fwd_sage8; the library cannot tell them
+ * apart.  d must be 64 or 128.  Other arguments as for the INT8 pair.
+ */
+attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* v,
+                                      int in_dtype, int B, int H, int N, int d,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int B,
+                                 int H, int N, int d, int causal, float scale,
+                                 const float* bias, int out_dtype, void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd_f16/bf16

@@ -28,11 +28,12 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert {"attn_fwd_f16", "attn_fwd_bf16", "attn_fwd_strided_f16", "attn_fwd_strided_bf16",
             "attn_bwd_workspace_size", "attn_bwd_f16", "attn_bwd_bf16",
+            "attn_k_smooth_quant_fp8qk", "attn_fwd_sage8_fp8qk",
             "attn_sage8_workspace_size", "attn_k_smooth_quant", "attn_sage8_workspace_layout",
             "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 3
+    assert L.attn_abi_version() == 4
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -148,3 +149,17 @@ def test_bwd_validation(name, dt):
     assert _bwd(fn, ws=FAKE + 16, grad=dt) == E_ALIGN
     assert _bwd(fn, o=FAKE + 8, grad=dt) == E_ALIGN
     assert _bwd(fn, dbias=FAKE + 2, grad=dt) == E_ALIGN
+
+
+def test_fp8qk_validation():
+    L = attn.lib()
+    need = L.attn_sage8_workspace_size(1, 2, 100, 64)
+    prep = L.attn_k_smooth_quant_fp8qk
+    assert prep(None, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need, None) == E_NULL
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 96, FAKE, need, None) == E_HEADDIM  # d = 96: INT8 only
+    assert prep(FAKE, FAKE, FAKE, F32, 1, 2, 100, 64, FAKE, need, None) == E_DTYPE
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need - 1, None) == E_WS
+    fwd8 = L.attn_fwd_sage8_fp8qk
+    assert fwd8(None, FAKE, None, 1, 2, 100, 64, 0, 0.1, None, BF16, None) == E_WS
+    assert fwd8(FAKE, FAKE, None, 1, 2, 100, 96, 0, 0.1, None, BF16, None) == E_HEADDIM
+    assert fwd8(FAKE, FAKE, None, 1, 2, 100, 64, 3, 0.1, None, BF16, None) == E_ARG

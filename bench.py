@@ -364,6 +364,23 @@ def extra_workloads(attn, workloads, stream, dev):
         if "bf16" in res:
             res["sage8"]["speedup_vs_bf16_attention"] = round(tf8 / res["bf16"]["tflops"], 3)
             res["sage8"]["speedup_vs_bf16_end_to_end"] = round(tfe / res["bf16"]["tflops"], 3)
+        # the FP8-QK variant (Q and centred K in e4m3 blocks) on the same data
+        wsf = attn.sage8_prep(q2, k2, v2, qk="fp8").workspace
+        prepf = attn.Sage8Prepared(wsf, tuple(q2.shape), q2.dtype, qk="fp8")
+        fpf = lambda: attn.sage8_prep(q2, k2, v2, workspace=wsf, qk="fp8")  # noqa: E731
+        f8f = lambda: attn.fwd_sage8(prepf, causal=c2["causal"], bias=b2)  # noqa: E731
+        _warm(fpf)
+        spf = _stats(_time_launches(fpf, 20, stream))
+        _warm(f8f)
+        s8f = _stats(_time_launches(f8f, 20, stream))
+        tff = F2 / (s8f["ms_avg"] * 1e-3) / 1e12
+        tffe = F2 / ((s8f["ms_avg"] + spf["ms_avg"]) * 1e-3) / 1e12
+        res["sage8_fp8qk"] = {"attention": {**s8f, "tflops": round(tff, 2),
+                                            "frac_of_8bit_peak": round(tff / PEAK_8BIT_TFLOPS, 4)},
+                              "prep": {**spf, "GBs": round(prep_bytes(*q2.shape) / (spf["ms_avg"] * 1e-3) / 1e9, 1)},
+                              "tflops_prep_plus_attention": round(tffe, 2),
+                              "speedup_vs_int8_qk_attention": round(tff / tf8, 3)}
+        del wsf, prepf
         if sparse:
             res["flops_counted"] = f"{F2:.4e} (gated-on block pairs only, {c2['gate_keep']} of the off-diagonal kept)"
         extra[f"{c2['name']}: B={c2['B']} H={c2['H']} N={c2['N']} d={c2['d']} "

@@ -14,7 +14,8 @@ raised.
     fwd_sage8(prep, causal=False, ...)          # 8-bit forward
     sageattn(q, k, v, causal=False, ...)        # both 8-bit steps
 
-Tensors are [B, H, N, d] contiguous CUDA (HIP) tensors, d in {64, 128}.
+Tensors are [B, H, N, d] contiguous CUDA (HIP) tensors, d in {64, 96, 128}
+(the 8-bit path and its FP8-QK variant: INT8 scores at 64, 96, 128; FP8 at 64, 128).
 ``bias`` is fp32 [B, H, ceil(N/64), ceil(N/64)]: an additive logit per
 64-query x 64-key block in natural-log units.
 """
@@ -149,7 +150,7 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, bias=None, grad_dtype=N
     """Gradients of the fused forward: given the forward's inputs, its output
     o (q's dtype, or float32 for an exact row statistic D) and LSE, and
     dout = dL/dO, returns (dq, dk, dv), plus the fp32 gradient of the
-    [B,H,nb,nb] block bias when return_dbias.  d must be 64 or 128."""
+    [B,H,nb,nb] block bias when return_dbias.  d must be 64, 96 or 128."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     for name, t, dts in (("o", o, (q.dtype, torch.float32)), ("dout", dout, (q.dtype,))):
@@ -197,7 +198,7 @@ class _Attention(torch.autograd.Function):
 
 
 def attention(q, k, v, causal=False, scale=None, bias=None):
-    """Differentiable fused attention (fp16/bf16, d = 64 or 128): the forward
+    """Differentiable fused attention (fp16/bf16, d = 64, 96 or 128): the forward
     kernel, and the backward kernels for torch.autograd (gradients for q, k,
     v and the block bias)."""
     return _Attention.apply(q, k, v, bias, bool(causal), scale)

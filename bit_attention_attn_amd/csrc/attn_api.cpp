@@ -117,7 +117,7 @@ attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const 
       dq == nullptr || dk == nullptr || dv == nullptr)
     return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (d != 64 && d != 96 && d != 128) return ATTN_ERR_HEADDIM;
   if ((int64_t)B * H * N * d >= kMaxElems) return ATTN_ERR_SHAPE;
   if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_ARG;
@@ -240,7 +240,7 @@ attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int N, int d) {
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 96 && d != 128)) return 0;
   if ((int64_t)B * H * N * d >= kMaxElems) return 0;
   return ((size_t)B * H * N * sizeof(float) + 255) & ~(size_t)255;
 }

@@ -31,18 +31,26 @@ namespace {
 
 constexpr int kBN = 64;  // keys per block
 
-// ---- D = rowsum(dO * O) in fp32, one row per D/8 consecutive threads; O in
-// the input dtype or (OF32) fp32 ------------------------------------------------------
+// threads per row of the D kernel: D/8 rounded up to a power of two, so a
+// row's threads are consecutive lanes of one wave (d = 96: 12 chunks on 16
+// threads, the last 4 adding nothing)
+template <int D>
+constexpr int delta_tpr() { return D <= 64 ? 8 : 16; }
+
+// ---- D = rowsum(dO * O) in fp32, one row per delta_tpr<D>() consecutive
+// threads; O in the input dtype or (OF32) fp32 ---------------------------------
 template <int D, bool BF16, bool OF32>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__ o,
                                                         const uint16_t* __restrict__ dout,
                                                         float* __restrict__ delta, int64_t rows) {
-  constexpr int kCpr = D / 8;        // 8-element chunks per row (8 or 16)
-  constexpr int kRows = 256 / kCpr;  // rows per workgroup
-  const int tid = threadIdx.x, ch = tid % kCpr;
-  const int64_t row = (int64_t)blockIdx.x * kRows + tid / kCpr;
+  constexpr int kCpr = D / 8;               // 8-element chunks per row (8, 12 or 16)
+  constexpr int kTpr = delta_tpr<D>();      // threads per row
+  constexpr int kRows = 256 / kTpr;         // rows per workgroup
+  static_assert(kCpr <= kTpr && (kTpr & (kTpr - 1)) == 0, "row threads");
+  const int tid = threadIdx.x, ch = tid % kTpr;
+  const int64_t row = (int64_t)blockIdx.x * kRows + tid / kTpr;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && ch < kCpr) {
     const u32x4_t b = *(const u32x4_t*)(dout + row * D + ch * 8);
     float ov[8];
     if constexpr (OF32) {
@@ -61,9 +69,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(ov[e], in_to_f32<BF16>((uint16_t)(b[e >> 1] >> (16 * (e & 1)))), acc);
   }
-  // the kCpr threads of a row are consecutive lanes of one wave
+  // the kTpr threads of a row are consecutive lanes of one wave
 #pragma unroll
-  for (int off = kCpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  for (int off = kTpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && ch == 0) delta[row] = acc;
 }
 
@@ -136,8 +144,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   const float* bias_row = HAS_BIAS ? bias + ((size_t)bh * p.nb + min(qw0 / kBN, p.nb - 1)) * p.nb : nullptr;
 
   // loader (as in the forward): chunk tid + i*threads of a block at byte
-  // 16*tid + kb*64*D*2 + 16*i*threads; rows past N read zeros
-  constexpr int kNst = kBN * kCpr / kThreads;
+  // 16*tid + kb*64*D*2 + 16*i*threads; rows past N read zeros.  At d = 96 a
+  // block is 768 chunks, so the second round covers only the first 256
+  // threads (the others' loads are never stored).
+  constexpr int kChunks = kBN * kCpr;
+  constexpr int kNst = (kChunks + kThreads - 1) / kThreads;
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(p.k + head, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(p.v + head, (uint32_t)N * D * 2);
   const uint32_t voff = 16u * tid;
@@ -153,6 +164,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
 #pragma unroll
     for (int i = 0; i < kNst; ++i) {
       const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
+      if (kChunks % kThreads != 0 && idx >= kChunks) continue;
       *(u32x4_t*)(kl + buf * kKTile + row * kKRow + ch * 8) = kst[i];
       *(u32x4_t*)(vl + buf * kVTile + row * kVRow + ch * 8) = vst[i];
     }
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
 template <int D, bool BF16>
 hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  constexpr int kRowsPerBlock = 256 / (D / 8);
+  constexpr int kRowsPerBlock = 256 / delta_tpr<D>();
   const dim3 dgrid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   if (a.o_f32)
     hipLaunchKernelGGL((bwd_delta_kernel<D, BF16, true>), dgrid, dim3(256), 0, stream, a.o,
@@ -295,6 +307,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd16(const BwdArgs& a, bool bf16, hipStream_t stream) {
   hipError_t e;
   if (a.d == 64) e = bf16 ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+  else if (a.d == 96) e = bf16 ? launch_d<96, true>(a, stream) : launch_d<96, false>(a, stream);
   else e = bf16 ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
   if (e != hipSuccess) return e;
   return launch_bwd16_kv(a, bf16, stream);

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const fl
 
   // loader: chunk tid + i*threads of the Q (dO) block at byte 16*tid +
   // jq*64*D*2 + 16*i*threads; rows past N read zeros
-  constexpr int kNst = kQBk * kCpr / kThreads;
+  constexpr int kNst = kQBk * kCpr / kThreads;  // 2, 3 or 4
+  static_assert(kNst * kThreads == kQBk * kCpr, "whole chunks per thread");
   const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(p.q + head, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(p.dout + head, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t lrs = buffer_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
@@ -312,6 +313,9 @@ hipError_t launch_bwd16_kv(const BwdArgs& a, bool bf16, hipStream_t stream) {
   if (a.d == 64) {
     if (bf16) launch_kv_d<64, true>(p, a, stream);
     else launch_kv_d<64, false>(p, a, stream);
+  } else if (a.d == 96) {
+    if (bf16) launch_kv_d<96, true>(p, a, stream);
+    else launch_kv_d<96, false>(p, a, stream);
   } else {
     if (bf16) launch_kv_d<128, true>(p, a, stream);
     else launch_kv_d<128, false>(p, a, stream);

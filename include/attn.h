@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
     ATTN_OK = 0,
@@ -239,7 +239,7 @@ size_t attn_bwd_workspace_size(int B, int H, int N, int d);
  *  causal, scale, bias  as passed to the forward.
  *  workspace  device buffer of at least attn_bwd_workspace_size bytes,
  *             256-byte aligned; overwritten.
- *  d must be 64 or 128.  Products run on the matrix cores with fp32
+ *  d must be 64, 96 or 128.  Products run on the matrix cores with fp32
  *  accumulation; P and dS are rounded to the input dtype for the products
  *  that use them.  Rows with LSE = -inf (no visible key) pass no gradient.
  *  dbias is accumulated with at most two atomic additions per element onto

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
             "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 4
+    assert L.attn_abi_version() == 5
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -134,12 +134,13 @@ def test_bwd_validation(name, dt):
     L = attn.lib()
     fn = getattr(L, name)
     assert L.attn_bwd_workspace_size(1, 2, 100, 64) == 1024  # 200 fp32 rows, rounded to 256 bytes
-    assert L.attn_bwd_workspace_size(1, 2, 100, 96) == 0      # d = 96 has no backward
+    assert L.attn_bwd_workspace_size(1, 2, 100, 96) == 1024
+    assert L.attn_bwd_workspace_size(1, 2, 100, 80) == 0      # no such head dimension
     assert _bwd(fn, q=None, grad=dt) == E_NULL
     assert _bwd(fn, lse=None, grad=dt) == E_NULL
     assert _bwd(fn, dq=None, grad=dt) == E_NULL
     assert _bwd(fn, B=0, grad=dt) == E_SHAPE
-    assert _bwd(fn, d=96, grad=dt) == E_HEADDIM
+    assert _bwd(fn, d=80, grad=dt) == E_HEADDIM
     assert _bwd(fn, causal=2, grad=dt) == E_ARG
     assert _bwd(fn, scale=float("nan"), grad=dt) == E_ARG
     assert _bwd(fn, grad=F16 if dt == BF16 else BF16, odt=dt) == E_DTYPE

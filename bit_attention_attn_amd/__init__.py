@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.attn_k_smooth_quant_fp8qk.restype = i
     L.attn_fwd_sage8_fp8qk.argtypes = L.attn_fwd_sage8.argtypes
     L.attn_fwd_sage8_fp8qk.restype = i
+    L.attn_k_smooth_quant_strided.argtypes = [vp, vp, vp, i, i, i, i, i, ll_p, i, vp, sz, vp]
+    L.attn_k_smooth_quant_strided.restype = i
+    L.attn_fwd_sage8_strided.argtypes = [vp, vp, vp, i, i, i, i, ll_p, i, f, vp, i, i, vp]
+    L.attn_fwd_sage8_strided.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_abi_version.argtypes = []
@@ -283,13 +287,24 @@ class Sage8Prepared:
         self.qk = qk  # "int8", or "fp8" for the FP8-QK variant
 
 
+_QK_FORMAT = {"int8": 0, "fp8": 1}
+
+
 def sage8_prep(q, k, v, workspace=None, qk="int8"):
     """K smoothing and 8-bit quantisation of Q, K, V into a device workspace.
+    q, k, v are logical [B,H,N,d] tensors, contiguous or any layout with d
+    contiguous (e.g. x.transpose(1, 2) of a token-major [B,N,H,d] tensor).
     qk="fp8" quantises Q and K to e4m3 blocks (the FP8-QK variant, d = 64 or
     128) instead of INT8; fwd_sage8 then uses FP8 scores."""
-    if qk not in ("int8", "fp8"):
+    if qk not in _QK_FORMAT:
         raise ValueError('qk must be "int8" or "fp8"')
-    _check_qkv(q, k, v)
+    contiguous = all(isinstance(t, torch.Tensor) and t.is_contiguous() for t in (q, k, v))
+    if contiguous:
+        _check_qkv(q, k, v)
+    else:
+        _check_views((q, k, v), 4)
+        if k.shape != q.shape or v.shape != q.shape:
+            raise ValueError("q, k, v must have the same logical shape")
     B, H, N, d = q.shape
     L = lib()
     need = L.attn_sage8_workspace_size(B, H, N, d)
@@ -297,40 +312,70 @@ def sage8_prep(q, k, v, workspace=None, qk="int8"):
         raise AttnError(2, "attn_sage8_workspace_size")
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
-    fn = L.attn_k_smooth_quant_fp8qk if qk == "fp8" else L.attn_k_smooth_quant
     with torch.cuda.device(q.device):
-        st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d,
-                _ptr(workspace), workspace.numel(), _stream(q.device))
+        if contiguous:
+            fn = L.attn_k_smooth_quant_fp8qk if qk == "fp8" else L.attn_k_smooth_quant
+            st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d,
+                    _ptr(workspace), workspace.numel(), _stream(q.device))
+        else:
+            fn = L.attn_k_smooth_quant_strided
+            arr = (ctypes.c_longlong * 9)(*[int(t.stride(i)) for t in (q, k, v) for i in range(3)])
+            st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d, arr, _QK_FORMAT[qk],
+                    _ptr(workspace), workspace.numel(), _stream(q.device))
     if st != 0:
         raise AttnError(st, fn.__name__)
     return Sage8Prepared(workspace, (B, H, N, d), q.dtype, qk)
 
 
 def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtype=None,
-              return_lse=False):
-    """8-bit fused forward from a prepared workspace."""
+              return_lse=False, layout_like=None):
+    """8-bit fused forward from a prepared workspace.  O is contiguous
+    [B,H,N,d], or has the layout of the logical [B,H,N,d] tensor layout_like
+    (torch.empty_like, so a token-major view gives a token-major O)."""
     B, H, N, d = prep.shape
     dev = prep.workspace.device
     bias = _check_bias(bias, B, H, N, dev)
     out_dtype = prep.in_dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    if layout_like is not None:
+        if tuple(layout_like.shape) != (B, H, N, d):
+            raise ValueError("layout_like must have the prepared [B,H,N,d] shape")
+        o = torch.empty_like(layout_like, dtype=out_dtype, device=dev)
+    else:
+        o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
-    fn = lib().attn_fwd_sage8_fp8qk if prep.qk == "fp8" else lib().attn_fwd_sage8
     with torch.cuda.device(dev):
-        st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
-                _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
+        if o.is_contiguous():
+            fn = lib().attn_fwd_sage8_fp8qk if prep.qk == "fp8" else lib().attn_fwd_sage8
+            st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
+                    _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
+        else:
+            fn = lib().attn_fwd_sage8_strided
+            arr = (ctypes.c_longlong * 3)(*[int(o.stride(i)) for i in range(3)])
+            st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, arr, int(bool(causal)), float(scale),
+                    _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _QK_FORMAT[prep.qk], _stream(dev))
     if st != 0:
         raise AttnError(st, fn.__name__)
     return (o, lse) if return_lse else o
 
 
-def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False, qk="int8"):
-    """8-bit attention in one call (preparation, then the forward)."""
+def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False, qk="int8",
+             tensor_layout="HND"):
+    """8-bit attention in one call (preparation, then the forward).
+    tensor_layout "HND": q, k, v are [B,H,N,d]; "NHD": they are token-major
+    [B,N,H,d] and O comes back token-major.  Either may be a strided view
+    with d contiguous."""
+    if tensor_layout not in ("HND", "NHD"):
+        raise ValueError('tensor_layout must be "HND" or "NHD"')
+    if tensor_layout == "NHD":
+        q, k, v = (t.transpose(1, 2) for t in (q, k, v))
     prep = sage8_prep(q, k, v, qk=qk)
-    return fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
-                     return_lse=return_lse)
+    res = fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
+                    return_lse=return_lse, layout_like=q)
+    if tensor_layout == "NHD":
+        return (res[0].transpose(1, 2), res[1]) if return_lse else res.transpose(1, 2)
+    return res
 
 
 def sage8_workspace_views(prep: Sage8Prepared) -> dict:

@@ -74,8 +74,12 @@ struct Sage8Layout {
 Sage8Layout sage8_layout(int B, int H, int N, int d);
 // qk_fp8: Q and K in e4m3 blocks (the FP8-QK variant; d = 64 or 128) instead
 // of INT8; the forward must be told the format the preparation wrote.
+// strides: element strides (batch, head, token) of q, k, v with d
+// contiguous (9 values); nullptr for contiguous [B,H,N,d].
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H,
-                             int N, int d, void* ws, hipStream_t stream, bool qk_fp8);
+                             int N, int d, const int64_t* strides, void* ws, hipStream_t stream, bool qk_fp8);
+// O is written with the element strides a.strides[9..11] (batch, head,
+// token) when a.general, else contiguous [B,H,N,d].
 hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream, bool qk_fp8);
 
 }  // namespace attn

@@ -84,17 +84,24 @@ __device__ __forceinline__ int key_pos(int k) {
 }
 
 // ---- colstats: grid (nchunk, B*H), prep_threads<D>() threads --------------------------
+// Input layout: element strides (batch, head, token) of q, k, v, d contiguous.
+struct PrepIn {
+  int H;
+  int64_t s[9];
+};
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                       int N, double* __restrict__ kpart,
-                                                      float* __restrict__ vpart, int nchunk) {
+                                                      float* __restrict__ vpart, int nchunk, PrepIn in) {
   constexpr int kCpr = D / 8;                        // 16-byte chunks per row
   constexpr int kRows = prep_threads<D>() / kCpr;    // rows per pass
   __shared__ double ssum[kRows][D];
   __shared__ float smax[kRows][D];
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
-  const size_t head = (size_t)bh * N * D;
+  const int b = bh / in.H, h = bh - b * in.H;
+  const uint32_t ksn = (uint32_t)in.s[5], vsn = (uint32_t)in.s[8];  // token strides
   double acc[8];
   float mx[8];
 #pragma unroll
@@ -104,15 +111,17 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
   }
   // buffer loads: rows past N read zeros, which change neither the sums nor
   // the absolute maxima, so the row loop has a fixed trip count
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k + head, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v + head, (uint32_t)N * D * 2);
-  const uint32_t voff = 16u * tid;  // row rg, chunk ch of a pass
+  // (the byte offsets stay below 2^32 for rows up to N + kChunk: checked by
+  // the caller)
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k + b * in.s[3] + h * in.s[4], (uint32_t)N * ksn * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v + b * in.s[6] + h * in.s[7], (uint32_t)N * vsn * 2);
+  const uint32_t kvoff = 2u * (rg * ksn + 8u * ch), vvoff = 2u * (rg * vsn + 8u * ch);  // row rg, chunk ch
   const int n0 = chunk * kChunk;
 #pragma unroll
   for (int i = 0; i < kChunk / kRows; ++i) {
-    const uint32_t soff = (uint32_t)(n0 + i * kRows) * D * 2;
-    const u32x4_t kx = buffer_load16(krs, voff, soff);
-    const u32x4_t vx = buffer_load16(vrs, voff, soff);
+    const uint32_t n = (uint32_t)(n0 + i * kRows);
+    const u32x4_t kx = buffer_load16(krs, kvoff, n * ksn * 2);
+    const u32x4_t vx = buffer_load16(vrs, vvoff, n * vsn * 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint16_t kb = (uint16_t)(kx[e >> 1] >> (16 * (e & 1)));
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
                                                    const float* __restrict__ kmean, const float* __restrict__ vinv,
                                                    int8_t* __restrict__ qq, int8_t* __restrict__ kq,
                                                    uint8_t* __restrict__ vq, float* __restrict__ sq,
-                                                   float* __restrict__ sk) {
+                                                   float* __restrict__ sk, PrepIn in) {
   constexpr int kThreads = prep_threads<D>();
   constexpr int kCpr = D / 8;
   constexpr int kRows = kThreads / kCpr;  // rows per pass
@@ -228,7 +237,10 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint8_t vt[D][kQB];  // transposed, permuted V codes
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
-  const size_t head = (size_t)bh * N * D;
+  const int b = bh / in.H, h = bh - b * in.H;
+  const uint16_t* qh = q + b * in.s[0] + h * in.s[1];
+  const uint16_t* kh = k + b * in.s[3] + h * in.s[4];
+  const uint16_t* vh = v + b * in.s[6] + h * in.s[7];
   const size_t headp = (size_t)bh * np * D;
   const int n0 = blk * kQB;
 
@@ -245,9 +257,9 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
     const int r = rg + i * kRows, n = n0 + r;
     u32x4_t qx = {0u, 0u, 0u, 0u}, kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
     if (n < N) {
-      qx = *(const u32x4_t*)(q + head + (size_t)n * D + ch * 8);
-      kx = *(const u32x4_t*)(k + head + (size_t)n * D + ch * 8);
-      vx = *(const u32x4_t*)(v + head + (size_t)n * D + ch * 8);
+      qx = *(const u32x4_t*)(qh + n * in.s[2] + ch * 8);
+      kx = *(const u32x4_t*)(kh + n * in.s[5] + ch * 8);
+      vx = *(const u32x4_t*)(vh + n * in.s[8] + ch * 8);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -299,15 +311,22 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
 }
 
 template <int D, bool BF16, bool QKFP8>
-hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, int N, void* ws,
-                     hipStream_t stream) {
+hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, int N, const int64_t* strides,
+                     void* ws, hipStream_t stream) {
   const Sage8Layout L = sage8_layout(B, H, N, D);
+  PrepIn in;
+  in.H = H;
+  for (int t = 0; t < 3; ++t) {
+    in.s[3 * t + 0] = strides ? strides[3 * t + 0] : (int64_t)H * N * D;
+    in.s[3 * t + 1] = strides ? strides[3 * t + 1] : (int64_t)N * D;
+    in.s[3 * t + 2] = strides ? strides[3 * t + 2] : D;
+  }
   char* w = static_cast<char*>(ws);
   const int bh = B * H;
   const int np = L.nblk * kQB;
   hipLaunchKernelGGL((sage8_colstats<D, BF16>), dim3(L.nchunk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N,
-                     reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk);
+                     reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk, in);
   hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3((256 / D) * D), 0, stream,
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
@@ -318,7 +337,7 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
                      reinterpret_cast<const float*>(w + L.kmean), reinterpret_cast<const float*>(w + L.vinv),
                      reinterpret_cast<int8_t*>(w + L.qq), reinterpret_cast<int8_t*>(w + L.kq),
                      reinterpret_cast<uint8_t*>(w + L.vq), reinterpret_cast<float*>(w + L.sq),
-                     reinterpret_cast<float*>(w + L.sk));
+                     reinterpret_cast<float*>(w + L.sk), in);
   return hipGetLastError();
 }
 
@@ -342,6 +361,8 @@ struct Fwd8Params {
   int ntiles;  // B*H*nq
   float c;     // scale * log2(e), never 0
   int out_kind;
+  int H;
+  int64_t os[3];  // element strides (batch, head, token) of O
 };
 
 constexpr int kNW8 = 4;                // waves per workgroup
@@ -646,7 +667,8 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   // lane (l32, hf) holds d = 32dt + 8g + 4hf + u of query qi: 16-byte (fp32)
   // or 8-byte (fp16 / bf16) stores straight from the accumulators
   const float* svh = p.sv + (size_t)bh * D;
-  const size_t orow = ((size_t)bh * N + qi) * D;
+  const int ob = bh / p.H;
+  const int64_t orow = ob * p.os[0] + (bh - ob * p.H) * p.os[1] + (int64_t)qi * p.os[2];
   if (qi < N)
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -690,6 +712,10 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   p.c = (float)((double)a.scale * 1.4426950408889634);
   if (p.c == 0.f) p.c = 1.17549435e-38f;
   p.out_kind = a.out_kind;
+  p.H = a.H;
+  p.os[0] = a.general ? a.strides[9] : (int64_t)a.H * a.N * D;
+  p.os[1] = a.general ? a.strides[10] : (int64_t)a.N * D;
+  p.os[2] = a.general ? a.strides[11] : D;
   // persistent grid for causal shapes (tiles differ in cost), one workgroup
   // per tile otherwise
   const int grid = CAUSAL ? persistent_grid(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), kThreads8,
@@ -705,21 +731,21 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
 
 namespace {
 template <bool QKFP8>
-hipError_t prep_q(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d, void* ws,
-                  hipStream_t stream) {
-  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8>(q, k, v, B, H, N, ws, stream)
-                           : prep_impl<64, false, QKFP8>(q, k, v, B, H, N, ws, stream);
-  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8>(q, k, v, B, H, N, ws, stream)
-                           : prep_impl<96, false, QKFP8>(q, k, v, B, H, N, ws, stream);
-  return bf16 ? prep_impl<128, true, QKFP8>(q, k, v, B, H, N, ws, stream)
-              : prep_impl<128, false, QKFP8>(q, k, v, B, H, N, ws, stream);
+hipError_t prep_q(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
+                  const int64_t* st, void* ws, hipStream_t stream) {
+  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8>(q, k, v, B, H, N, st, ws, stream)
+                           : prep_impl<64, false, QKFP8>(q, k, v, B, H, N, st, ws, stream);
+  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8>(q, k, v, B, H, N, st, ws, stream)
+                           : prep_impl<96, false, QKFP8>(q, k, v, B, H, N, st, ws, stream);
+  return bf16 ? prep_impl<128, true, QKFP8>(q, k, v, B, H, N, st, ws, stream)
+              : prep_impl<128, false, QKFP8>(q, k, v, B, H, N, st, ws, stream);
 }
 }  // namespace
 
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
-                             void* ws, hipStream_t stream, bool qk_fp8) {
-  return qk_fp8 ? prep_q<true>(q, k, v, bf16, B, H, N, d, ws, stream)
-                : prep_q<false>(q, k, v, bf16, B, H, N, d, ws, stream);
+                             const int64_t* strides, void* ws, hipStream_t stream, bool qk_fp8) {
+  return qk_fp8 ? prep_q<true>(q, k, v, bf16, B, H, N, d, strides, ws, stream)
+                : prep_q<false>(q, k, v, bf16, B, H, N, d, strides, ws, stream);
 }
 
 namespace {

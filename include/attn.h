@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum {
     ATTN_OK = 0,
@@ -68,6 +68,12 @@ typedef enum {
     ATTN_DTYPE_BF16 = 1,
     ATTN_DTYPE_F32 = 2
 } attn_dtype;
+
+/* Number format of Q and K in the 8-bit path's workspace. */
+typedef enum {
+    ATTN_QK_INT8 = 0,  /* the INT8 recipe (attn_k_smooth_quant)            */
+    ATTN_QK_FP8 = 1    /* the FP8-QK variant (attn_k_smooth_quant_fp8qk)   */
+} attn_qk_format;
 
 /*
  * attn_fwd_f16 / attn_fwd_bf16 -- fused attention forward (fp16 / bf16).
@@ -204,6 +210,35 @@ attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* 
 attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int B,
                                  int H, int N, int d, int causal, float scale,
                                  const float* bias, int out_dtype, void* stream);
+
+/*
+ * attn_k_smooth_quant_strided / attn_fwd_sage8_strided -- the 8-bit pair on
+ * inputs and outputs of any layout with d contiguous (token-major [B,N,H,d],
+ * views into a fused QKV projection, ...), so the 8-bit path takes the same
+ * tensors as the 16-bit strided forward.  The computation and the workspace
+ * are exactly those of the contiguous pair for the same logical [B,H,N,d]
+ * data; qk_format (ATTN_QK_INT8 or ATTN_QK_FP8) selects the recipe (INT8, or
+ * the FP8-QK variant with d = 64 or 128) and must match between the two.
+ *
+ *  strides    host array of 9 element strides: (batch, head, token) of q,
+ *             then k, then v.  Each a multiple of 8 and >= 0, token strides
+ *             >= d, and (N + 256) * token stride * 2 < 2^32 (the column
+ *             statistics read whole 256-token chunks; rows past N read as 0).
+ *  o_strides  host array of 3 element strides (batch, head, token) of o,
+ *             with the same rules (without the 256-token margin).
+ *  The LSE stays [B,H,N] contiguous.  Other arguments and errors as for
+ *  attn_k_smooth_quant and attn_fwd_sage8; a NULL stride array is
+ *  ATTN_ERR_NULL, an unknown qk_format ATTN_ERR_ARG.
+ */
+attn_status attn_k_smooth_quant_strided(const void* q, const void* k, const void* v,
+                                        int in_dtype, int B, int H, int N, int d,
+                                        const long long* strides, int qk_format,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+attn_status attn_fwd_sage8_strided(const void* workspace, void* o, float* lse, int B,
+                                   int H, int N, int d, const long long* o_strides,
+                                   int causal, float scale, const float* bias,
+                                   int out_dtype, int qk_format, void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd_f16/bf16

@@ -29,11 +29,12 @@ def test_library_exports_every_declared_function():
     assert {"attn_fwd_f16", "attn_fwd_bf16", "attn_fwd_strided_f16", "attn_fwd_strided_bf16",
             "attn_bwd_workspace_size", "attn_bwd_f16", "attn_bwd_bf16",
             "attn_k_smooth_quant_fp8qk", "attn_fwd_sage8_fp8qk",
+            "attn_k_smooth_quant_strided", "attn_fwd_sage8_strided",
             "attn_sage8_workspace_size", "attn_k_smooth_quant", "attn_sage8_workspace_layout",
             "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 5
+    assert L.attn_abi_version() == 6
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -164,3 +165,42 @@ def test_fp8qk_validation():
     assert fwd8(None, FAKE, None, 1, 2, 100, 64, 0, 0.1, None, BF16, None) == E_WS
     assert fwd8(FAKE, FAKE, None, 1, 2, 100, 96, 0, 0.1, None, BF16, None) == E_HEADDIM
     assert fwd8(FAKE, FAKE, None, 1, 2, 100, 64, 3, 0.1, None, BF16, None) == E_ARG
+
+
+def test_sage8_strided_validation():
+    """Argument checks of the strided 8-bit pair (all run before any device
+    call, so they hold without a GPU)."""
+    L = attn.lib()
+    ll = ctypes.c_longlong
+    B, H, N, d = 1, 2, 100, 64
+    need = L.attn_sage8_workspace_size(B, H, N, d)
+    contig = [H * N * d, N * d, d] * 3
+    nhd = [N * H * d, d, H * d] * 3
+    prep = L.attn_k_smooth_quant_strided
+
+    def p(st, fmt=0, dd=d, ws=FAKE, nb=need, q=FAKE):
+        arr = (ll * 9)(*st) if st is not None else None
+        return prep(q, FAKE, FAKE, BF16, B, H, N, dd, arr, fmt, ws, nb, None)
+
+    assert p(None) == E_NULL
+    assert p(contig, q=None) == E_NULL
+    assert p(contig, fmt=2) == E_ARG
+    assert p(contig, fmt=1, dd=96) == E_HEADDIM      # FP8 scores: d = 64 or 128
+    assert p(contig, nb=need - 1) == E_WS
+    assert p(nhd[:2] + [d - 8] + nhd[3:]) == E_ARG    # token stride below d
+    assert p(nhd[:1] + [d + 4] + nhd[2:]) == E_ALIGN  # not a multiple of 8 elements
+    assert p([-8] + nhd[1:]) == E_ARG
+    big = (1 << 31) // (N + 256) // 8 * 8 + 8          # (N + 256) rows no longer fit 32-bit byte offsets
+    assert p(nhd[:5] + [big] + nhd[6:]) == E_SHAPE
+    fwd8 = L.attn_fwd_sage8_strided
+
+    def f(st, fmt=0, dd=d, o=FAKE):
+        arr = (ll * 3)(*st) if st is not None else None
+        return fwd8(FAKE, o, None, B, H, N, dd, arr, 0, 0.125, None, BF16, fmt, None)
+
+    assert f(None) == E_NULL
+    assert f([N * H * d, d, H * d], o=None) == E_NULL
+    assert f([N * H * d, d, H * d], fmt=5) == E_ARG
+    assert f([N * H * d, d, 8]) == E_ARG              # token stride below d
+    assert f([N * H * d, d + 2, H * d]) == E_ALIGN
+    assert f([N * H * d, d, H * d], fmt=1, dd=96) == E_HEADDIM

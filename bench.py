@@ -46,12 +46,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 704988683,
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 699951673,
               "sha256": "a394d17d13525a848762ea47ce3ea79edc382e8cf22656cc4f74fda5c29ae56d"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344952343,
-             "sha256": "c904286068ede1d569e6b2e55383086c9abfe1d1e7cf6f4e1a56c79e1044223b"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880727617,
-              "sha256": "c904286068ede1d569e6b2e55383086c9abfe1d1e7cf6f4e1a56c79e1044223b"},
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344963033,
+             "sha256": "d21b85f617e8aa74c194aa640f22d66b26a463b09ee6f659b93351623a7cf6f2"},
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880740309,
+              "sha256": "d21b85f617e8aa74c194aa640f22d66b26a463b09ee6f659b93351623a7cf6f2"},
 }
 
 

@@ -11,7 +11,9 @@
 // workgroups when NW = 4, from one when NW = 8), so one wave's softmax runs
 // on the vector ALU while the other's products run on the matrix cores.
 // Keys and values stream through LDS in blocks of 64; the global loads of a
-// future block are in flight while the current one is computed.
+// future block are in flight while the current one is computed, and (dense
+// layout, no bias) the next work item's Q rows and first block load during
+// the current item's last block.
 //
 // Per key block and wave:
 //   S^T = K Q^T (32x32x16 MFMA, fp32 accumulation): one query per lane
@@ -125,9 +127,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // Loop over (b, h, query tile) work items (work_queue: per-XCD queues,
   // balanced heavy-first order when the grid is persistent).
   const WorkQueue wq = work_queue(p.nbh, p.nq);
+  constexpr bool DENSE = MODE == kDense;
+  constexpr int kNst = kBN * kCpr / kThreads;
+  u32x4_t qf[QS][kKS];
+  u32x4_t kst[kNst], vst[kNst];
+  // Dense layout without a bias: the next work item's Q rows and first K/V
+  // block are loaded during the current item's last block, so a new item
+  // starts without waiting for global memory (pre: qf and kst/vst already
+  // hold this item's Q and block 0).
+  bool pre = false;
   for (int round = 0;; ++round) {
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
+  int bh_n = 0, tq_n = 0;
+  const bool has_next = DENSE && work_item(wq, round + 1, p.nq, bh_n, tq_n);
   const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kWQ;
@@ -162,13 +175,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // Q^T as the B operand of S^T = K Q^T: for query sub-tile qs the lane holds
   // Q[qw0 + 32qs + l32][16kk + 8hf .. +7].  Rows past N read row N-1 (their
   // results are never stored).
-  u32x4_t qf[QS][kKS];
+  if (!(DENSE && pre)) {
 #pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-    const int row = min(qw0 + 32 * qs + l32, N - 1);
-    const uint16_t* src = Q + (size_t)row * qsn + 8 * hf;
+    for (int qs = 0; qs < QS; ++qs) {
+      const int row = min(qw0 + 32 * qs + l32, N - 1);
+      const uint16_t* src = Q + (size_t)row * qsn + 8 * hf;
 #pragma unroll
-    for (int kk = 0; kk < kKS; ++kk) qf[qs][kk] = *(const u32x4_t*)(src + 16 * kk);
+      for (int kk = 0; kk < kKS; ++kk) qf[qs][kk] = *(const u32x4_t*)(src + 16 * kk);
+    }
   }
 
   const int kend = CAUSAL ? min(N, q0 + kBM) : N;
@@ -184,7 +198,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // later), so every load is unconditional.
   // (general layout: key rows ksn / vsn elements apart, so each chunk has its
   // own per-lane offset and the block offset is kb*64 rows)
-  constexpr int kNst = kBN * kCpr / kThreads;
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K, (uint32_t)N * ksn * 2);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V, (uint32_t)N * vsn * 2);
   const uint32_t voff = 16u * tid;
@@ -197,7 +210,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       vvo[i] = (uint32_t)(row * vsn * 2 + ch * 16);
     }
   }
-  u32x4_t kst[kNst], vst[kNst];
   auto load_k = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < kNst; ++i) {
@@ -403,8 +415,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   int j0 = 0;
   if constexpr (HAS_BIAS) j0 = gate.first();
   __builtin_amdgcn_sched_barrier(0);
-  load_k(min(j0, nkb - 1));
-  load_v(min(j0, nkb - 1));
+  if (!(DENSE && pre)) {
+    load_k(min(j0, nkb - 1));
+    load_v(min(j0, nkb - 1));
+  }
   store_k(0);
   store_v(0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -426,7 +440,43 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   } else {
     // every block is active (the plain counted loop schedules measurably
     // better than the general one)
-    for (int j = 0; j < nkb; ++j) step(j, j + 1, j & 1, 0.f);
+    for (int j = 0; j + 1 < nkb; ++j) step(j, j + 1, j & 1, 0.f);
+    // the last block: the next item's Q rows and first K/V block are
+    // loaded meanwhile (Q after this block's last use of it)
+    {
+      const int jc = nkb - 1, buf = jc & 1;
+      const int qt_n = CAUSAL ? p.nq - 1 - tq_n : tq_n;
+      const int qw0_n = qt_n * kBM + wave * kWQ;
+      const size_t off_n = (size_t)bh_n * N * D;
+      if (has_next) {
+        const __amdgpu_buffer_rsrc_t krn = buffer_rsrc(p.k + off_n, (uint32_t)N * D * 2);
+        const __amdgpu_buffer_rsrc_t vrn = buffer_rsrc(p.v + off_n, (uint32_t)N * D * 2);
+#pragma unroll
+        for (int i = 0; i < kNst; ++i) {
+          kst[i] = buffer_load16(krn, voff, 16 * i * kThreads);
+          vst[i] = buffer_load16(vrn, voff, 16 * i * kThreads);
+        }
+      }
+      const bool work = wave_has_rows && jc <= wave_last;
+      if (work) qk(buf, sc);
+      if (has_next) {
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          const int row = min(qw0_n + 32 * qs + l32, N - 1);
+          const uint16_t* src = p.q + off_n + (size_t)row * D + 8 * hf;
+#pragma unroll
+          for (int kk = 0; kk < kKS; ++kk) qf[qs][kk] = *(const u32x4_t*)(src + 16 * kk);
+        }
+      }
+      if (work) {
+        if (needs_mask(jc)) apply_mask(jc, sc);
+        float kc[QS];
+        block_max(sc, kc, 0.f);
+        softmax_p(sc, kc);
+        pv(buf);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: normalise, LSE, stores straight from the accumulators
@@ -456,6 +506,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
         }
     }
   }
+  pre = has_next;
   }  // work items
 }
 

@@ -46,11 +46,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 699951673,
-              "sha256": "a394d17d13525a848762ea47ce3ea79edc382e8cf22656cc4f74fda5c29ae56d"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344963033,
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 712088245,
+              "sha256": "7d9896cb2c2b352bdb642ca683d3906401a98889d81d4e5a8fd52ba4963405ab"},
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344958859,
              "sha256": "d21b85f617e8aa74c194aa640f22d66b26a463b09ee6f659b93351623a7cf6f2"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880740309,
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880740068,
               "sha256": "d21b85f617e8aa74c194aa640f22d66b26a463b09ee6f659b93351623a7cf6f2"},
 }
 

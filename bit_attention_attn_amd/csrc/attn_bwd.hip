@@ -90,6 +90,7 @@ struct BwdQParams {
   float c;  // scale * log2(e), never 0
   float scale;
   int out_f32;
+  int lpt;  // causal: items heaviest first across the heads (work_queue)
 };
 
 template <int D, bool BF16, bool CAUSAL, bool HAS_BIAS>
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   const int hf = lane >> 5;
   const int N = p.N;
 
-  const WorkQueue wq = work_queue(p.nbh, p.nq);
+  const WorkQueue wq = work_queue(p.nbh, p.nq, p.lpt != 0);
   for (int round = 0;; ++round) {
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
@@ -292,7 +293,11 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.out_f32 = a.grad_kind == kOutF32;
   const dim3 grid(p.nq * p.nbh), block(512);
+  p.lpt = 0;
   if (a.causal) {
+    p.lpt = sorted_order(a.bias ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, BF16, true, true>)
+                                : reinterpret_cast<const void*>(&bwd_dq_kernel<D, BF16, true, false>),
+                         512, p.nbh, p.nq);
     if (a.bias) hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, true, true>), grid, block, 0, stream, p, a.bias);
     else hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, true, false>), grid, block, 0, stream, p, a.bias);
   } else {

@@ -206,12 +206,20 @@ struct BlockGate {
 // slots: in round k, slot s takes queue entry k*n + s, or k*n + n-1-s in odd
 // rounds.  This pairs entries e and 2n-1-e; when 2n is a multiple of the
 // tiles per head those two tiles cost the same together for every pair, so
-// the slots are balanced (the host makes the grid persistent only then).
-// With one workgroup per item it is the plain XCD-grouped order.
+// the slots are balanced (the host makes the grid persistent only then:
+// also every slot must get whole pairs of rounds).
+// With one workgroup per item the order is XCD-grouped, head-major (the
+// concurrent workgroups share one head's keys and values in L2), or with
+// lpt tile-major across the XCD's heads: tile position 0 of every head, then
+// position 1, ...  The dispatcher starts the workgroups in that order as
+// slots free up, which for causal tiles (position 0 the heaviest) is list
+// scheduling heaviest first.  The host asks for it when there are few items
+// per slot, where the balance matters more than the L2 sharing
+// (sorted_order).
 struct WorkQueue {
-  int nslot, slot, qlen, xcd, split;
+  int nslot, slot, qlen, xcd, split, lpt;
 };
-__device__ __forceinline__ WorkQueue work_queue(int nbh, int nq) {
+__device__ __forceinline__ WorkQueue work_queue(int nbh, int nq, bool lpt = false) {
   const int G = gridDim.x, w = blockIdx.x;
   WorkQueue q;
   q.split = (nbh & 7) == 0 && (G & 7) == 0;
@@ -219,11 +227,20 @@ __device__ __forceinline__ WorkQueue work_queue(int nbh, int nq) {
   q.slot = q.split ? w >> 3 : w;
   q.qlen = (q.split ? nbh >> 3 : nbh) * nq;
   q.xcd = w & 7;
+  q.lpt = lpt && q.nslot >= q.qlen;  // one workgroup per item
   return q;
 }
 // Returns false when the workgroup is done; else the head bh and the tile
 // position r within the head (causal callers process tile nq-1-r).
 __device__ __forceinline__ bool work_item(const WorkQueue& q, int round, int nq, int& bh, int& r) {
+  if (q.lpt) {
+    if (round > 0 || q.slot >= q.qlen) return false;
+    const int nh = q.qlen / nq;  // heads served by this queue
+    r = q.slot / nh;
+    const int hl = q.slot - r * nh;
+    bh = q.split ? q.xcd + 8 * hl : hl;
+    return true;
+  }
   const int j = round * q.nslot + ((round & 1) ? q.nslot - 1 - q.slot : q.slot);
   if (j >= q.qlen) return false;
   const int hl = j / nq;

@@ -591,28 +591,37 @@ hipError_t launch_g(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Cached per kernel and device.
-int persistent_grid(const void* kernel, int threads, int nbh, int nq) {
+// Workgroups of `kernel` resident at once on the current device (a multiple
+// of 8 when at least 8), cached per kernel and device; -1 on a HIP error.
+int resident_slots(const void* kernel, int threads) {
   struct Entry { const void* k; int dev; int slots; };
   static Entry cache[64];
   static std::atomic<int> used{0};
-  const int items = nbh * nq;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  int slots = 0;
   const int n = used.load(std::memory_order_acquire);
   for (int i = 0; i < n && i < 64; ++i)
-    if (cache[i].k == kernel && cache[i].dev == dev) slots = cache[i].slots;
-  if (slots == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    slots = per_cu * cus;
-    if (slots >= 8) slots &= ~7;
-    if (slots <= 0) return -1;
-    const int i = used.fetch_add(1, std::memory_order_acq_rel);
-    if (i < 64) cache[i] = Entry{kernel, dev, slots};
-  }
+    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].slots;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  int slots = per_cu * cus;
+  if (slots >= 8) slots &= ~7;
+  if (slots <= 0) return -1;
+  const int i = used.fetch_add(1, std::memory_order_acq_rel);
+  if (i < 64) cache[i] = Entry{kernel, dev, slots};
+  return slots;
+}
+
+bool sorted_order(const void* kernel, int threads, int nbh, int nq, int per_slot) {
+  const int slots = resident_slots(kernel, threads);
+  return slots > 0 && (int64_t)nbh * nq < (int64_t)per_slot * slots;
+}
+
+int persistent_grid(const void* kernel, int threads, int nbh, int nq) {
+  const int items = nbh * nq;
+  const int slots = resident_slots(kernel, threads);
+  if (slots <= 0) return -1;
   // Persistent only when the alternating order of the per-XCD queues
   // balances exactly (2 x slots per XCD a multiple of the tiles per head,
   // heads spread evenly over the XCDs) and there is more than one round;

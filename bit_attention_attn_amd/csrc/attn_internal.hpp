@@ -34,6 +34,13 @@ struct FwdArgs {
 // balance exactly and there is more than one round, else nbh * nq (one
 // workgroup per item); -1 on a HIP error.
 int persistent_grid(const void* kernel, int threads, int nbh, int nq);
+// Whether a one-workgroup-per-item causal launch of nbh * nq items should
+// start its items heaviest first across the heads (work_queue's lpt order):
+// when there are fewer than 10 items per resident workgroup slot, the
+// balance of the last rounds matters more than L2 sharing.  Measured on the
+// 8-bit forward: +10% at 5.3 items per slot (4x32x4096), -1.4% at 10.7
+// (1x32x32768).
+bool sorted_order(const void* kernel, int threads, int nbh, int nq, int per_slot = 10);
 
 // 16-bit path (fp16 when bf16 == false).
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream);

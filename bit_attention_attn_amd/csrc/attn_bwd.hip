@@ -115,7 +115,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   const int hf = lane >> 5;
   const int N = p.N;
 
-  const WorkQueue wq = work_queue(p.nbh, p.nq, p.lpt != 0);
+  const WorkQueue wq = work_queue(p.nbh, p.nq, p.lpt);
   for (int round = 0;; ++round) {
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const fl
   const int hf = lane >> 5;
   const int N = p.N;
 
-  const WorkQueue wq = work_queue(p.nbh, p.nkt, p.lpt != 0);
+  const WorkQueue wq = work_queue(p.nbh, p.nkt, p.lpt);
   for (int round = 0;; ++round) {
   int bh, kt;
   if (!work_item(wq, round, p.nkt, bh, kt)) break;  // causal: low key tiles (most queries) first
@@ -270,7 +270,7 @@ void launch_kv(BwdKParams p, const BwdArgs& a, hipStream_t stream) {
                           : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, BF16, CAUSAL, HAS_BIAS, false>);
   // (20 items per slot: measured -5% time at 4x32x4096, where the key side
   // has 16 per slot; unchanged at 1x32x32768, 32 per slot)
-  p.lpt = CAUSAL && sorted_order(k, 256, p.nbh, p.nkt, 20);
+  p.lpt = !CAUSAL ? 0 : sorted_order(k, 256, p.nbh, p.nkt, 20);
   if (a.dbias)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, HAS_BIAS, true>), grid, block, 0, stream, p, a.bias,
                        a.dbias);

@@ -219,7 +219,7 @@ struct BlockGate {
 struct WorkQueue {
   int nslot, slot, qlen, xcd, split, lpt;
 };
-__device__ __forceinline__ WorkQueue work_queue(int nbh, int nq, bool lpt = false) {
+__device__ __forceinline__ WorkQueue work_queue(int nbh, int nq, int lpt = 0) {
   const int G = gridDim.x, w = blockIdx.x;
   WorkQueue q;
   q.split = (nbh & 7) == 0 && (G & 7) == 0;
@@ -227,17 +227,21 @@ __device__ __forceinline__ WorkQueue work_queue(int nbh, int nq, bool lpt = fals
   q.slot = q.split ? w >> 3 : w;
   q.qlen = (q.split ? nbh >> 3 : nbh) * nq;
   q.xcd = w & 7;
-  q.lpt = lpt && q.nslot >= q.qlen;  // one workgroup per item
+  q.lpt = q.nslot >= q.qlen ? lpt : 0;  // one workgroup per item
   return q;
 }
 // Returns false when the workgroup is done; else the head bh and the tile
 // position r within the head (causal callers process tile nq-1-r).
 __device__ __forceinline__ bool work_item(const WorkQueue& q, int round, int nq, int& bh, int& r) {
   if (q.lpt) {
+    // groups of lpt heads in turn, tile-major within a group
     if (round > 0 || q.slot >= q.qlen) return false;
     const int nh = q.qlen / nq;  // heads served by this queue
-    r = q.slot / nh;
-    const int hl = q.slot - r * nh;
+    const int g = min(q.lpt, nh), per = g * nq;
+    const int grp = q.slot / per, h0 = grp * g, gh = min(g, nh - h0);
+    const int jj = q.slot - grp * per;
+    r = jj / gh;
+    const int hl = h0 + (jj - r * gh);
     bh = q.split ? q.xcd + 8 * hl : hl;
     return true;
   }

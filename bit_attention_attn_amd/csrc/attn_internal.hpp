@@ -40,7 +40,8 @@ int persistent_grid(const void* kernel, int threads, int nbh, int nq);
 // balance of the last rounds matters more than L2 sharing.  Measured on the
 // 8-bit forward: +10% at 5.3 items per slot (4x32x4096), -1.4% at 10.7
 // (1x32x32768).
-bool sorted_order(const void* kernel, int threads, int nbh, int nq, int per_slot = 10);
+// Returns the number of heads per group of that order (0: head-major).
+int sorted_order(const void* kernel, int threads, int nbh, int nq, int per_slot = 10);
 
 // 16-bit path (fp16 when bf16 == false).
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream);

@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
 
   // Loop over (b, h, query tile) work items (work_queue: per-XCD queues,
   // balanced heavy-first order when the grid is persistent).
-  const WorkQueue wq = work_queue(p.nbh, p.nq, p.lpt != 0);
+  const WorkQueue wq = work_queue(p.nbh, p.nq, p.lpt);
   for (int round = 0;; ++round) {
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
@@ -722,7 +722,7 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   // at 4x32x4096 over the persistent balanced order, which with 5.3 rounds
   // per slot leaves the last rounds uneven), else head by head (L2 sharing).
   const int grid = p.ntiles;
-  p.lpt = CAUSAL && sorted_order(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), kThreads8,
+  p.lpt = !CAUSAL ? 0 : sorted_order(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), kThreads8,
                                  p.nbh, p.nq);
   hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), dim3(grid), dim3(kThreads8), 0, stream, p, a.bias,
                      reinterpret_cast<const float*>(w + L.sk));

@@ -46,12 +46,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 712088245,
-              "sha256": "7d9896cb2c2b352bdb642ca683d3906401a98889d81d4e5a8fd52ba4963405ab"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 344958859,
-             "sha256": "d21b85f617e8aa74c194aa640f22d66b26a463b09ee6f659b93351623a7cf6f2"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880740068,
-              "sha256": "d21b85f617e8aa74c194aa640f22d66b26a463b09ee6f659b93351623a7cf6f2"},
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 615268844,
+              "sha256": "e042dba7eed10de822d1cbfbddea59740ff952b6cdb5023d713116396fce9014"},
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 579063489,
+             "sha256": "03bd99f81e43610e5ba7a19ebe80c328bc853dd529d3045388dbce13c56208d6"},
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880733777,
+              "sha256": "03bd99f81e43610e5ba7a19ebe80c328bc853dd529d3045388dbce13c56208d6"},
 }
 
 

@@ -13,6 +13,7 @@ raised.
     prep = sage8_prep(q, k, v)                  # 8-bit preparation
     fwd_sage8(prep, causal=False, ...)          # 8-bit forward
     sageattn(q, k, v, causal=False, ...)        # both 8-bit steps
+    sageattn_varlen(q, k, v, cu_seqlens, max_seqlen, ...)  # 8-bit, packed sequences
 
 Tensors are [B, H, N, d] contiguous CUDA (HIP) tensors, d in {64, 96, 128}
 (the 8-bit path and its FP8-QK variant: INT8 scores at 64, 96, 128; FP8 at 64, 128).
@@ -27,8 +28,9 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_strided", "fwd_varlen", "bwd", "attention", "sage8_prep", "fwd_sage8", "sageattn", "AttnError",
-           "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH", "status_str"]
+__all__ = ["fwd", "fwd_strided", "fwd_varlen", "bwd", "attention", "sage8_prep", "sage8_prep_varlen", "fwd_sage8",
+           "sageattn", "sageattn_varlen", "AttnError", "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH",
+           "status_str"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
@@ -82,9 +84,9 @@ def lib() -> ctypes.CDLL:
     L.attn_k_smooth_quant_fp8qk.restype = i
     L.attn_fwd_sage8_fp8qk.argtypes = L.attn_fwd_sage8.argtypes
     L.attn_fwd_sage8_fp8qk.restype = i
-    L.attn_k_smooth_quant_strided.argtypes = [vp, vp, vp, i, i, i, i, i, ll_p, i, vp, sz, vp]
+    L.attn_k_smooth_quant_strided.argtypes = [vp, vp, vp, i, i, i, i, i, ll_p, vp, i, vp, sz, vp]
     L.attn_k_smooth_quant_strided.restype = i
-    L.attn_fwd_sage8_strided.argtypes = [vp, vp, vp, i, i, i, i, ll_p, i, f, vp, i, i, vp]
+    L.attn_fwd_sage8_strided.argtypes = [vp, vp, vp, i, i, i, i, ll_p, vp, i, f, vp, i, i, vp]
     L.attn_fwd_sage8_strided.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
@@ -250,6 +252,12 @@ def fwd_strided(q, k, v, causal=False, scale=None, out_dtype=None, return_lse=Fa
     return (o, lse) if return_lse else o
 
 
+def _check_cu(cu_seqlens, device):
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.device != device or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+
+
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False):
     """Fused attention forward on packed sequences: q, k, v [total,H,d] (d
     contiguous), cu_seqlens int32 [B+1] on the device (sequence b is tokens
@@ -259,9 +267,7 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dt
     _check_views((q, k, v), 3)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
-    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
-            or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous()):
-        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    _check_cu(cu_seqlens, q.device)
     total, H, d = q.shape
     B = cu_seqlens.numel() - 1
     out_dtype = q.dtype if out_dtype is None else out_dtype
@@ -280,11 +286,14 @@ class Sage8Prepared:
     """Workspace written by the 8-bit preparation, with the shape it was
     prepared for (the forward must use the same shape)."""
 
-    def __init__(self, workspace, shape, in_dtype, qk="int8"):
+    def __init__(self, workspace, shape, in_dtype, qk="int8", cu_seqlens=None, total=None):
         self.workspace = workspace
         self.shape = tuple(shape)
         self.in_dtype = in_dtype
         self.qk = qk  # "int8", or "fp8" for the FP8-QK variant
+        # packed sequences: the int32 [B+1] offsets and the packed token count
+        self.cu_seqlens = cu_seqlens
+        self.total = total
 
 
 _QK_FORMAT = {"int8": 0, "fp8": 1}
@@ -320,25 +329,62 @@ def sage8_prep(q, k, v, workspace=None, qk="int8"):
         else:
             fn = L.attn_k_smooth_quant_strided
             arr = (ctypes.c_longlong * 9)(*[int(t.stride(i)) for t in (q, k, v) for i in range(3)])
-            st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d, arr, _QK_FORMAT[qk],
+            st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d, arr, None, _QK_FORMAT[qk],
                     _ptr(workspace), workspace.numel(), _stream(q.device))
     if st != 0:
         raise AttnError(st, fn.__name__)
     return Sage8Prepared(workspace, (B, H, N, d), q.dtype, qk)
 
 
+def sage8_prep_varlen(q, k, v, cu_seqlens, max_seqlen, workspace=None, qk="int8"):
+    """8-bit preparation of packed sequences: q, k, v [total,H,d] (d
+    contiguous), cu_seqlens int32 [B+1] on the device (sequence b is tokens
+    cu_seqlens[b] .. cu_seqlens[b+1]-1), max_seqlen the longest length.  Each
+    sequence is prepared on its own (its K mean, V scales and 64-row blocks),
+    into slot b of a [B,H,max_seqlen,d] workspace."""
+    if qk not in _QK_FORMAT:
+        raise ValueError('qk must be "int8" or "fp8"')
+    _check_views((q, k, v), 3)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    _check_cu(cu_seqlens, q.device)
+    total, H, d = q.shape
+    B, N = cu_seqlens.numel() - 1, int(max_seqlen)
+    L = lib()
+    need = L.attn_sage8_workspace_size(B, H, N, d)
+    if need == 0:
+        raise AttnError(2, "attn_sage8_workspace_size")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    fn = L.attn_k_smooth_quant_strided
+    arr = (ctypes.c_longlong * 9)(*[x for t in (q, k, v) for x in (0, int(t.stride(1)), int(t.stride(0)))])
+    with torch.cuda.device(q.device):
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], B, H, N, d, arr, _ptr(cu_seqlens), _QK_FORMAT[qk],
+                _ptr(workspace), workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+    return Sage8Prepared(workspace, (B, H, N, d), q.dtype, qk, cu_seqlens=cu_seqlens, total=total)
+
+
 def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtype=None,
               return_lse=False, layout_like=None):
     """8-bit fused forward from a prepared workspace.  O is contiguous
     [B,H,N,d], or has the layout of the logical [B,H,N,d] tensor layout_like
-    (torch.empty_like, so a token-major view gives a token-major O)."""
+    (torch.empty_like, so a token-major view gives a token-major O).  After
+    sage8_prep_varlen, O is packed [total,H,d] and takes no bias; the LSE is
+    [B,H,max_seqlen] either way."""
     B, H, N, d = prep.shape
     dev = prep.workspace.device
+    packed = prep.cu_seqlens is not None
+    if packed and (bias is not None or layout_like is not None):
+        raise ValueError("packed sequences take neither a bias nor layout_like")
     bias = _check_bias(bias, B, H, N, dev)
     out_dtype = prep.in_dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if layout_like is not None:
+    if packed:
+        o = torch.empty((prep.total, H, d), dtype=out_dtype, device=dev)
+    elif layout_like is not None:
         if tuple(layout_like.shape) != (B, H, N, d):
             raise ValueError("layout_like must have the prepared [B,H,N,d] shape")
         o = torch.empty_like(layout_like, dtype=out_dtype, device=dev)
@@ -346,15 +392,17 @@ def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtyp
         o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
     with torch.cuda.device(dev):
-        if o.is_contiguous():
+        if o.is_contiguous() and not packed:
             fn = lib().attn_fwd_sage8_fp8qk if prep.qk == "fp8" else lib().attn_fwd_sage8
             st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
                     _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
         else:
             fn = lib().attn_fwd_sage8_strided
-            arr = (ctypes.c_longlong * 3)(*[int(o.stride(i)) for i in range(3)])
-            st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, arr, int(bool(causal)), float(scale),
-                    _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _QK_FORMAT[prep.qk], _stream(dev))
+            ost = (0, o.stride(1), o.stride(0)) if packed else (o.stride(0), o.stride(1), o.stride(2))
+            arr = (ctypes.c_longlong * 3)(*[int(x) for x in ost])
+            st = fn(_ptr(prep.workspace), _ptr(o), _ptr(lse), B, H, N, d, arr, _ptr(prep.cu_seqlens),
+                    int(bool(causal)), float(scale), _ptr(bias), _DTYPE_CODE.get(out_dtype, -1),
+                    _QK_FORMAT[prep.qk], _stream(dev))
     if st != 0:
         raise AttnError(st, fn.__name__)
     return (o, lse) if return_lse else o
@@ -376,6 +424,15 @@ def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, retur
     if tensor_layout == "NHD":
         return (res[0].transpose(1, 2), res[1]) if return_lse else res.transpose(1, 2)
     return res
+
+
+def sageattn_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False,
+                    qk="int8"):
+    """8-bit attention on packed sequences in one call: q, k, v [total,H,d],
+    cu_seqlens int32 [B+1] on the device, max_seqlen the longest length.  O
+    is [total,H,d]; each sequence attends only within itself."""
+    prep = sage8_prep_varlen(q, k, v, cu_seqlens, max_seqlen, qk=qk)
+    return fwd_sage8(prep, causal=causal, scale=scale, out_dtype=out_dtype, return_lse=return_lse)
 
 
 def sage8_workspace_views(prep: Sage8Prepared) -> dict:

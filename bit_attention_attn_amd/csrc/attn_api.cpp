@@ -156,8 +156,8 @@ attn_status check_strides(const long long* st, int n, int N, int d, int extra) {
 }
 
 attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int B, int H, int N, int d,
-                  const long long* strides, void* workspace, size_t workspace_bytes, void* stream,
-                  bool qk_fp8) {
+                  const long long* strides, const int* cu_seqlens, void* workspace, size_t workspace_bytes,
+                  void* stream, bool qk_fp8) {
   if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
   attn_status s = check_shape(B, H, N, d);
   if (s != ATTN_OK) return s;
@@ -167,6 +167,7 @@ attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int
   if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
   if (workspace_bytes < attn::sage8_layout(B, H, N, d).total) return ATTN_ERR_WORKSPACE;
+  if (cu_seqlens != nullptr && !aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
   int64_t st[9];
   if (strides != nullptr) {
     // the column statistics read whole 256-row chunks, up to 255 rows past N
@@ -176,14 +177,15 @@ attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int
   }
   s = check_device();
   if (s != ATTN_OK) return s;
-  if (attn::launch_sage8_prep(q, k, v, in_dtype == ATTN_DTYPE_BF16, B, H, N, d, strides ? st : nullptr, workspace,
-                              static_cast<hipStream_t>(stream), qk_fp8) != hipSuccess)
+  if (attn::launch_sage8_prep(q, k, v, in_dtype == ATTN_DTYPE_BF16, B, H, N, d, strides ? st : nullptr, cu_seqlens,
+                              workspace, static_cast<hipStream_t>(stream), qk_fp8) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
 attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N, int d, int causal, float scale,
-                 const float* bias, int out_dtype, const long long* o_strides, void* stream, bool qk_fp8) {
+                 const float* bias, int out_dtype, const long long* o_strides, const int* cu_seqlens, void* stream,
+                 bool qk_fp8) {
   if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
   attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
   if (s != ATTN_OK) return s;
@@ -191,6 +193,8 @@ attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N
   if (out_dtype != ATTN_DTYPE_F16 && out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32)
     return ATTN_ERR_DTYPE;
   if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens != nullptr && bias != nullptr) return ATTN_ERR_ARG;
+  if (cu_seqlens != nullptr && !aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
   if (o_strides != nullptr) {
     s = check_strides(o_strides, 1, N, d, 0);
     if (s != ATTN_OK) return s;
@@ -204,6 +208,7 @@ attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N
     a.general = true;
     for (int i = 0; i < 3; ++i) a.strides[9 + i] = o_strides[i];
   }
+  a.cu = cu_seqlens;
   if (attn::launch_fwd_sage8(workspace, a, static_cast<hipStream_t>(stream), qk_fp8) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -253,39 +258,39 @@ int attn_sage8_workspace_layout(int B, int H, int N, int d, size_t* out, int n) 
 
 attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
                                 int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
-  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, workspace, workspace_bytes, stream, false);
+  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, nullptr, workspace, workspace_bytes, stream, false);
 }
 
 attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
                                       int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
-  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, workspace, workspace_bytes, stream, true);
+  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, nullptr, workspace, workspace_bytes, stream, true);
 }
 
 attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
                            int causal, float scale, const float* bias, int out_dtype, void* stream) {
-  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, nullptr, stream, false);
+  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, nullptr, nullptr, stream, false);
 }
 
 attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
                                  int causal, float scale, const float* bias, int out_dtype, void* stream) {
-  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, nullptr, stream, true);
+  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, nullptr, nullptr, stream, true);
 }
 
 attn_status attn_k_smooth_quant_strided(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
-                                        int N, int d, const long long* strides, int qk_format, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+                                        int N, int d, const long long* strides, const int* cu_seqlens,
+                                        int qk_format, void* workspace, size_t workspace_bytes, void* stream) {
   if (strides == nullptr) return ATTN_ERR_NULL;
   if (qk_format != ATTN_QK_INT8 && qk_format != ATTN_QK_FP8) return ATTN_ERR_ARG;
-  return prep8(q, k, v, in_dtype, B, H, N, d, strides, workspace, workspace_bytes, stream,
+  return prep8(q, k, v, in_dtype, B, H, N, d, strides, cu_seqlens, workspace, workspace_bytes, stream,
                qk_format == ATTN_QK_FP8);
 }
 
 attn_status attn_fwd_sage8_strided(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
-                                   const long long* o_strides, int causal, float scale, const float* bias,
-                                   int out_dtype, int qk_format, void* stream) {
+                                   const long long* o_strides, const int* cu_seqlens, int causal, float scale,
+                                   const float* bias, int out_dtype, int qk_format, void* stream) {
   if (o_strides == nullptr) return ATTN_ERR_NULL;
   if (qk_format != ATTN_QK_INT8 && qk_format != ATTN_QK_FP8) return ATTN_ERR_ARG;
-  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, o_strides, stream,
+  return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, o_strides, cu_seqlens, stream,
               qk_format == ATTN_QK_FP8);
 }
 

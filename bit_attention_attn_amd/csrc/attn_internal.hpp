@@ -84,10 +84,14 @@ Sage8Layout sage8_layout(int B, int H, int N, int d);
 // of INT8; the forward must be told the format the preparation wrote.
 // strides: element strides (batch, head, token) of q, k, v with d
 // contiguous (9 values); nullptr for contiguous [B,H,N,d].
+// cu (nullable, device int32 [B+1]): packed sequences along the token axis
+// (the batch strides are then unused); each fills its own workspace slot.
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H,
-                             int N, int d, const int64_t* strides, void* ws, hipStream_t stream, bool qk_fp8);
+                             int N, int d, const int64_t* strides, const int* cu, void* ws, hipStream_t stream,
+                             bool qk_fp8);
 // O is written with the element strides a.strides[9..11] (batch, head,
-// token) when a.general, else contiguous [B,H,N,d].
+// token) when a.general, else contiguous [B,H,N,d].  With a.cu (packed
+// sequences, no bias) batch entry b writes its rows from token a.cu[b].
 hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream, bool qk_fp8);
 
 }  // namespace attn

@@ -85,10 +85,28 @@ __device__ __forceinline__ int key_pos(int k) {
 
 // ---- colstats: grid (nchunk, B*H), prep_threads<D>() threads --------------------------
 // Input layout: element strides (batch, head, token) of q, k, v, d contiguous.
+// cu (nullable, device int32 [B+1]) packs the sequences along the token axis:
+// batch entry b is tokens cu[b] .. cu[b+1]-1 (at most N of them), and every
+// statistic of the recipe (K mean, V channel scales, 64-row blocks) is taken
+// over that sequence alone, so its workspace slot is the one it would get on
+// its own.
 struct PrepIn {
   int H;
   int64_t s[9];
+  const int* cu;
 };
+
+// Sequence of batch entry b: its length (<= N) and the element offset of its
+// first row of tensor t (0: q, 1: k, 2: v) at head h.
+__device__ __forceinline__ int seq_span(const PrepIn& in, int b, int h, int N, int t, int64_t& base) {
+  if (in.cu == nullptr) {
+    base = b * in.s[3 * t] + h * in.s[3 * t + 1];
+    return N;
+  }
+  const int t0 = in.cu[b];
+  base = (int64_t)t0 * in.s[3 * t + 2] + h * in.s[3 * t + 1];
+  return max(0, min(in.cu[b + 1] - t0, N));
+}
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -102,6 +120,9 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
   const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
   const int b = bh / in.H, h = bh - b * in.H;
   const uint32_t ksn = (uint32_t)in.s[5], vsn = (uint32_t)in.s[8];  // token strides
+  int64_t kb0, vb0;
+  const int n_k = seq_span(in, b, h, N, 1, kb0);
+  seq_span(in, b, h, N, 2, vb0);
   double acc[8];
   float mx[8];
 #pragma unroll
@@ -109,12 +130,12 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
     acc[e] = 0.0;
     mx[e] = 0.f;
   }
-  // buffer loads: rows past N read zeros, which change neither the sums nor
-  // the absolute maxima, so the row loop has a fixed trip count
+  // buffer loads: rows past the sequence read zeros, which change neither
+  // the sums nor the absolute maxima, so the row loop has a fixed trip count
   // (the byte offsets stay below 2^32 for rows up to N + kChunk: checked by
   // the caller)
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k + b * in.s[3] + h * in.s[4], (uint32_t)N * ksn * 2);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v + b * in.s[6] + h * in.s[7], (uint32_t)N * vsn * 2);
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k + kb0, (uint32_t)n_k * ksn * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v + vb0, (uint32_t)n_k * vsn * 2);
   const uint32_t kvoff = 2u * (rg * ksn + 8u * ch), vvoff = 2u * (rg * vsn + 8u * ch);  // row rg, chunk ch
   const int n0 = chunk * kChunk;
 #pragma unroll
@@ -156,7 +177,7 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
 template <int D>
 __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
                                                     int nchunk, int N, float* __restrict__ kmean,
-                                                    float* __restrict__ sv, float* __restrict__ vinv) {
+                                                    float* __restrict__ sv, float* __restrict__ vinv, PrepIn in) {
   constexpr int kG = 256 / D;  // chunk groups; the block has kG * D threads
   __shared__ double ssum[kG][D];
   __shared__ float smax[kG][D];
@@ -187,7 +208,9 @@ __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__
       s += ssum[i][c];
       m = fmaxf(m, smax[i][c]);
     }
-    kmean[(size_t)bh * D + c] = (float)(s / (double)N);
+    int64_t base;
+    const int n = seq_span(in, bh / in.H, 0, N, 1, base);
+    kmean[(size_t)bh * D + c] = n > 0 ? (float)(s / (double)n) : 0.f;
     sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
     vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
   }
@@ -238,9 +261,13 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
   const int b = bh / in.H, h = bh - b * in.H;
-  const uint16_t* qh = q + b * in.s[0] + h * in.s[1];
-  const uint16_t* kh = k + b * in.s[3] + h * in.s[4];
-  const uint16_t* vh = v + b * in.s[6] + h * in.s[7];
+  int64_t qb0, kb0, vb0;
+  const int n_seq = seq_span(in, b, h, N, 0, qb0);
+  seq_span(in, b, h, N, 1, kb0);
+  seq_span(in, b, h, N, 2, vb0);
+  const uint16_t* qh = q + qb0;
+  const uint16_t* kh = k + kb0;
+  const uint16_t* vh = v + vb0;
   const size_t headp = (size_t)bh * np * D;
   const int n0 = blk * kQB;
 
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   for (int i = 0; i < kPass; ++i) {
     const int r = rg + i * kRows, n = n0 + r;
     u32x4_t qx = {0u, 0u, 0u, 0u}, kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (n < N) {
+    if (n < n_seq) {
       qx = *(const u32x4_t*)(qh + n * in.s[2] + ch * 8);
       kx = *(const u32x4_t*)(kh + n * in.s[5] + ch * 8);
       vx = *(const u32x4_t*)(vh + n * in.s[8] + ch * 8);
@@ -267,12 +294,12 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
       const uint16_t kb = (uint16_t)(kx[e >> 1] >> (16 * (e & 1)));
       const uint16_t vb = (uint16_t)(vx[e >> 1] >> (16 * (e & 1)));
       xq[i][e] = in_to_f32<BF16>(qb);
-      xk[i][e] = n < N ? in_to_f32<BF16>(kb) - km[e] : 0.f;
+      xk[i][e] = n < n_seq ? in_to_f32<BF16>(kb) - km[e] : 0.f;
       aq = fmaxf(aq, fabsf(xq[i][e]));
       ak = fmaxf(ak, fabsf(xk[i][e]));
       // V code, byte-scattered into the transposed tile
       const float t = in_to_f32<BF16>(vb) * vi[e];
-      const uint32_t code = n < N ? (__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false) & 0xFF) : 0u;
+      const uint32_t code = n < n_seq ? (__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false) & 0xFF) : 0u;
       vt[ch * 8 + e][key_pos(r)] = (uint8_t)code;
     }
   }
@@ -312,10 +339,11 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
 
 template <int D, bool BF16, bool QKFP8>
 hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, int N, const int64_t* strides,
-                     void* ws, hipStream_t stream) {
+                     const int* cu, void* ws, hipStream_t stream) {
   const Sage8Layout L = sage8_layout(B, H, N, D);
   PrepIn in;
   in.H = H;
+  in.cu = cu;
   for (int t = 0; t < 3; ++t) {
     in.s[3 * t + 0] = strides ? strides[3 * t + 0] : (int64_t)H * N * D;
     in.s[3 * t + 1] = strides ? strides[3 * t + 1] : (int64_t)N * D;
@@ -330,7 +358,7 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
   hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3((256 / D) * D), 0, stream,
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
-                     reinterpret_cast<float*>(w + L.vinv));
+                     reinterpret_cast<float*>(w + L.vinv), in);
   hipLaunchKernelGGL((sage8_quant<D, BF16, QKFP8>), dim3(L.nblk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), N, np, L.nblk,
@@ -364,6 +392,7 @@ struct Fwd8Params {
   int H;
   int64_t os[3];  // element strides (batch, head, token) of O
   int lpt;        // causal: items heaviest first across the heads (work_queue)
+  const int* cu;  // VARLEN: packed sequences, device int32 [B+1]
 };
 
 constexpr int kNW8 = 4;                // waves per workgroup
@@ -399,7 +428,10 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // which do not share the in-order vector-load counter with the K/V prefetch.
 // QKFP8: Qq and Kq hold e4m3 codes (the FP8-QK variant) and S^T = Kq Qq^T
 // runs on the FP8 32x32x64 instruction, with no offset on the accumulators.
-template <int D, bool CAUSAL, bool BIAS, bool QKFP8>
+// VARLEN: batch entry b is the packed sequence of tokens cu[b] .. cu[b+1]-1
+// (its workspace slot prepared from that sequence alone): its length bounds
+// the keys and rows, and its rows of O start at token cu[b].
+template <int D, bool CAUSAL, bool BIAS, bool QKFP8, bool VARLEN>
 __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const float* __restrict__ bias,
                                                             const float* __restrict__ sk) {
   using S = Fwd8Smem<D>;
@@ -426,8 +458,9 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
   const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
-  const int N = p.N;
+  const int N = VARLEN ? max(0, min(p.cu[bh / p.H + 1] - p.cu[bh / p.H], p.N)) : p.N;
   const int q0 = qt * kBM8;
+  if (VARLEN && q0 >= N) continue;  // past a shorter sequence's end
   const int qw0 = q0 + wave * 32;
   const size_t headp = (size_t)bh * p.np * D;
   const int8_t* __restrict__ Qq = p.qq + headp;
@@ -662,14 +695,15 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
     }
     dot = xor32_sum(dot);
     if (hf == 0 && qi < N)
-      p.lse[(size_t)bh * N + qi] =
+      p.lse[(size_t)bh * p.N + qi] =
           l_tot > 0.f ? (m_run + __log2f(l_tot) - kPlog + c * (sqw * dot)) * kLn2 : -INFINITY;
   }
   // lane (l32, hf) holds d = 32dt + 8g + 4hf + u of query qi: 16-byte (fp32)
   // or 8-byte (fp16 / bf16) stores straight from the accumulators
   const float* svh = p.sv + (size_t)bh * D;
   const int ob = bh / p.H;
-  const int64_t orow = ob * p.os[0] + (bh - ob * p.H) * p.os[1] + (int64_t)qi * p.os[2];
+  const int64_t orow = (VARLEN ? (int64_t)p.cu[ob] * p.os[2] : ob * p.os[0]) + (bh - ob * p.H) * p.os[1] +
+                       (int64_t)qi * p.os[2];
   if (qi < N)
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -690,7 +724,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   }  // work items
 }
 
-template <int D, bool CAUSAL, bool BIAS, bool QKFP8>
+template <int D, bool CAUSAL, bool BIAS, bool QKFP8, bool VARLEN = false>
 hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   const Sage8Layout L = sage8_layout(a.B, a.H, a.N, D);
   const char* w = static_cast<const char*>(ws);
@@ -717,14 +751,16 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
   p.os[0] = a.general ? a.strides[9] : (int64_t)a.H * a.N * D;
   p.os[1] = a.general ? a.strides[10] : (int64_t)a.N * D;
   p.os[2] = a.general ? a.strides[11] : D;
+  p.cu = a.cu;
   // One workgroup per tile.  Causal tiles differ in cost: with few items per
   // resident slot they start heaviest first across the heads (measured +10%
   // at 4x32x4096 over the persistent balanced order, which with 5.3 rounds
   // per slot leaves the last rounds uneven), else head by head (L2 sharing).
   const int grid = p.ntiles;
-  p.lpt = !CAUSAL ? 0 : sorted_order(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), kThreads8,
-                                 p.nbh, p.nq);
-  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, BIAS, QKFP8>), dim3(grid), dim3(kThreads8), 0, stream, p, a.bias,
+  p.lpt = !CAUSAL ? 0
+                  : sorted_order(reinterpret_cast<const void*>(&fwd8_kernel<D, CAUSAL, BIAS, QKFP8, VARLEN>),
+                                 kThreads8, p.nbh, p.nq);
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, BIAS, QKFP8, VARLEN>), dim3(grid), dim3(kThreads8), 0, stream, p, a.bias,
                      reinterpret_cast<const float*>(w + L.sk));
   return hipGetLastError();
 }
@@ -734,25 +770,28 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
 namespace {
 template <bool QKFP8>
 hipError_t prep_q(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
-                  const int64_t* st, void* ws, hipStream_t stream) {
-  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8>(q, k, v, B, H, N, st, ws, stream)
-                           : prep_impl<64, false, QKFP8>(q, k, v, B, H, N, st, ws, stream);
-  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8>(q, k, v, B, H, N, st, ws, stream)
-                           : prep_impl<96, false, QKFP8>(q, k, v, B, H, N, st, ws, stream);
-  return bf16 ? prep_impl<128, true, QKFP8>(q, k, v, B, H, N, st, ws, stream)
-              : prep_impl<128, false, QKFP8>(q, k, v, B, H, N, st, ws, stream);
+                  const int64_t* st, const int* cu, void* ws, hipStream_t stream) {
+  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream)
+                           : prep_impl<64, false, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream);
+  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream)
+                           : prep_impl<96, false, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream);
+  return bf16 ? prep_impl<128, true, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream)
+              : prep_impl<128, false, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream);
 }
 }  // namespace
 
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
-                             const int64_t* strides, void* ws, hipStream_t stream, bool qk_fp8) {
-  return qk_fp8 ? prep_q<true>(q, k, v, bf16, B, H, N, d, strides, ws, stream)
-                : prep_q<false>(q, k, v, bf16, B, H, N, d, strides, ws, stream);
+                             const int64_t* strides, const int* cu, void* ws, hipStream_t stream, bool qk_fp8) {
+  return qk_fp8 ? prep_q<true>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream)
+                : prep_q<false>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream);
 }
 
 namespace {
 template <int D, bool QKFP8>
 hipError_t fwd8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  // packed sequences take no block bias (rejected by the caller)
+  if (a.cu) return a.causal ? fwd8_impl<D, true, false, QKFP8, true>(ws, a, stream)
+                            : fwd8_impl<D, false, false, QKFP8, true>(ws, a, stream);
   if (a.bias) return a.causal ? fwd8_impl<D, true, true, QKFP8>(ws, a, stream)
                               : fwd8_impl<D, false, true, QKFP8>(ws, a, stream);
   return a.causal ? fwd8_impl<D, true, false, QKFP8>(ws, a, stream) : fwd8_impl<D, false, false, QKFP8>(ws, a, stream);

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef enum {
     ATTN_OK = 0,
@@ -226,19 +226,33 @@ attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int
  *             statistics read whole 256-token chunks; rows past N read as 0).
  *  o_strides  host array of 3 element strides (batch, head, token) of o,
  *             with the same rules (without the 256-token margin).
- *  The LSE stays [B,H,N] contiguous.  Other arguments and errors as for
- *  attn_k_smooth_quant and attn_fwd_sage8; a NULL stride array is
- *  ATTN_ERR_NULL, an unknown qk_format ATTN_ERR_ARG.
+ *  cu_seqlens nullable device int32 [B+1]: packed sequences, as for
+ *             attn_fwd_strided_f16.  Sequence b is tokens cu_seqlens[b] ..
+ *             cu_seqlens[b+1]-1 of the token axis of q, k, v and o (the
+ *             batch strides are then unused) and N is the longest length.
+ *             The preparation treats each sequence as a batch entry of its
+ *             own: K mean, V channel scales and the 64-row Q/K blocks are
+ *             taken over that sequence alone, so its workspace slot and its
+ *             rows of O are bit for bit those of a separate call on it.  The
+ *             values are read on the device and not validated (non-decreasing,
+ *             lengths <= N; longer lengths are clamped to N); a length of 0 is
+ *             allowed.  Both calls must get the same array; the forward then
+ *             takes no bias (ATTN_ERR_ARG).
+ *  The LSE stays [B,H,N] contiguous (row b,h,i for i below sequence b's
+ *  length).  Other arguments and errors as for attn_k_smooth_quant and
+ *  attn_fwd_sage8; a NULL stride array is ATTN_ERR_NULL, an unknown
+ *  qk_format ATTN_ERR_ARG, a misaligned cu_seqlens ATTN_ERR_ALIGN.
  */
 attn_status attn_k_smooth_quant_strided(const void* q, const void* k, const void* v,
                                         int in_dtype, int B, int H, int N, int d,
-                                        const long long* strides, int qk_format,
-                                        void* workspace, size_t workspace_bytes,
-                                        void* stream);
+                                        const long long* strides, const int* cu_seqlens,
+                                        int qk_format, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 attn_status attn_fwd_sage8_strided(const void* workspace, void* o, float* lse, int B,
                                    int H, int N, int d, const long long* o_strides,
-                                   int causal, float scale, const float* bias,
-                                   int out_dtype, int qk_format, void* stream);
+                                   const int* cu_seqlens, int causal, float scale,
+                                   const float* bias, int out_dtype, int qk_format,
+                                   void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd_f16/bf16

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
             "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 6
+    assert L.attn_abi_version() == 7
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -178,9 +178,9 @@ def test_sage8_strided_validation():
     nhd = [N * H * d, d, H * d] * 3
     prep = L.attn_k_smooth_quant_strided
 
-    def p(st, fmt=0, dd=d, ws=FAKE, nb=need, q=FAKE):
+    def p(st, fmt=0, dd=d, ws=FAKE, nb=need, q=FAKE, cu=None):
         arr = (ll * 9)(*st) if st is not None else None
-        return prep(q, FAKE, FAKE, BF16, B, H, N, dd, arr, fmt, ws, nb, None)
+        return prep(q, FAKE, FAKE, BF16, B, H, N, dd, arr, cu, fmt, ws, nb, None)
 
     assert p(None) == E_NULL
     assert p(contig, q=None) == E_NULL
@@ -192,11 +192,12 @@ def test_sage8_strided_validation():
     assert p([-8] + nhd[1:]) == E_ARG
     big = (1 << 31) // (N + 256) // 8 * 8 + 8          # (N + 256) rows no longer fit 32-bit byte offsets
     assert p(nhd[:5] + [big] + nhd[6:]) == E_SHAPE
+    assert p(nhd, cu=FAKE + 2) == E_ALIGN             # cu_seqlens not 4-byte aligned
     fwd8 = L.attn_fwd_sage8_strided
 
-    def f(st, fmt=0, dd=d, o=FAKE):
+    def f(st, fmt=0, dd=d, o=FAKE, cu=None, bias=None):
         arr = (ll * 3)(*st) if st is not None else None
-        return fwd8(FAKE, o, None, B, H, N, dd, arr, 0, 0.125, None, BF16, fmt, None)
+        return fwd8(FAKE, o, None, B, H, N, dd, arr, cu, 0, 0.125, bias, BF16, fmt, None)
 
     assert f(None) == E_NULL
     assert f([N * H * d, d, H * d], o=None) == E_NULL
@@ -204,3 +205,5 @@ def test_sage8_strided_validation():
     assert f([N * H * d, d, 8]) == E_ARG              # token stride below d
     assert f([N * H * d, d + 2, H * d]) == E_ALIGN
     assert f([N * H * d, d, H * d], fmt=1, dd=96) == E_HEADDIM
+    assert f([0, d, H * d], cu=FAKE, bias=FAKE) == E_ARG  # packed sequences take no bias
+    assert f([0, d, H * d], cu=FAKE + 2) == E_ALIGN

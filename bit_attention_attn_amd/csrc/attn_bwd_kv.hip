@@ -21,15 +21,21 @@
 // half to the zeroed output with one atomic add (two addends on zero, so the
 // result does not depend on their order).
 //
+// The mask is applied only in halves that the causal diagonal or the ends
+// of the sequence cut through, by a second copy of the element loop; the
+// products are shared, so the rest of a half is one straight-line body.
+//
 // The two accumulators (2 x 16 x D/32 registers) plus K, V and the staging
 // registers exceed 256 VGPRs at d = 128, so this file is built without the
-// VGPR-form option: the accumulators live in AGPRs, one wave per SIMD.
+// VGPR-form option: the accumulators live in AGPRs, one wave per SIMD
+// (two at d = 64, where everything fits in 256 registers).
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -62,7 +68,7 @@ struct BwdKParams {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool HAS_BIAS, bool DBIAS>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const float* __restrict__ bias,
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKParams p, const float* __restrict__ bias,
                                                           float* __restrict__ dbias) {
   constexpr int kThreads = 64 * kNWk;
   constexpr int kKS = D / 16;
@@ -137,8 +143,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const fl
       *(u32x4_t*)(ql + buf * kTile + row * kRow + ch * 8) = qst[i];
       *(u32x4_t*)(dl + buf * kTile + row * kRow + ch * 8) = dst[i];
     }
-    // a row with no visible key (LSE = -inf) has P = 0 everywhere
-    if (wave == 0) stat[buf][0][lane] = sst == -INFINITY ? INFINITY : sst * kLog2e;
+    // -LSE in base 2 (a row with no visible key, LSE = -inf, keeps -inf:
+    // its P is 0 everywhere)
+    if (wave == 0) stat[buf][0][lane] = sst == -INFINITY ? -INFINITY : -(sst * kLog2e);
     if (wave == 1) stat[buf][1][lane] = sst;
   };
 
@@ -152,48 +159,64 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const fl
   const int tq = 4 * hf + (t16 >> 2);
   const int tcol = 16 * (g16 & 1) + 4 * (t16 & 3);
 
-  // one 32-query half u of staged block jq; returns this lane's sum of dS
-  auto half = [&](int jq, int buf, int u) {
-    const int qs0 = jq * kQBk + 32 * u;
-    const float bl = HAS_BIAS ? bias[((size_t)bh * p.nb + jq) * p.nb + kb] * kLog2e : 0.f;
+  // S and dP of the 32-query half u of staged block buf
+  auto scores = [&](int buf, int u, f32x16_t& s, f32x16_t& dp) {
     const uint16_t* Qs = ql + buf * kTile + (32 * u + l32) * kRow + 8 * hf;
     const uint16_t* Ds = dl + buf * kTile + (32 * u + l32) * kRow + 8 * hf;
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    s = f32x16_t{};
+    dp = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
       s = mfma32x32x16<BF16>(*(const u32x4_t*)(Qs + 16 * kk), kf[kk], s);
       dp = mfma32x32x16<BF16>(*(const u32x4_t*)(Ds + 16 * kk), vf[kk], dp);
     }
-    const bool msk = (CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N || kw0 + 32 > N;
+  };
+  // P and dS of half u packed as the B operands (step t holds queries
+  // 32u + 16t + 4hf + {0..3} and 32u + 16t + 8 + 4hf + {0..3}); returns this
+  // lane's sum of dS.  MASK: zero the pairs the causal mask or the ends of
+  // the sequence hide (P and dS set to 0, so nothing from a hidden row
+  // reaches the sums).
+  auto probs = [&](auto mask_tag, int jq, int buf, int u, float bl, const f32x16_t& s, const f32x16_t& dp,
+                   u32x4_t (&pp)[2], u32x4_t (&pd)[2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int qs0 = jq * kQBk + 32 * u;
     float pr[16], ds[16], dsum = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // rows 32u + 8g + 4hf .. +3 of the block
+      // rows 32u + 8g + 4hf .. +3 of the block (l4: -LSE * log2(e))
       const f32x4_t l4 = *(const f32x4_t*)(&stat[buf][0][32 * u + 8 * g + 4 * hf]);
       const f32x4_t d4 = *(const f32x4_t*)(&stat[buf][1][32 * u + 8 * g + 4 * hf]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        float x = exp2_approx(fmaf(s[r], c, bl - l4[e]));
-        if (msk) {
+        const float x = exp2_approx(fmaf(s[r], c, HAS_BIAS ? bl + l4[e] : l4[e]));
+        float y = x * (dp[r] - d4[e]);
+        float xm = x;
+        if constexpr (MASK) {
           const int q = qs0 + 8 * g + 4 * hf + e;
-          if ((CAUSAL && key > q) || q >= N || key >= N) x = 0.f;
+          const bool hide = (CAUSAL && key > q) || q >= N || key >= N;
+          xm = hide ? 0.f : x;
+          y = hide ? 0.f : y;
         }
-        pr[r] = x;
-        ds[r] = x * (dp[r] - d4[e]);
-        dsum += ds[r];
+        pr[r] = xm;
+        ds[r] = y;
+        dsum += y;
       }
     }
-    // P and dS in the register order of the B operand: step t holds queries
-    // 32u + 16t + 4hf + {0..3} and 32u + 16t + 8 + 4hf + {0..3}
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      u32x4_t pp, pd;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        pp[e >> 1] = pack2<BF16>(pr[8 * t + e], pr[8 * t + e + 1]);
-        pd[e >> 1] = pack2<BF16>(ds[8 * t + e], ds[8 * t + e + 1]);
+        pp[t][e >> 1] = pack2<BF16>(pr[8 * t + e], pr[8 * t + e + 1]);
+        pd[t][e >> 1] = pack2<BF16>(ds[8 * t + e], ds[8 * t + e + 1]);
       }
+    return dsum;
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over half u (dO^T and Q^T by the
+  // transposing LDS read)
+  auto accum = [&](int buf, int u, const u32x4_t (&pp)[2], const u32x4_t (&pd)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       const int rowt = (32 * u + 16 * t + tq) * kRow + tcol;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
@@ -201,10 +224,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const fl
         const uint16_t* qtp = ql + buf * kTile + rowt + 32 * dt;
         const u32x2_t dlo = lds_read_tr16(dtp), dhi = lds_read_tr16(dtp + 8 * kRow);
         const u32x2_t qlo = lds_read_tr16(qtp), qhi = lds_read_tr16(qtp + 8 * kRow);
-        dva[dt] = mfma32x32x16<BF16>(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, pp, dva[dt]);
-        dka[dt] = mfma32x32x16<BF16>(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, pd, dka[dt]);
+        dva[dt] = mfma32x32x16<BF16>(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, pp[t], dva[dt]);
+        dka[dt] = mfma32x32x16<BF16>(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, pd[t], dka[dt]);
       }
     }
+  };
+  // one 32-query half u of staged block jq: the scores, then P and dS
+  // (the masked body only where the causal mask or the ends of the
+  // sequence cut through the half), then the products; returns this
+  // lane's sum of dS
+  auto half = [&](int jq, int buf, int u, bool msk) {
+    const float bl = HAS_BIAS ? bias[((size_t)bh * p.nb + jq) * p.nb + kb] * kLog2e : 0.f;
+    f32x16_t s, dp;
+    u32x4_t pp[2], pd[2];
+    scores(buf, u, s, dp);
+    const float dsum = msk ? probs(std::true_type{}, jq, buf, u, bl, s, dp, pp, pd)
+                           : probs(std::false_type{}, jq, buf, u, bl, s, dp, pp, pd);
+    accum(buf, u, pp, pd);
     return dsum;
   };
 
@@ -224,7 +260,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKParams p, const fl
       const int qs0 = jq * kQBk + 32 * u;
       const bool live = wave_has_keys && qs0 < N && !(CAUSAL && qs0 + 31 < kw0) &&
                         (!HAS_BIAS || bias[((size_t)bh * p.nb + jq) * p.nb + kb] != -INFINITY);
-      if (live) dsum += half(jq, buf, u);
+      const bool msk = (CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N || kw0 + 32 > N;
+      if (live) dsum += half(jq, buf, u, msk);
     }
     if constexpr (DBIAS) {
       // sum over the wave, then one add per wave to the zeroed output

@@ -21,9 +21,12 @@
 // half to the zeroed output with one atomic add (two addends on zero, so the
 // result does not depend on their order).
 //
-// The mask is applied only in halves that the causal diagonal or the ends
-// of the sequence cut through, by a second copy of the element loop; the
-// products are shared, so the rest of a half is one straight-line body.
+// A block is one straight-line body: the scores of both halves first, then
+// each half's softmax next to the other half's products, so the matrix unit
+// has independent work while the wave computes exponentials.  The mask is
+// applied by a second copy of that body, used only on the blocks that the
+// causal diagonal or the ends of the sequence cut through (the query loop
+// runs in segments, so the copies never alternate inside it).
 //
 // The two accumulators (2 x 16 x D/32 registers) plus K, V and the staging
 // registers exceed 256 VGPRs at d = 128, so this file is built without the
@@ -229,18 +232,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKPara
       }
     }
   };
-  // one 32-query half u of staged block jq: the scores, then P and dS
-  // (the masked body only where the causal mask or the ends of the
-  // sequence cut through the half), then the products; returns this
-  // lane's sum of dS
-  auto half = [&](int jq, int buf, int u, bool msk) {
+  // One staged block of 64 queries, both halves in one straight-line body:
+  // the scores of half 1 are issued before the softmax of half 0, and the
+  // products of half 0 before the softmax of half 1, so the matrix unit has
+  // independent work while the wave computes exponentials.  MASK: the body
+  // for blocks that the causal diagonal or the ends of the sequence cut
+  // through (a half with no visible pair adds zeros).  Returns this lane's
+  // sum of dS.
+  auto block = [&](auto mask_tag, int jq, int buf) {
     const float bl = HAS_BIAS ? bias[((size_t)bh * p.nb + jq) * p.nb + kb] * kLog2e : 0.f;
-    f32x16_t s, dp;
-    u32x4_t pp[2], pd[2];
-    scores(buf, u, s, dp);
-    const float dsum = msk ? probs(std::true_type{}, jq, buf, u, bl, s, dp, pp, pd)
-                           : probs(std::false_type{}, jq, buf, u, bl, s, dp, pp, pd);
-    accum(buf, u, pp, pd);
+    f32x16_t s0, dp0, s1, dp1;
+    u32x4_t pp0[2], pd0[2], pp1[2], pd1[2];
+    scores(buf, 0, s0, dp0);
+    scores(buf, 1, s1, dp1);
+    float dsum = probs(mask_tag, jq, buf, 0, bl, s0, dp0, pp0, pd0);
+    accum(buf, 0, pp0, pd0);
+    dsum += probs(mask_tag, jq, buf, 1, bl, s1, dp1, pp1, pd1);
+    accum(buf, 1, pp1, pd1);
     return dsum;
   };
 
@@ -251,28 +259,37 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKPara
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
   __syncthreads();
-  for (int jq = jq0, buf = 0; jq < nqb; ++jq, buf ^= 1) {
-    const bool more = jq + 1 < nqb;
-    if (more) load_q(jq + 1);
-    float dsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int qs0 = jq * kQBk + 32 * u;
-      const bool live = wave_has_keys && qs0 < N && !(CAUSAL && qs0 + 31 < kw0) &&
+  // The query loop in three segments, each with one body: the blocks on
+  // the causal diagonal of the workgroup's keys (masked), the blocks past
+  // it (unmasked), and a ragged last block (masked); a workgroup whose keys
+  // reach past N masks every block.  The bodies switch only between
+  // segments, never inside the loop.
+  int jm = CAUSAL ? min(jq0 + kBK / kQBk, nqb) : jq0;
+  if (k0 + kBK > N) jm = nqb;
+  const int jt = max(jm, N % kQBk != 0 ? nqb - 1 : nqb);
+  int buf = 0;
+  auto segment = [&](auto mask_tag, int jb, int je) {
+    for (int jq = jb; jq < je; ++jq, buf ^= 1) {
+      const bool more = jq + 1 < nqb;
+      if (more) load_q(jq + 1);
+      const bool live = wave_has_keys && !(CAUSAL && jq * kQBk + kQBk - 1 < kw0) &&
                         (!HAS_BIAS || bias[((size_t)bh * p.nb + jq) * p.nb + kb] != -INFINITY);
-      const bool msk = (CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N || kw0 + 32 > N;
-      if (live) dsum += half(jq, buf, u, msk);
-    }
-    if constexpr (DBIAS) {
-      // sum over the wave, then one add per wave to the zeroed output
+      float dsum = 0.f;
+      if (live) dsum = block(mask_tag, jq, buf);
+      if constexpr (DBIAS) {
+        // sum over the wave, then one add per wave to the zeroed output
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
-      dsum = xor32_sum(dsum);
-      if (lane == 0 && wave_has_keys) atomicAdd(&dbias[((size_t)bh * p.nb + jq) * p.nb + kb], dsum);
+        for (int off = 16; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
+        dsum = xor32_sum(dsum);
+        if (lane == 0 && wave_has_keys) atomicAdd(&dbias[((size_t)bh * p.nb + jq) * p.nb + kb], dsum);
+      }
+      if (more) store_q(buf ^ 1);
+      __syncthreads();
     }
-    if (more) store_q(buf ^ 1);
-    __syncthreads();
-  }
+  };
+  segment(std::true_type{}, jq0, jm);
+  segment(std::false_type{}, jm, jt);
+  segment(std::true_type{}, jt, nqb);
 
   // ---- epilogue: dK = scale * dka, dV = dva; lane (l32, hf) holds d =
   // 32dt + 8g + 4hf .. +3 of key `key`

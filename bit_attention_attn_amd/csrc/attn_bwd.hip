@@ -24,6 +24,8 @@
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace attn {
@@ -182,52 +184,71 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   const int tkey = 4 * hf + (t16 >> 2);
   const int tcol = 16 * (g16 & 1) + 4 * (t16 & 3);
 
-  auto block = [&](int j, int buf) {
-    const float bl = HAS_BIAS ? bias_row[j] * kLog2e : 0.f;
-    const float off = bl - lse2;  // exponent of P: c*S + off
-    const bool msk = (CAUSAL && j == wave_last) || (j + 1) * kBN > N;
+  // S^T and dP^T of key half T (32 keys) of staged block buf
+  auto scores = [&](int buf, int T, f32x16_t& s, f32x16_t& dp) {
+    const uint16_t* Ks = kl + buf * kKTile + (32 * T + l32) * kKRow + 8 * hf;
+    const uint16_t* Vs = vl + buf * kVTile + (32 * T + l32) * kVRow + 8 * hf;
+    s = f32x16_t{};
+    dp = f32x16_t{};
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const uint16_t* Ks = kl + buf * kKTile + (32 * T + l32) * kKRow + 8 * hf;
-      const uint16_t* Vs = vl + buf * kVTile + (32 * T + l32) * kVRow + 8 * hf;
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    for (int kk = 0; kk < kKS; ++kk) {
+      s = mfma32x32x16<BF16>(*(const u32x4_t*)(Ks + 16 * kk), qf[kk], s);
+      dp = mfma32x32x16<BF16>(*(const u32x4_t*)(Vs + 16 * kk), df[kk], dp);
+    }
+  };
+  // dS^T of half T in the register order of the B operand: pb[t] holds keys
+  // 32T + 16t + 4hf + {0..3} and 32T + 16t + 8 + 4hf + {0..3}.  MASK: keys
+  // the causal mask or the end of the sequence hide get dS = 0.
+  auto probs = [&](auto mask_tag, int j, int T, float off, const f32x16_t& s, const f32x16_t& dp,
+                   u32x4_t (&pb)[2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) {
-        s = mfma32x32x16<BF16>(*(const u32x4_t*)(Ks + 16 * kk), qf[kk], s);
-        dp = mfma32x32x16<BF16>(*(const u32x4_t*)(Vs + 16 * kk), df[kk], dp);
-      }
-      // dS^T in the register order of the B operand: pb[t] holds keys
-      // 32T + 16t + 4hf + {0..3} and 32T + 16t + 8 + 4hf + {0..3}
-      u32x4_t pb[2];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int e = 0; e < 8; e += 2) {
+        float ds[2];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float ds[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * t + e + u;
-            float pr = exp2_approx(fmaf(s[r], c, off));
-            if (msk) {
-              const int key = j * kBN + 32 * T + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if ((CAUSAL && key > qi) || key >= N) pr = 0.f;
-            }
-            ds[u] = pr * (dp[r] - dlt);
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * t + e + u;
+          const float pr = exp2_approx(fmaf(s[r], c, off));
+          ds[u] = pr * (dp[r] - dlt);
+          if constexpr (MASK) {
+            const int key = j * kBN + 32 * T + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if ((CAUSAL && key > qi) || key >= N) ds[u] = 0.f;
           }
-          pb[t][e >> 1] = pack2<BF16>(ds[0], ds[1]);
         }
+        pb[t][e >> 1] = pack2<BF16>(ds[0], ds[1]);
+      }
+  };
+  // dQ^T += K^T dS^T over half T (K^T by the transposing LDS read)
+  auto accum = [&](int buf, int T, const u32x4_t (&pb)[2]) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint16_t* kt = kl + buf * kKTile + (32 * T + 16 * t + tkey) * kKRow + tcol;
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* kt = kl + buf * kKTile + (32 * T + 16 * t + tkey) * kKRow + tcol;
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          const u32x2_t lo = lds_read_tr16(kt + 32 * dt);
-          const u32x2_t hi = lds_read_tr16(kt + 32 * dt + 8 * kKRow);
-          const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-          acc[dt] = mfma32x32x16<BF16>(a, pb[t], acc[dt]);
-        }
+      for (int dt = 0; dt < kDT; ++dt) {
+        const u32x2_t lo = lds_read_tr16(kt + 32 * dt);
+        const u32x2_t hi = lds_read_tr16(kt + 32 * dt + 8 * kKRow);
+        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+        acc[dt] = mfma32x32x16<BF16>(a, pb[t], acc[dt]);
       }
     }
+  };
+  // One staged block of 64 keys in one straight-line body: the scores of
+  // both halves first, then each half's softmax next to the other half's
+  // products.  MASK: the body for blocks the causal diagonal or the end of
+  // the sequence cut through.
+  auto block = [&](auto mask_tag, int j, int buf) {
+    const float bl = HAS_BIAS ? bias_row[j] * kLog2e : 0.f;
+    const float off = bl - lse2;  // exponent of P: c*S + off
+    f32x16_t s0, dp0, s1, dp1;
+    u32x4_t pb0[2], pb1[2];
+    scores(buf, 0, s0, dp0);
+    scores(buf, 1, s1, dp1);
+    probs(mask_tag, j, 0, off, s0, dp0, pb0);
+    accum(buf, 0, pb0);
+    probs(mask_tag, j, 1, off, s1, dp1, pb1);
+    accum(buf, 1, pb1);
   };
 
   __builtin_amdgcn_sched_barrier(0);
@@ -235,13 +256,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   store_kv(0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    const bool more = j + 1 < nkb;
-    if (more) load_kv(j + 1);
-    if (wave_has_rows && j <= wave_last && (!HAS_BIAS || bias_row[j] != -INFINITY)) block(j, j & 1);
-    if (more) store_kv((j + 1) & 1);
-    __syncthreads();
-  }
+  // The key loop in two segments, each with one body: the blocks before the
+  // workgroup's causal diagonal (unmasked; all of them without a causal
+  // mask, but a ragged last block), then the rest (masked).  The bodies
+  // switch only between the segments.
+  const int jm = CAUSAL ? min(q0 / kBN, nkb) : (N % kBN != 0 ? nkb - 1 : nkb);
+  auto segment = [&](auto mask_tag, int jb, int je) {
+    for (int j = jb; j < je; ++j) {
+      const bool more = j + 1 < nkb;
+      if (more) load_kv(j + 1);
+      if (wave_has_rows && j <= wave_last && (!HAS_BIAS || bias_row[j] != -INFINITY)) block(mask_tag, j, j & 1);
+      if (more) store_kv((j + 1) & 1);
+      __syncthreads();
+    }
+  };
+  segment(std::false_type{}, 0, jm);
+  segment(std::true_type{}, jm, nkb);
 
   // ---- epilogue: dQ = scale * acc; lane (l32, hf) holds d = 32dt + 8g +
   // 4hf .. +3 of query qi

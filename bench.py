@@ -46,11 +46,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 710299058,
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 710081221,
               "sha256": "e042dba7eed10de822d1cbfbddea59740ff952b6cdb5023d713116396fce9014"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 581571262,
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 581489469,
              "sha256": "671fc2311657d9cac2fce501171ac72388ff21e21af1fe4767749100fe510e67"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880751209,
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880752756,
               "sha256": "671fc2311657d9cac2fce501171ac72388ff21e21af1fe4767749100fe510e67"},
 }
 
@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workload", type=int, default=0,
                     help="profiling mode: run only this workload (1-5) --steps times and print its timing")
-    ap.add_argument("--path", default="bf16", choices=["bf16", "sage8"],
+    ap.add_argument("--path", default="bf16", choices=["bf16", "sage8", "bwd"],
                     help="profiling mode: which path to run")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes")
@@ -169,6 +169,16 @@ def profile_one(args):
     out_dtype = torch.float32 if cfg["out"] == "f32" else None
     if args.path == "bf16":
         fn = lambda: attn.fwd(q, k, v, causal=cfg["causal"], bias=bias, out_dtype=out_dtype)  # noqa: E731
+    elif args.path == "bwd":
+        # the backward (five products: 2.5x the forward's flops) from the
+        # forward's O and LSE, with a seeded dO
+        o, lse = attn.fwd(q, k, v, causal=cfg["causal"], bias=bias, return_lse=True)
+        dout = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(args.workload),
+                           device=dev, dtype=q.dtype)
+        F *= 2.5
+
+        def fn():
+            return attn.bwd(q, k, v, o, dout, lse, causal=cfg["causal"], bias=bias, return_dbias=bias is not None)
     else:
         ws = attn.sage8_prep(q, k, v).workspace
 

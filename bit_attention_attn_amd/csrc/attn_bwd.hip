@@ -21,6 +21,10 @@
 //   dQ^T += K^T dS^T: dS^T goes from the accumulator registers straight into
 //       the B operand, K^T comes from the row-major K tile by the
 //       transposing LDS read (the forward's P V step with K in place of V).
+// A block is one straight-line body (the scores of both halves first, then
+// each half's dS next to the other half's products); the mask is a second
+// copy of that body, used on the blocks past the start of the workgroup's
+// causal diagonal and on a ragged last block.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 

@@ -105,9 +105,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   constexpr int kKS = D / 16;  // k-steps over d
   constexpr int kDT = D / 32;  // 32-row tiles of dQ^T
   constexpr int kCpr = D / 8;  // 16-byte chunks per row
-  // K rows are read both ways: 288-byte rows (d = 128) or 192-byte rows
-  // (d = 64) suit the transposing reads; V rows are read as rows only.
-  constexpr int kKRow = D == 64 ? D + 32 : D + 16;
+  // K rows are read both ways (rows for the scores, transposing reads for
+  // dQ); the padding is the fastest of a sweep of 8 to 40 elements at
+  // d = 128, and also faster than 32 at d = 64.  V rows are read as rows
+  // only.
+  constexpr int kKRow = D == 96 ? D + 16 : D + 24;
   constexpr int kVRow = D + 8;
   constexpr int kKTile = kBN * kKRow, kVTile = kBN * kVRow;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (kKTile + kVTile)];

@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKPara
   constexpr int kDT = D / 32;
   constexpr int kCpr = D / 8;
   // Q and dO rows are read both ways (rows for S and dP, transposing reads
-  // for dK and dV)
-  constexpr int kRow = D == 64 ? D + 32 : D + 16;
+  // for dK and dV); the row padding is the fastest of a sweep of 8 to 64
+  // elements at d = 64 and 128 (fewest bank conflicts across both reads)
+  constexpr int kRow = D == 96 ? D + 16 : D + 24;
   constexpr int kTile = kQBk * kRow;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * kTile];
   __shared__ __attribute__((aligned(16))) float stat[2][2][kQBk];  // [buf][lse2, delta][row]

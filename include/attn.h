@@ -29,7 +29,8 @@
  *    keeps no mutable state between calls and is safe to call from several
  *    host threads (on distinct output buffers).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
- *    stream).  Every argument check runs before any launch: a non-zero
+ *    stream) and may be recorded into a HIP graph: they launch kernels only
+ *    (no allocation, no memset, no host synchronisation).  Every argument check runs before any launch: a non-zero
  *    status means nothing was launched and nothing was written.  Faults of
  *    the device itself surface at stream synchronisation.
  *  - There is no fallback path: an unsupported shape, dtype or device is an

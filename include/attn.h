@@ -30,9 +30,10 @@
  *    host threads (on distinct output buffers).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *    stream) and may be recorded into a HIP graph: they launch kernels only
- *    (no allocation, no memset, no host synchronisation).  Every argument check runs before any launch: a non-zero
- *    status means nothing was launched and nothing was written.  Faults of
- *    the device itself surface at stream synchronisation.
+ *    (no allocation, no memset, no host synchronisation).  Every argument
+ *    check runs before any launch: a non-zero status means nothing was
+ *    launched and nothing was written.  Faults of the device itself surface
+ *    at stream synchronisation.
  *  - There is no fallback path: an unsupported shape, dtype or device is an
  *    error, never a slower materialising implementation (page 3, the
  *    glossary entry's warning about silent fallbacks).

@@ -46,11 +46,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 710081221,
+    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 710497717,
               "sha256": "e042dba7eed10de822d1cbfbddea59740ff952b6cdb5023d713116396fce9014"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 581489469,
+    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 580376390,
              "sha256": "671fc2311657d9cac2fce501171ac72388ff21e21af1fe4767749100fe510e67"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880752756,
+    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880751721,
               "sha256": "671fc2311657d9cac2fce501171ac72388ff21e21af1fe4767749100fe510e67"},
 }
 

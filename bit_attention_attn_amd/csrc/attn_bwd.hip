@@ -107,8 +107,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdQParams p, const floa
   constexpr int kCpr = D / 8;  // 16-byte chunks per row
   // K rows are read both ways (rows for the scores, transposing reads for
   // dQ); the padding is the fastest of a sweep of 8 to 40 elements at
-  // d = 128, and also faster than 32 at d = 64.  V rows are read as rows
-  // only.
+  // d = 128, faster than 32 at d = 64, and 16 beats 24 and 40 at d = 96.
+  // V rows are read as rows only.
   constexpr int kKRow = D == 96 ? D + 16 : D + 24;
   constexpr int kVRow = D + 8;
   constexpr int kKTile = kBN * kKRow, kVTile = kBN * kVRow;

@@ -79,7 +79,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKPara
   constexpr int kCpr = D / 8;
   // Q and dO rows are read both ways (rows for S and dP, transposing reads
   // for dK and dV); the row padding is the fastest of a sweep of 8 to 64
-  // elements at d = 64 and 128 (fewest bank conflicts across both reads)
+  // elements at d = 64 and 128, and of 16, 24 and 40 at d = 96 (fewest bank
+  // conflicts across both reads)
   constexpr int kRow = D == 96 ? D + 16 : D + 24;
   constexpr int kTile = kQBk * kRow;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * kTile];

@@ -96,6 +96,14 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.fwd(q, q, q)
+    # packed sequences: [total,H,d] tensors and int32 offsets on q's device
+    qp = torch.zeros((8, 1, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    for fn in (attn.fwd_varlen, attn.sage8_prep_varlen, attn.sageattn_varlen):
+        with pytest.raises(ValueError):
+            fn(qp, qp, qp, cu, 8)
+    with pytest.raises(ValueError):
+        attn.sage8_prep_varlen(qp, qp, qp, cu, 8, qk="int4")
 
 
 def _strided(fn, strides, q=FAKE, o=FAKE, cu=None, B=1, H=2, N=64, d=64, causal=0, out=BF16):

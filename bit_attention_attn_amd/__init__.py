@@ -252,10 +252,26 @@ def fwd_strided(q, k, v, causal=False, scale=None, out_dtype=None, return_lse=Fa
     return (o, lse) if return_lse else o
 
 
-def _check_cu(cu_seqlens, device):
+def _check_cu(cu_seqlens, device, max_seqlen=None, total=None):
+    """Packed-sequence offsets: a contiguous int32 [B+1] tensor on the device.
+    With max_seqlen and total, also the contract the kernels rely on (they
+    clamp a longer sequence to max_seqlen and would leave the rest of its
+    rows unwritten): offsets non-decreasing from 0 up to at most total,
+    every length at most max_seqlen.  This reads the B+1 offsets back to the
+    host (one small synchronous copy)."""
     if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
             or cu_seqlens.device != device or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2):
         raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    if max_seqlen is None:
+        return
+    if int(max_seqlen) < 1:
+        raise ValueError("max_seqlen must be >= 1")
+    cu = cu_seqlens.cpu()
+    lens = cu[1:] - cu[:-1]
+    if int(cu[0]) < 0 or bool((lens < 0).any()) or int(cu[-1]) > total:
+        raise ValueError("cu_seqlens must be non-decreasing offsets into the packed token axis")
+    if int(lens.max()) > int(max_seqlen):
+        raise ValueError(f"a sequence is longer than max_seqlen ({int(lens.max())} > {int(max_seqlen)})")
 
 
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False):
@@ -267,8 +283,8 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dt
     _check_views((q, k, v), 3)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
-    _check_cu(cu_seqlens, q.device)
     total, H, d = q.shape
+    _check_cu(cu_seqlens, q.device, max_seqlen, total)
     B = cu_seqlens.numel() - 1
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
@@ -347,8 +363,8 @@ def sage8_prep_varlen(q, k, v, cu_seqlens, max_seqlen, workspace=None, qk="int8"
     _check_views((q, k, v), 3)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
-    _check_cu(cu_seqlens, q.device)
     total, H, d = q.shape
+    _check_cu(cu_seqlens, q.device, max_seqlen, total)
     B, N = cu_seqlens.numel() - 1, int(max_seqlen)
     L = lib()
     need = L.attn_sage8_workspace_size(B, H, N, d)

@@ -28,11 +28,23 @@ attn_status check_shape(int B, int H, int N, int d) {
   return ATTN_OK;
 }
 
+// A block bias (or its gradient) is fp32 [B,H,nb,nb], nb = ceil(N/64).  The
+// tensor obeys the per-tensor rule (< 2^31 elements), and the forward kernels
+// address one head's nb*nb values with 32-bit byte offsets through a buffer
+// descriptor, so nb*nb*4 must stay below 2^32 (nb <= 32767, N <= 2,097,088).
+attn_status check_bias_size(int B, int H, int N) {
+  const int64_t nb = ((int64_t)N + 63) / 64;
+  if ((int64_t)B * H * nb * nb >= kMaxElems) return ATTN_ERR_SHAPE;
+  if (nb * nb * 4 >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
 attn_status check_common(void* o, float* lse, int B, int H, int N, int d, int causal, float scale,
                          const float* bias) {
   if (o == nullptr) return ATTN_ERR_NULL;
   attn_status s = check_shape(B, H, N, d);
   if (s != ATTN_OK) return s;
+  if (bias != nullptr && (s = check_bias_size(B, H, N)) != ATTN_OK) return s;
   if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_ARG;
   if (!aligned(o, 16)) return ATTN_ERR_ALIGN;
@@ -76,6 +88,23 @@ attn_status fwd16(bool bf16, const void* q, const void* k, const void* v, void* 
   return ATTN_OK;
 }
 
+// Strides of a strided call (n tensors, 3 strides each): every stride
+// non-negative and a multiple of 8 elements (16-byte rows), token strides at
+// least d, and `extra` rows past N still addressable with 32-bit byte
+// offsets from a head's base.
+attn_status check_strides(const long long* st, int n, int N, int d, int extra) {
+  for (int t = 0; t < n; ++t) {
+    for (int i = 0; i < 3; ++i) {
+      const long long x = st[3 * t + i];
+      if (x < 0 || x > (1LL << 31)) return ATTN_ERR_ARG;
+      if (x % 8 != 0) return ATTN_ERR_ALIGN;
+    }
+    if (st[3 * t + 2] < d) return ATTN_ERR_ARG;
+    if ((long long)(N + extra) * st[3 * t + 2] * 2 >= (1LL << 32)) return ATTN_ERR_SHAPE;
+  }
+  return ATTN_OK;
+}
+
 attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int H, int N, int d, const long long* strides, const int* cu_seqlens, int causal,
                           float scale, int out_dtype, void* stream) {
@@ -86,18 +115,11 @@ attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v
   if (out_dtype != in_dtype && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
   if (cu_seqlens != nullptr && !aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
-  // every stride non-negative and a multiple of 8 elements (16-byte rows),
-  // token strides at least d; a head's rows must be addressable with 32-bit
-  // byte offsets
-  for (int t = 0; t < 4; ++t) {
-    for (int i = 0; i < 3; ++i) {
-      const long long st = strides[3 * t + i];
-      if (st < 0 || st > (1LL << 31)) return ATTN_ERR_ARG;
-      if (st % 8 != 0) return ATTN_ERR_ALIGN;
-    }
-    if (strides[3 * t + 2] < d) return ATTN_ERR_ARG;
-    if ((long long)N * strides[3 * t + 2] * 2 >= (1LL << 32)) return ATTN_ERR_SHAPE;
-  }
+  // the key and value loads of the last block read whole 64-row blocks, up
+  // to 63 rows past N, which must stay addressable with 32-bit byte offsets
+  // from a head's base (the buffer descriptor returns zeros for them)
+  s = check_strides(strides, 4, N, d, 64);
+  if (s != ATTN_OK) return s;
   s = check_device();
   if (s != ATTN_OK) return s;
   attn::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, d, causal, scale,
@@ -124,6 +146,7 @@ attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const 
   const int in_dtype = bf16 ? ATTN_DTYPE_BF16 : ATTN_DTYPE_F16;
   if (grad_dtype != in_dtype && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
   if (o_dtype != in_dtype && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if ((bias != nullptr || dbias != nullptr) && check_bias_size(B, H, N) != ATTN_OK) return ATTN_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_size(B, H, N, d)) return ATTN_ERR_WORKSPACE;
   for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned(ptr, 16)) return ATTN_ERR_ALIGN;
@@ -136,22 +159,6 @@ attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const 
                   grad_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16),
                   o_dtype == ATTN_DTYPE_F32};
   if (attn::launch_bwd16(a, bf16, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
-  return ATTN_OK;
-}
-
-// Strides of a strided 8-bit call: every stride non-negative and a multiple
-// of 8 elements (16-byte rows), token strides at least d, and `extra` rows
-// past N still addressable with 32-bit byte offsets from a head's base.
-attn_status check_strides(const long long* st, int n, int N, int d, int extra) {
-  for (int t = 0; t < n; ++t) {
-    for (int i = 0; i < 3; ++i) {
-      const long long x = st[3 * t + i];
-      if (x < 0 || x > (1LL << 31)) return ATTN_ERR_ARG;
-      if (x % 8 != 0) return ATTN_ERR_ALIGN;
-    }
-    if (st[3 * t + 2] < d) return ATTN_ERR_ARG;
-    if ((long long)(N + extra) * st[3 * t + 2] * 2 >= (1LL << 32)) return ATTN_ERR_SHAPE;
-  }
   return ATTN_OK;
 }
 

@@ -36,7 +36,6 @@
 #include "attn_internal.hpp"
 
 #include <math.h>
-#include <stdlib.h>
 
 #include <atomic>
 
@@ -553,33 +552,19 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tiling per head dimension.  ATTN_FWD16_TILING selects another variant, to
-// compare them on the GPU.  Measured on MI355X (TFLOPS; prefill 4x32x4096 /
+// Tiling per head dimension, measured on MI355X (TFLOPS; prefill 4x32x4096 /
 // long-context 1x32x32768, causal, d = 128; DiT-gated 2x24x16384, d = 64):
-//   d = 128: QS1 NW8 (default) 743 / 1085; QS1 NW4 688 / 1003.  Tried and
+//   d = 128: QS1 NW8 743 / 1085 against QS1 NW4 688 / 1003.  Tried and
 //     dropped: software-pipelined S of block j+1 next to the softmax of block j
 //     (653 / 1030); two wave groups in ping-pong phases (596 / 950: a product
 //     phase has one matrix-issuing wave per SIMD, LDS waits are exposed);
 //     waves staggered by one product (701 / 983, and register spills).
-//   d = 64: QS2 NW4 (default) 936-950; QS1 NW4 854.
-int tiling_override() {
-  static const int v = [] {
-    const char* e = getenv("ATTN_FWD16_TILING");
-    return e ? atoi(e) : -1;
-  }();
-  return v;
-}
-
+//   d = 64: QS2 NW4 936-950 against QS1 NW4 854.
 template <bool BF16, bool CAUSAL, int MODE>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  const int t = tiling_override();
-  if (a.d == 64) {
-    if (t == 1) return launch_impl<64, BF16, CAUSAL, 1, 4, MODE>(a, stream);
-    return launch_impl<64, BF16, CAUSAL, 2, 4, MODE>(a, stream);
-  }
+  if (a.d == 64) return launch_impl<64, BF16, CAUSAL, 2, 4, MODE>(a, stream);
   // d = 96: a 64 x 96 tile is 768 16-byte chunks, which 4 waves split evenly
   if (a.d == 96) return launch_impl<96, BF16, CAUSAL, 1, 4, MODE>(a, stream);
-  if (t == 1) return launch_impl<128, BF16, CAUSAL, 1, 4, MODE>(a, stream);
   return launch_impl<128, BF16, CAUSAL, 1, 8, MODE>(a, stream);
 }
 
@@ -616,11 +601,6 @@ int resident_slots(const void* kernel, int threads) {
 int sorted_order(const void* kernel, int threads, int nbh, int nq, int per_slot) {
   const int slots = resident_slots(kernel, threads);
   if (slots <= 0 || (int64_t)nbh * nq >= (int64_t)per_slot * slots) return 0;
-  static const int forced = [] {
-    const char* e = getenv("ATTN_LPT_GROUP");
-    return e ? atoi(e) : 0;
-  }();
-  if (forced > 0) return forced;
   // heads per group: the smallest power of two with at least two items per
   // slot of an XCD in a group (measured on the 8-bit forward, against one
   // group of all of an XCD's heads: 4x32x4096 +3% and HBM reads 438 MB

@@ -89,6 +89,8 @@ typedef enum {
  *  bias       nullable fp32 [B,H,nb,nb], nb = ceil(N/64): additive logit
  *             (natural-log units, not multiplied by scale) for each
  *             64-query x 64-key block.  -inf entries mask whole blocks.
+ *             With a bias, B*H*nb*nb must be below 2^31 and nb below 32768
+ *             (N <= 2,097,088), else ATTN_ERR_SHAPE.
  *  Products run on the matrix cores with fp32 accumulation; P is rounded
  *  to the input dtype for the P V product.
  */
@@ -111,7 +113,9 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
  *  strides    host array of 12 element strides: for q, k, v, o in turn the
  *             (batch, head, token) strides; d is contiguous.  Each stride is
  *             >= 0 and a multiple of 8 elements (16-byte rows), each token
- *             stride >= d, and N * token stride * 2 < 2^32 bytes.
+ *             stride >= d, and (N + 64) * token stride * 2 < 2^32 bytes
+ *             (the last key block reads whole 64-row blocks; rows past N
+ *             read as zeros).
  *  cu_seqlens nullable device int32 [B+1]: packed sequences.  Sequence b is
  *             tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of the token axis
  *             (the batch strides are then unused) and attends only within
@@ -286,7 +290,8 @@ size_t attn_bwd_workspace_size(int B, int H, int N, int d);
  *             ATTN_DTYPE_F32.  Fully overwritten.
  *  dbias      nullable fp32 [B,H,nb,nb], nb = ceil(N/64): the gradient of
  *             the block bias (also defined when bias is NULL, as the
- *             gradient at bias = 0).  Fully overwritten.
+ *             gradient at bias = 0).  Fully overwritten.  With a bias or
+ *             dbias, nb is bounded as for the forward's bias.
  *  causal, scale, bias  as passed to the forward.
  *  workspace  device buffer of at least attn_bwd_workspace_size bytes,
  *             256-byte aligned; overwritten.

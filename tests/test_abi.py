@@ -215,3 +215,42 @@ def test_sage8_strided_validation():
     assert f([N * H * d, d, H * d], fmt=1, dd=96) == E_HEADDIM
     assert f([0, d, H * d], cu=FAKE, bias=FAKE) == E_ARG  # packed sequences take no bias
     assert f([0, d, H * d], cu=FAKE + 2) == E_ALIGN
+
+
+def test_bias_size_bounds():
+    """A block bias [B,H,nb,nb] is bounded: nb below 32768 (one head's gates
+    addressed with 32-bit byte offsets) and B*H*nb*nb below 2^31 elements.
+    Past either bound every entry point that takes a bias (or its gradient)
+    returns ATTN_ERR_SHAPE instead of reading a wrapped descriptor."""
+    L = attn.lib()
+    n_max = 64 * 32767             # nb = 32767: the largest accepted
+    n_over = n_max + 1             # nb = 32768: nb*nb*4 = 2^32
+    for fn in (L.attn_fwd_bf16, L.attn_fwd_f16):
+        assert _fwd(fn, bias=FAKE, N=n_over, d=64, out=BF16 if fn is L.attn_fwd_bf16 else F16) == E_SHAPE
+        # at the bound the bias check passes and the next check (causal) fails
+        assert _fwd(fn, bias=FAKE, N=n_max, d=64, causal=2,
+                    out=BF16 if fn is L.attn_fwd_bf16 else F16) == E_ARG
+        # 3 heads of 32767^2 gates exceed 2^31 elements
+        assert _fwd(fn, bias=FAKE, H=3, N=n_max, d=64, out=BF16 if fn is L.attn_fwd_bf16 else F16) == E_SHAPE
+        # without a bias the same shape is not limited by it
+        assert _fwd(fn, N=n_over, d=64, causal=2, out=BF16 if fn is L.attn_fwd_bf16 else F16) == E_ARG
+    for fwd8 in (L.attn_fwd_sage8, L.attn_fwd_sage8_fp8qk):
+        assert fwd8(FAKE, FAKE, None, 1, 1, n_over, 64, 0, 0.1, FAKE, BF16, None) == E_SHAPE
+        assert fwd8(FAKE, FAKE, None, 1, 1, n_max, 64, 2, 0.1, FAKE, BF16, None) == E_ARG
+    for name in ("attn_bwd_bf16", "attn_bwd_f16"):
+        fn = getattr(L, name)
+        dt = BF16 if name.endswith("bf16") else F16
+        assert _bwd(fn, dbias=FAKE, B=1, H=1, N=n_over, grad=dt, wsb=1 << 30) == E_SHAPE
+
+
+def test_strided_tail_rows_must_be_addressable():
+    """The 16-bit strided forward reads whole 64-row key blocks, up to 63
+    rows past N: (N + 64) rows of the token stride must fit 32-bit byte
+    offsets, not only N of them."""
+    L = attn.lib()
+    ts = 1 << 20                                   # token stride (elements)
+    N = 2000                                       # N*ts*2 < 2^32 <= (N+64)*ts*2
+    assert N * ts * 2 < (1 << 32) <= (N + 64) * ts * 2
+    good = [0, 64, ts] * 4
+    for name, dt in (("attn_fwd_strided_bf16", BF16), ("attn_fwd_strided_f16", F16)):
+        assert _strided(getattr(L, name), good, N=N, out=dt) == E_SHAPE

@@ -113,3 +113,21 @@ def test_packed_sequences_empty_and_padded_lse():
         s0, s1 = int(cu[b]), int(cu[b + 1])
         seq = [t[s0:s1].transpose(0, 1).unsqueeze(0) for t in x]
         _check(o[s0:s1].transpose(0, 1).unsqueeze(0), None, *seq, True, 1 / math.sqrt(d), f"seq {b}")
+
+
+def test_packed_sequences_longer_than_max_seqlen_are_rejected():
+    """The kernels clamp a sequence to max_seqlen, which would leave the rest
+    of its rows unwritten: the binding checks the offsets first."""
+    H, d = 2, 64
+    x = torch.randn((100, H, d), generator=torch.Generator("cpu").manual_seed(3)).to(torch.bfloat16).to(DEV)
+    cu = torch.tensor([0, 30, 100], dtype=torch.int32, device=DEV)   # lengths 30 and 70
+    for fn in (attn.fwd_varlen, attn.sageattn_varlen):
+        with pytest.raises(ValueError):
+            fn(x, x, x, cu, 64)
+        with pytest.raises(ValueError):
+            fn(x, x, x, torch.tensor([0, 70, 50], dtype=torch.int32, device=DEV), 70)  # decreasing
+        with pytest.raises(ValueError):
+            fn(x, x, x, torch.tensor([0, 70, 101], dtype=torch.int32, device=DEV), 70)  # past the tokens
+    o = attn.fwd_varlen(x, x, x, cu, 70)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()

@@ -2,24 +2,30 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 
-A step is one pass of the whole hot path over the LLM-prefill workload
-(B=4, H=32, N=4096, d=128, causal, bf16 Q/K/V ~ N(0,1), scale 1/sqrt(128),
-bf16 output): the bf16 fused forward, then the 8-bit preparation (K mean,
-INT8 Q/K, e4m3 V into a preallocated workspace) and the 8-bit fused forward
-on the same inputs.  Inputs are resident in device memory before the timed
-region and no cache is flushed between steps.  ``value`` is the attention
-FLOPs the step computes (two forwards, 4*B*H*N^2*d/2 each) divided by the
-step time.  Each kernel launch is bracketed by HIP events on the stream the
-kernels run on (torch's current stream, which the binding passes to the
-library), giving per-kernel averages; ``roofline`` describes the kernel with
-the largest share of the step.  Other workloads are timed after the main loop
-and reported under ``workloads`` (not part of ``value``).
+A step is one launch of the bf16 fused forward on the long-context workload
+(B=1, H=32, N=32768, d=128, causal, bf16 Q/K/V ~ N(0,1), scale 1/sqrt(128),
+bf16 output).  Inputs are resident in device memory before the timed region
+and no cache is flushed between steps.  ``value`` is the step's attention
+FLOPs (4*B*H*N^2*d/2) divided by the step time: the bf16 forward's TFLOPS,
+with ``roofline`` its fraction of the bf16 dense matrix peak.  Each launch is
+bracketed by HIP events on the stream the kernels run on (torch's current
+stream, which the binding passes to the library).
+
+On the same inputs the 8-bit path is then timed (its preparation and its
+forward, 20 launches each after warm-up; INT8 scores with FP8 P and V, the
+FP8-QK variant, and INT8 scores with 16-bit P V) and reported under ``paths``
+with its speedup over the bf16 forward, attention alone and with the
+preparation.  Other workloads follow under ``workloads`` and ``backward``;
+none of them is part of ``value``.
 
 Prints ONE JSON line.  Only one GPU is supported: --gpus above 1 exits.
 
 Extra modes (for profiler runs):
-    --workload W --path bf16|sage8   run one workload's path --steps times
-    --copy-bytes NBYTES              run a plain device copy --steps times
+    --workload W --path bf16|sage8|sage8pv16|bwd  run one workload's path --steps times
+    --copy-bytes NBYTES                 run a plain device copy --steps times
+    --trace-summary CSV [--skip S]      per (kernel, grid) durations of a rocprofv3
+                                        kernel-trace CSV, the first S dispatches of
+                                        each (kernel, grid) left out (warm-up)
 """
 from __future__ import annotations
 
@@ -39,19 +45,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, datasheet
 PEAK_8BIT_TFLOPS = 5000.0   # MI355X dense fp8 / int8 MFMA, datasheet
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 
-# HBM traffic per launch (bytes) from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# runs on the LLM-prefill workload, scaled by the same counters on a plain
+# HBM traffic per launch (bytes) of a kernel on a workload, from rocprofv3
+# --pmc FETCH_SIZE / WRITE_SIZE runs, scaled by the same counters on a plain
 # 1 GiB device copy (FETCH_SIZE reads half the copied bytes: factor 2;
-# WRITE_SIZE reads them exactly: factor 1); profiles/llm-prefill_hbm-traffic.txt.
+# WRITE_SIZE reads them exactly: factor 1); profiles/*_hbm-traffic.txt.
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    "fwd16": {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 710497717,
-              "sha256": "e042dba7eed10de822d1cbfbddea59740ff952b6cdb5023d713116396fce9014"},
-    "fwd8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 580376390,
-             "sha256": "671fc2311657d9cac2fce501171ac72388ff21e21af1fe4767749100fe510e67"},
-    "prep8": {"sources": ["attn_sage8.hip", "attn_common.hpp"], "bytes": 880751721,
-              "sha256": "671fc2311657d9cac2fce501171ac72388ff21e21af1fe4767749100fe510e67"},
+    ("fwd16", 3): {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": None, "sha256": ""},
 }
 
 
@@ -69,6 +70,10 @@ def parse():
                     help="profiling mode: run only this workload (1-5) --steps times and print its timing")
     ap.add_argument("--path", default="bf16", choices=["bf16", "sage8", "bwd"],
                     help="profiling mode: which path to run")
+    ap.add_argument("--trace-summary", default="",
+                    help="print per (kernel, grid) durations of a rocprofv3 kernel-trace CSV and exit")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="with --trace-summary: leave out the first SKIP dispatches of each (kernel, grid)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes")
     return ap.parse_args()
@@ -87,9 +92,9 @@ def sources_sha(files):
     return h.hexdigest()
 
 
-def traffic_for(key):
-    t = TRAFFIC[key]
-    if t["bytes"] is None or t["sha256"] != sources_sha(t["sources"]):
+def traffic_for(kernel, workload):
+    t = TRAFFIC.get((kernel, workload))
+    if t is None or t["bytes"] is None or t["sha256"] != sources_sha(t["sources"]):
         return None
     return t["bytes"]
 
@@ -152,6 +157,7 @@ def cpu_baseline(inp, cfg, seconds):
         done_rows += batch
         batch = min(batch * 2, 4096)
     return dict(value=round(flops / elapsed / 1e12, 6), unit="TFLOPS", cores=oracle.max_threads(), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"{done_rows} random query rows of the {cfg['name']} workload, fp64 three-loop oracle "
                        f"(OpenMP over rows) for {elapsed:.1f} s; flops counted as 4*d per visible key, as on the GPU")
 
@@ -209,12 +215,56 @@ def copy_calibration(args):
                       "GBs_read_plus_write": round(2 * n * 4 / (st["ms_avg"] * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sage8_paths(attn, q, k, v, causal, bias, F, t16_ms, stream):
+    """The 8-bit path on the given inputs: preparation and forward timed
+    separately (20 launches each after 0.1 s of warm-up) for each recipe, with
+    the speedup over the bf16 forward time t16_ms (when given), attention
+    alone and with the preparation (page 1, "SageAttention": the conversion
+    overhead counts)."""
+    res = {}
+    shape = tuple(q.shape)
+    for name, qk in (("int8_qk_fp8_pv", "int8"), ("fp8_qk_fp8_pv", "fp8")):
+        ws = attn.sage8_prep(q, k, v, qk=qk).workspace
+        prep = attn.Sage8Prepared(ws, shape, q.dtype, qk=qk)
+        fp = lambda: attn.sage8_prep(q, k, v, workspace=ws, qk=qk)  # noqa: E731
+        f8 = lambda: attn.fwd_sage8(prep, causal=causal, bias=bias)  # noqa: E731
+        _warm(fp)
+        sp = _stats(_time_launches(fp, 20, stream))
+        _warm(f8)
+        s8 = _stats(_time_launches(f8, 20, stream))
+        tf8 = F / (s8["ms_avg"] * 1e-3) / 1e12
+        tfe = F / ((s8["ms_avg"] + sp["ms_avg"]) * 1e-3) / 1e12
+        res[name] = {"attention": {**s8, "tflops": round(tf8, 2),
+                                   "frac_of_8bit_peak": round(tf8 / PEAK_8BIT_TFLOPS, 4)},
+                     "prep": {**sp, "GBs": round(prep_bytes(*shape) / (sp["ms_avg"] * 1e-3) / 1e9, 1)},
+                     "tflops_prep_plus_attention": round(tfe, 2)}
+        if t16_ms is not None:
+            res[name]["speedup_vs_bf16_attention"] = round(t16_ms / s8["ms_avg"], 3)
+            res[name]["speedup_vs_bf16_end_to_end"] = round(t16_ms / (s8["ms_avg"] + sp["ms_avg"]), 3)
+        del ws, prep
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(attention heads shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary, args.skip)
     import torch
     import __graft_entry__
     __graft_entry__._ensure_built()
@@ -229,71 +279,46 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    cfg, inp = workloads.config_inputs(2)
+    cfg, inp = workloads.config_inputs(3)
     log(f"inputs ready: {cfg['name']}")
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     F = workloads.flops(B, H, N, d, causal)
-    ws = attn.sage8_prep(q, k, v).workspace
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         attn.fwd(q, k, v, causal=causal)
-        if ev is not None:
-            ev[1].record(stream)
-        prep = attn.sage8_prep(q, k, v, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
-        attn.fwd_sage8(prep, causal=causal)
-        if ev is not None:
-            ev[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(K):
-        step(ev[s])
+        ev[s][0].record(stream)
+        step()
+        ev[s][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
     log(f"timed {K} steps: {ms_per_step:.4f} ms per step")
     k16 = _stats([e[0].elapsed_time(e[1]) for e in ev])
-    kprep = _stats([e[1].elapsed_time(e[2]) for e in ev])
-    k8 = _stats([e[2].elapsed_time(e[3]) for e in ev])
-    value = 2 * F / (ms_per_step * 1e-3) / 1e12
-
+    value = F / (ms_per_step * 1e-3) / 1e12
     tf16 = F / (k16["ms_avg"] * 1e-3) / 1e12
-    tf8 = F / (k8["ms_avg"] * 1e-3) / 1e12
-    tf8_e2e = F / ((k8["ms_avg"] + kprep["ms_avg"]) * 1e-3) / 1e12
-    pbytes = prep_bytes(B, H, N, d)
-    prep_gbs = pbytes / (kprep["ms_avg"] * 1e-3) / 1e9
-    kernels = {
-        "fwd16": dict(bound="mfma", achieved=round(tf16, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=round(tf16 / PEAK_BF16_TFLOPS, 4), traffic=traffic_for("fwd16"),
-                      kernel="fwd16_kernel<128, bf16, causal> (bf16 fused forward)", ms=k16["ms_avg"],
-                      units_per_launch=f"{F:.4e} flop (4*B*H*N^2*d/2)"),
-        "fwd8": dict(bound="mfma", achieved=round(tf8, 2), peak=PEAK_8BIT_TFLOPS, unit="TFLOP/s",
-                     frac=round(tf8 / PEAK_8BIT_TFLOPS, 4), traffic=traffic_for("fwd8"),
-                     kernel="fwd8_kernel<128, causal> (INT8 QK^T, FP8 PV fused forward)", ms=k8["ms_avg"],
-                     units_per_launch=f"{F:.4e} flop (4*B*H*N^2*d/2)"),
-        "prep8": dict(bound="hbm", achieved=round(prep_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=round(prep_gbs / PEAK_HBM_GBS, 4), traffic=traffic_for("prep8"),
-                      kernel="sage8 colstats + finalize + quant (three launches)", ms=kprep["ms_avg"],
-                      units_per_launch=f"{pbytes} bytes (9 per element of Q/K/V)"),
-    }
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    roof = {kk: kernels[dom][kk] for kk in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")}
-    roof["ms_avg"] = kernels[dom]["ms"]
+    roof = dict(bound="mfma", achieved=round(tf16, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(tf16 / PEAK_BF16_TFLOPS, 4), traffic=traffic_for("fwd16", 3),
+                kernel="fwd16_kernel<128, bf16, causal, 1, 8, dense> (bf16 fused forward)",
+                ms_avg=k16["ms_avg"], units_per_launch=f"{F:.4e} flop (4*B*H*N^2*d/2)")
+
+    log("8-bit path on the same inputs")
+    paths = {"bf16": {**k16, "tflops": round(tf16, 2), "frac_of_peak": round(tf16 / PEAK_BF16_TFLOPS, 4)}}
+    paths.update(sage8_paths(attn, q, k, v, causal, None, F, k16["ms_avg"], stream))
 
     out = {
         "metric": METRIC,
@@ -306,24 +331,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 + int8/fp8(e4m3)",
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, no dataset)",
         "config": {"workload": f"{cfg['name']}: B={B} H={H} N={N} d={d} causal, bf16 in/out; "
-                               "step = bf16 forward + 8-bit prep + 8-bit forward",
+                               "step = one bf16 fused forward",
                    "batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": causal,
                    "cache_flush": False},
         "roofline": roof,
-        "kernels": {n: {kk: vv for kk, vv in kv.items()} for n, kv in kernels.items()},
-        "per_kernel_ms": {"fwd16": k16, "prep8": kprep, "fwd8": k8},
-        "paths": {
-            "bf16": {"tflops": round(tf16, 2), "frac_of_peak": round(tf16 / PEAK_BF16_TFLOPS, 4)},
-            "sage8": {"tflops_attention": round(tf8, 2), "frac_of_8bit_peak": round(tf8 / PEAK_8BIT_TFLOPS, 4),
-                      "tflops_prep_plus_attention": round(tf8_e2e, 2),
-                      "speedup_vs_bf16_attention": round(tf8 / tf16, 3),
-                      "speedup_vs_bf16_end_to_end": round(tf8_e2e / tf16, 3)},
-        },
+        "paths": paths,
     }
-
     if not args.no_extra:
         out["workloads"] = extra_workloads(attn, workloads, stream, dev)
         out["backward"] = backward_workloads(attn, workloads, stream, dev)
@@ -334,13 +350,37 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def trace_summary(path, skip):
+    """Per (kernel, grid) dispatch durations of a rocprofv3 kernel-trace CSV,
+    leaving out the first `skip` dispatches of each (kernel, grid)."""
+    import csv
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            key = (name, r.get("Grid_Size_X", r.get("Grid_Size", "")), r.get("Workgroup_Size_X",
+                                                                                r.get("Workgroup_Size", "")))
+            groups.setdefault(key, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows = []
+    for (name, grid, wg), ts in groups.items():
+        ts.sort()
+        durs = [(e - s) / 1e6 for s, e in ts]
+        kept = durs[skip:] if len(durs) > skip else durs
+        rows.append((sum(durs), name, grid, wg, len(durs), sum(durs) / len(durs), len(kept), sum(kept) / len(kept)))
+    rows.sort(reverse=True)
+    print(f"{'n':>6} {'avg ms':>9} {'kept':>5} {'kept avg':>9}  kernel [grid x; workgroup]")
+    for _, name, grid, wg, n, avg, nk, avgk in rows:
+        short = name if len(name) < 110 else name[:107] + "..."
+        print(f"{n:>6} {avg:9.4f} {nk:>5} {avgk:9.4f}  {short} [{grid}; {wg}]")
+
+
 def extra_workloads(attn, workloads, stream, dev):
-    """The long-context, 8-bit-outlier, DiT-gated and block-sparse DiT
+    """The llm-prefill, 8-bit-outlier, DiT-gated and block-sparse DiT
     workloads at full size: 20 timed launches per path after 0.1 s of
     warm-up launches."""
     import torch
     extra = {}
-    for cid in (3, 4, 5, 6):
+    for cid in (2, 4, 5, 6):
         c2, i2 = workloads.config_inputs(cid)
         log(f"workload {c2['name']}")
         q2, k2, v2 = (i2[n].to(dev) for n in ("q", "k", "v"))
@@ -352,51 +392,25 @@ def extra_workloads(attn, workloads, stream, dev):
               else workloads.flops(c2["B"], c2["H"], c2["N"], c2["d"], c2["causal"]))
         del i2
         res = {}
+        t16 = None
         if cid != 4:
             fn = lambda: attn.fwd(q2, k2, v2, causal=c2["causal"], bias=b2)  # noqa: E731
             _warm(fn)
             st = _stats(_time_launches(fn, 20, stream))
             tf = F2 / (st["ms_avg"] * 1e-3) / 1e12
             res["bf16"] = {**st, "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-        ws = attn.sage8_prep(q2, k2, v2).workspace
-        prep = attn.Sage8Prepared(ws, tuple(q2.shape), q2.dtype)
-        fp = lambda: attn.sage8_prep(q2, k2, v2, workspace=ws)  # noqa: E731
-        f8 = lambda: attn.fwd_sage8(prep, causal=c2["causal"], bias=b2)  # noqa: E731
-        _warm(fp)
-        sp = _stats(_time_launches(fp, 20, stream))
-        _warm(f8)
-        s8 = _stats(_time_launches(f8, 20, stream))
-        tf8 = F2 / (s8["ms_avg"] * 1e-3) / 1e12
-        tfe = F2 / ((s8["ms_avg"] + sp["ms_avg"]) * 1e-3) / 1e12
-        res["sage8"] = {"attention": {**s8, "tflops": round(tf8, 2), "frac_of_8bit_peak": round(tf8 / PEAK_8BIT_TFLOPS, 4)},
-                        "prep": {**sp, "GBs": round(prep_bytes(*q2.shape) / (sp["ms_avg"] * 1e-3) / 1e9, 1)},
-                        "tflops_prep_plus_attention": round(tfe, 2)}
-        if "bf16" in res:
-            res["sage8"]["speedup_vs_bf16_attention"] = round(tf8 / res["bf16"]["tflops"], 3)
-            res["sage8"]["speedup_vs_bf16_end_to_end"] = round(tfe / res["bf16"]["tflops"], 3)
-        # the FP8-QK variant (Q and centred K in e4m3 blocks) on the same data
-        wsf = attn.sage8_prep(q2, k2, v2, qk="fp8").workspace
-        prepf = attn.Sage8Prepared(wsf, tuple(q2.shape), q2.dtype, qk="fp8")
-        fpf = lambda: attn.sage8_prep(q2, k2, v2, workspace=wsf, qk="fp8")  # noqa: E731
-        f8f = lambda: attn.fwd_sage8(prepf, causal=c2["causal"], bias=b2)  # noqa: E731
-        _warm(fpf)
-        spf = _stats(_time_launches(fpf, 20, stream))
-        _warm(f8f)
-        s8f = _stats(_time_launches(f8f, 20, stream))
-        tff = F2 / (s8f["ms_avg"] * 1e-3) / 1e12
-        tffe = F2 / ((s8f["ms_avg"] + spf["ms_avg"]) * 1e-3) / 1e12
-        res["sage8_fp8qk"] = {"attention": {**s8f, "tflops": round(tff, 2),
-                                            "frac_of_8bit_peak": round(tff / PEAK_8BIT_TFLOPS, 4)},
-                              "prep": {**spf, "GBs": round(prep_bytes(*q2.shape) / (spf["ms_avg"] * 1e-3) / 1e9, 1)},
-                              "tflops_prep_plus_attention": round(tffe, 2),
-                              "speedup_vs_int8_qk_attention": round(tff / tf8, 3)}
-        del wsf, prepf
+            t16 = st["ms_avg"]
+        res.update(sage8_paths(attn, q2, k2, v2, c2["causal"], b2, F2, t16, stream))
+        if cid == 2:
+            # the whole hot path once: bf16 forward, then 8-bit preparation and forward
+            r8 = res["int8_qk_fp8_pv"]
+            res["hot_path_step_ms"] = round(t16 + r8["prep"]["ms_avg"] + r8["attention"]["ms_avg"], 4)
         if sparse:
             res["flops_counted"] = f"{F2:.4e} (gated-on block pairs only, {c2['gate_keep']} of the off-diagonal kept)"
         extra[f"{c2['name']}: B={c2['B']} H={c2['H']} N={c2['N']} d={c2['d']} "
               f"{'causal' if c2['causal'] else 'non-causal'}{' +gate bias' if b2 is not None else ''}"
               f"{' (block-sparse)' if sparse else ''}"] = res
-        del q2, k2, v2, b2, ws, prep
+        del q2, k2, v2, b2
         torch.cuda.empty_cache()
     return extra
 

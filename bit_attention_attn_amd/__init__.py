@@ -258,7 +258,9 @@ def _check_cu(cu_seqlens, device, max_seqlen=None, total=None):
     clamp a longer sequence to max_seqlen and would leave the rest of its
     rows unwritten): offsets non-decreasing from 0 up to at most total,
     every length at most max_seqlen.  This reads the B+1 offsets back to the
-    host (one small synchronous copy)."""
+    host (one small synchronous copy), which a stream being recorded into a
+    graph cannot do: under capture the offsets are not read and the caller
+    keeps that contract."""
     if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
             or cu_seqlens.device != device or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2):
         raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
@@ -266,6 +268,8 @@ def _check_cu(cu_seqlens, device, max_seqlen=None, total=None):
         return
     if int(max_seqlen) < 1:
         raise ValueError("max_seqlen must be >= 1")
+    if torch.cuda.is_current_stream_capturing():
+        return
     cu = cu_seqlens.cpu()
     lens = cu[1:] - cu[:-1]
     if int(cu[0]) < 0 or bool((lens < 0).any()) or int(cu[-1]) > total:

@@ -25,6 +25,10 @@ Functions (each cites what it follows in the C source):
 * ``sage8_emulate_rows_fp32`` -- the same with the GPU kernel's fp32
                         decisions (lazy running maximum, P scale), for a
                         tight comparison with the GPU.
+* ``sage8_qk8_rows`` -- INT8 scores (dequantised with the block scales) and
+                        the exact softmax(.)V with the 16-bit V, in fp64: the
+                        variant that quantises only the first product (same
+                        passage of page 1).
 * ``e4m3_encode``, ``e4m3_decode`` -- OCP FP8 E4M3 from its definition.
 """
 import ctypes
@@ -81,6 +85,10 @@ def _load():
                                                    _i64, _i64, _i64, _i64, _int, ctypes.c_float,
                                                    _ptr, _i64, _ptr, _ptr, _int, _int]
     lib.sage8_oracle_emulate_rows_fp32.restype = _int
+    lib.sage8_oracle_qk8_rows.argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                          _i64, _i64, _i64, _i64, _int, _dbl,
+                                          _ptr, _i64, _ptr, _ptr, _int]
+    lib.sage8_oracle_qk8_rows.restype = _int
     _lib = lib
     return lib
 
@@ -309,4 +317,34 @@ def sage8_emulate_rows_fp32(prep, rows, causal=False, scale=None, bias=None, nth
                                                 _p(out), _p(lse), int(fp8), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"sage8_oracle_emulate_rows_fp32 failed with code {rc}")
+    return out, lse
+
+
+def sage8_qk8_rows(prep, v, rows, causal=False, scale=None, bias=None, nthreads=0):
+    """INT8 scores from the quantised Q and centred K of sage8_prepare (INT8
+    format), then the exact softmax and the exact product with v (the 16-bit
+    V, any float array [B,H,N,d]) in fp64.  Returns (O [nrows,d], LSE [nrows]);
+    the LSE adds back the score shift of the K centring."""
+    if prep.get("qk_fp8", False):
+        raise ValueError("sage8_qk8_rows takes INT8 scores")
+    qq = np.ascontiguousarray(prep["qq"], dtype=np.int8)
+    kq = np.ascontiguousarray(prep["kq"], dtype=np.int8)
+    sq, sk = _f32(prep["sq"]), _f32(prep["sk"])
+    v = _f32(v)
+    B, H, N, d = qq.shape
+    assert v.shape == qq.shape and kq.shape == qq.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if bias is not None:
+        bias = _f32(bias)
+        assert bias.shape == (B, H, (N + 63) // 64, (N + 63) // 64), bias.shape
+    km = _f32(prep["kmean"]) if prep.get("kmean") is not None else None
+    r = _rows(rows)
+    out = np.zeros((r.shape[0], d), dtype=np.float64)
+    lse = np.zeros((r.shape[0],), dtype=np.float64)
+    rc = _load().sage8_oracle_qk8_rows(_p(qq), _p(kq), _p(sq), _p(sk), _p(v), _p(km), _p(bias),
+                                       B, H, N, d, int(bool(causal)), float(scale), _p(r), r.shape[0],
+                                       _p(out), _p(lse), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"sage8_oracle_qk8_rows failed with code {rc}")
     return out, lse

@@ -517,3 +517,114 @@ int sage8_oracle_emulate_rows_fp32(const void* qq, const void* kq,
     }
     return failed ? 3 : 0;
 }
+
+/* ---- INT8 scores with the 16-bit P V product, modelled in fp64 ---------- */
+
+/*
+ * The variant of the 8-bit recipe that quantises only the first product
+ * (page 1, "SageAttention", claim vs reality section: INT8 for Q K^T after
+ * K is mean-centred; the page puts P and V in FP8 as the second ingredient,
+ * this variant keeps them in the inputs' 16-bit format).  For every row
+ * (b,h,i), in fp64, from the quantised data of steps 1-2 and the exact V:
+ *
+ *   s_j  = scale * sq[i/64] * sk[j/64] * sum_c Qq[i,c] Kq[j,c]
+ *          + bias[b,h,i/64,j/64]          for the keys the mask allows
+ *   m    = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j
+ *   O[c] = sum_j p_j V[j,c] / l
+ *   LSE  = m + ln l + scale * sq[i/64] * sum_c Qq[i,c] kmean[c]
+ *
+ * The scores are exact attention scores of the dequantised Q and centred K
+ * (the integer dot product is exact); centring K shifts every score of a row
+ * by the same amount, which leaves O unchanged and is added back to the LSE
+ * so that it refers to the original scores.  Everything after the scores is
+ * the exact softmax(.)V of the plain oracle: the row is formed whole, then
+ * normalised, then multiplied by V.  v holds the exact values of the 16-bit
+ * V ([B,H,N,d] float32); qq, kq are INT8 [B,H,N,d]; sq, sk [B,H,ceil(N/64)];
+ * kmean [B,H,d] (nullable: no LSE shift).  out [nrows,d], lse [nrows]
+ * (nullable), fp64.  A row with no visible key gives O = 0, LSE = -inf.
+ */
+int sage8_oracle_qk8_rows(const int8_t* qq, const int8_t* kq, const float* sq,
+                          const float* sk, const float* v, const float* kmean,
+                          const float* bias, int64_t B, int64_t H, int64_t N,
+                          int64_t d, int causal, double scale,
+                          const int64_t* rows, int64_t nrows, double* out,
+                          double* lse, int nthreads)
+{
+    if (!qq || !kq || !sq || !sk || !v || !rows || !out || B <= 0 || H <= 0 ||
+        N <= 0 || d <= 0 || nrows < 0)
+        return 1;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N)
+            return 2;
+    }
+    const int64_t nqk = (N + SAGE_QK_BLOCK - 1) / SAGE_QK_BLOCK;
+    const int64_t nbb = (N + SAGE_BIAS_BLOCK - 1) / SAGE_BIAS_BLOCK;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)N * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!s)
+                continue;
+            const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            const int64_t bh = b * H + h;
+            const int8_t* qi = qq + (bh * N + i) * d;
+            const double sqi = (double)sq[bh * nqk + i / SAGE_QK_BLOCK];
+            double m = -INFINITY;
+            for (int64_t j = 0; j < N; ++j) {
+                if (causal && j > i) {
+                    s[j] = -INFINITY;
+                    continue;
+                }
+                const int8_t* kj = kq + (bh * N + j) * d;
+                int64_t acc = 0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc += (int64_t)qi[c] * (int64_t)kj[c];
+                double sj = scale * (sqi * (double)sk[bh * nqk + j / SAGE_QK_BLOCK] * (double)acc);
+                if (bias)
+                    sj += (double)bias[(bh * nbb + i / SAGE_BIAS_BLOCK) * nbb + j / SAGE_BIAS_BLOCK];
+                s[j] = sj;
+                if (sj > m)
+                    m = sj;
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                s[j] = (m == -INFINITY) ? 0.0 : exp(s[j] - m);
+                l += s[j];
+            }
+            double* o = out + r * d;
+            for (int64_t c = 0; c < d; ++c)
+                o[c] = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                if (s[j] == 0.0)
+                    continue;
+                const float* vj = v + (bh * N + j) * d;
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] += s[j] * (double)vj[c];
+            }
+            for (int64_t c = 0; c < d; ++c)
+                o[c] = (l > 0.0) ? o[c] / l : 0.0;
+            if (lse) {
+                double shift = 0.0;
+                if (kmean)
+                    for (int64_t c = 0; c < d; ++c)
+                        shift += (double)qi[c] * (double)kmean[bh * d + c];
+                lse[r] = (l > 0.0) ? m + log(l) + scale * sqi * shift : -INFINITY;
+            }
+        }
+        free(s);
+    }
+    return failed ? 3 : 0;
+}

@@ -13,7 +13,7 @@ stream, which the binding passes to the library).
 
 On the same inputs the 8-bit path is then timed (its preparation and its
 forward, 20 launches each after warm-up; INT8 scores with FP8 P and V, the
-FP8-QK variant, and INT8 scores with 16-bit P V) and reported under ``paths``
+FP8-QK variant, and INT8 scores with the 16-bit P V) and reported under ``paths``
 with its speedup over the bf16 forward, attention alone and with the
 preparation.  Other workloads follow under ``workloads`` and ``backward``;
 none of them is part of ``value``.
@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workload", type=int, default=0,
                     help="profiling mode: run only this workload (1-5) --steps times and print its timing")
-    ap.add_argument("--path", default="bf16", choices=["bf16", "sage8", "bwd"],
+    ap.add_argument("--path", default="bf16", choices=["bf16", "sage8", "sage8pv16", "bwd"],
                     help="profiling mode: which path to run")
     ap.add_argument("--trace-summary", default="",
                     help="print per (kernel, grid) durations of a rocprofv3 kernel-trace CSV and exit")
@@ -185,6 +185,12 @@ def profile_one(args):
 
         def fn():
             return attn.bwd(q, k, v, o, dout, lse, causal=cfg["causal"], bias=bias, return_dbias=bias is not None)
+    elif args.path == "sage8pv16":
+        ws = attn.sage8_prep(q, k, v).workspace
+
+        def fn():
+            prep = attn.sage8_prep(q, k, v, workspace=ws)
+            return attn.fwd_sage8_pv16(prep, v, causal=cfg["causal"], bias=bias, out_dtype=out_dtype)
     else:
         ws = attn.sage8_prep(q, k, v).workspace
 
@@ -227,27 +233,38 @@ def cpu_model():
     return "unknown"
 
 
+# INT8 scores with the 16-bit P V product: half the FLOPs at the int8 rate,
+# half at the bf16 rate, so the time at peak is F/2/5000 + F/2/2500 = F/3333.
+PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_8BIT_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+
+
 def sage8_paths(attn, q, k, v, causal, bias, F, t16_ms, stream):
     """The 8-bit path on the given inputs: preparation and forward timed
     separately (20 launches each after 0.1 s of warm-up) for each recipe, with
     the speedup over the bf16 forward time t16_ms (when given), attention
     alone and with the preparation (page 1, "SageAttention": the conversion
-    overhead counts)."""
+    overhead counts).  Recipes: INT8 scores with FP8 P and V (the pages'
+    recipe), FP8 scores with FP8 P and V, INT8 scores with the 16-bit P V."""
     res = {}
     shape = tuple(q.shape)
-    for name, qk in (("int8_qk_fp8_pv", "int8"), ("fp8_qk_fp8_pv", "fp8")):
+    for name, qk in (("int8_qk_fp8_pv", "int8"), ("fp8_qk_fp8_pv", "fp8"), ("int8_qk_16bit_pv", "int8")):
         ws = attn.sage8_prep(q, k, v, qk=qk).workspace
         prep = attn.Sage8Prepared(ws, shape, q.dtype, qk=qk)
         fp = lambda: attn.sage8_prep(q, k, v, workspace=ws, qk=qk)  # noqa: E731
-        f8 = lambda: attn.fwd_sage8(prep, causal=causal, bias=bias)  # noqa: E731
+        if name == "int8_qk_16bit_pv":
+            f8 = lambda: attn.fwd_sage8_pv16(prep, v, causal=causal, bias=bias)  # noqa: E731
+            peak = PEAK_MIXED_TFLOPS
+        else:
+            f8 = lambda: attn.fwd_sage8(prep, causal=causal, bias=bias)  # noqa: E731
+            peak = PEAK_8BIT_TFLOPS
         _warm(fp)
         sp = _stats(_time_launches(fp, 20, stream))
         _warm(f8)
         s8 = _stats(_time_launches(f8, 20, stream))
         tf8 = F / (s8["ms_avg"] * 1e-3) / 1e12
         tfe = F / ((s8["ms_avg"] + sp["ms_avg"]) * 1e-3) / 1e12
-        res[name] = {"attention": {**s8, "tflops": round(tf8, 2),
-                                   "frac_of_8bit_peak": round(tf8 / PEAK_8BIT_TFLOPS, 4)},
+        res[name] = {"attention": {**s8, "tflops": round(tf8, 2), "peak": round(peak, 1),
+                                   "frac_of_peak": round(tf8 / peak, 4)},
                      "prep": {**sp, "GBs": round(prep_bytes(*shape) / (sp["ms_avg"] * 1e-3) / 1e9, 1)},
                      "tflops_prep_plus_attention": round(tfe, 2)}
         if t16_ms is not None:

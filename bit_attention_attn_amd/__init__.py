@@ -13,6 +13,8 @@ raised.
     prep = sage8_prep(q, k, v)                  # 8-bit preparation
     fwd_sage8(prep, causal=False, ...)          # 8-bit forward
     sageattn(q, k, v, causal=False, ...)        # both 8-bit steps
+    fwd_sage8_pv16(prep, v, causal=False, ...)  # INT8 scores, 16-bit P V
+    sageattn_pv16(q, k, v, causal=False, ...)   # both steps of that variant
     sageattn_varlen(q, k, v, cu_seqlens, max_seqlen, ...)  # 8-bit, packed sequences
 
 Tensors are [B, H, N, d] contiguous CUDA (HIP) tensors, d in {64, 96, 128}
@@ -29,7 +31,7 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_strided", "fwd_varlen", "bwd", "attention", "sage8_prep", "sage8_prep_varlen", "fwd_sage8",
-           "sageattn", "sageattn_varlen", "AttnError", "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH",
+           "fwd_sage8_pv16", "sageattn_pv16", "sageattn", "sageattn_varlen", "AttnError", "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH",
            "status_str"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -84,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.attn_k_smooth_quant_fp8qk.restype = i
     L.attn_fwd_sage8_fp8qk.argtypes = L.attn_fwd_sage8.argtypes
     L.attn_fwd_sage8_fp8qk.restype = i
+    L.attn_fwd_sage8_pv16.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, f, vp, i, vp]
+    L.attn_fwd_sage8_pv16.restype = i
     L.attn_k_smooth_quant_strided.argtypes = [vp, vp, vp, i, i, i, i, i, ll_p, vp, i, vp, sz, vp]
     L.attn_k_smooth_quant_strided.restype = i
     L.attn_fwd_sage8_strided.argtypes = [vp, vp, vp, i, i, i, i, ll_p, vp, i, f, vp, i, i, vp]
@@ -444,6 +448,42 @@ def sageattn(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, retur
     if tensor_layout == "NHD":
         return (res[0].transpose(1, 2), res[1]) if return_lse else res.transpose(1, 2)
     return res
+
+
+def fwd_sage8_pv16(prep: Sage8Prepared, v, causal=False, scale=None, bias=None, out_dtype=None,
+                   return_lse=False):
+    """8-bit forward with INT8 scores from the prepared workspace (INT8
+    format, contiguous preparation) and the 16-bit P V product with v, the
+    contiguous [B,H,N,d] V that was prepared.  O is contiguous [B,H,N,d]."""
+    B, H, N, d = prep.shape
+    dev = prep.workspace.device
+    if prep.qk != "int8" or prep.cu_seqlens is not None:
+        raise ValueError("the 16-bit P V variant takes a contiguous INT8 preparation")
+    if (not isinstance(v, torch.Tensor) or tuple(v.shape) != (B, H, N, d) or not v.is_contiguous()
+            or v.dtype != prep.in_dtype or v.device != dev):
+        raise ValueError("v must be the contiguous [B,H,N,d] V of the preparation, in its dtype")
+    bias = _check_bias(bias, B, H, N, dev)
+    out_dtype = prep.in_dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    fn = lib().attn_fwd_sage8_pv16
+    with torch.cuda.device(dev):
+        st = fn(_ptr(prep.workspace), _ptr(v), _DTYPE_CODE[v.dtype], _ptr(o), _ptr(lse), B, H, N, d,
+                int(bool(causal)), float(scale), _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(dev))
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+    return (o, lse) if return_lse else o
+
+
+def sageattn_pv16(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, return_lse=False):
+    """INT8 scores with the 16-bit P V product in one call: the 8-bit
+    preparation of contiguous [B,H,N,d] q, k, v, then fwd_sage8_pv16."""
+    _check_qkv(q, k, v)
+    prep = sage8_prep(q, k, v)
+    return fwd_sage8_pv16(prep, v, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
+                          return_lse=return_lse)
 
 
 def sageattn_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False,

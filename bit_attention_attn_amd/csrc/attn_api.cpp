@@ -221,6 +221,25 @@ attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N
   return ATTN_OK;
 }
 
+attn_status fwd_q8(const void* workspace, const void* v, int v_dtype, void* o, float* lse, int B, int H, int N,
+                   int d, int causal, float scale, const float* bias, int out_dtype, void* stream) {
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  if (v == nullptr) return ATTN_ERR_NULL;
+  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
+  if (s != ATTN_OK) return s;
+  if (v_dtype != ATTN_DTYPE_F16 && v_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (out_dtype != v_dtype && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+  if (!aligned(v, 16)) return ATTN_ERR_ALIGN;
+  s = check_device();
+  if (s != ATTN_OK) return s;
+  const bool bf16 = v_dtype == ATTN_DTYPE_BF16;
+  attn::FwdArgs a{nullptr, nullptr, v, o, lse, bias, B, H, N, d, causal, scale,
+                  out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16)};
+  if (attn::launch_fwd_q8(workspace, a, bf16, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +300,12 @@ attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B, in
 attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
                                  int causal, float scale, const float* bias, int out_dtype, void* stream) {
   return fwd8(workspace, o, lse, B, H, N, d, causal, scale, bias, out_dtype, nullptr, nullptr, stream, true);
+}
+
+attn_status attn_fwd_sage8_pv16(const void* workspace, const void* v, int v_dtype, void* o, float* lse, int B,
+                                int H, int N, int d, int causal, float scale, const float* bias, int out_dtype,
+                                void* stream) {
+  return fwd_q8(workspace, v, v_dtype, o, lse, B, H, N, d, causal, scale, bias, out_dtype, stream);
 }
 
 attn_status attn_k_smooth_quant_strided(const void* q, const void* k, const void* v, int in_dtype, int B, int H,

@@ -35,6 +35,14 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// INT8 score products start their accumulators from the bit pattern of
+// 1.5 * 2^23: with |S| < 2^22 (true for d <= 128: 128 * 127^2 < 2^22) the
+// int32 sum 0x4B400000 + S read as fp32 is exactly 12582912 + S, so the
+// scores leave the matrix unit as floats and the offset is folded into the
+// exponent.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
 // 32x32x16 MFMA on 16-bit inputs packed as 4 dwords per lane.
 template <bool BF16>
 __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {

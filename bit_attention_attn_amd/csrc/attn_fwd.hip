@@ -75,9 +75,17 @@ struct Fwd16Params {
   int H;
   const int* cu;
   int64_t qs[3], ks[3], vs[3], os[3];
+  // INT8 scores (Q8 kernels): the prepared INT8 Q and centred K [B,H,np,d],
+  // the Q block scales [B,H,nblk] and the K mean [B,H,d] (the K block scales
+  // come as their own kernel argument)
+  const int8_t* qq;
+  const int8_t* kq;
+  const float* sq;
+  const float* kmean;
+  int np, nblk;
 };
 
-template <int D, int QS, int NW>
+template <int D, int QS, int NW, bool Q8 = false>
 struct Fwd16Smem {
   using T = Tiling<QS, NW>;
   // Padded rows.  K: 16 bytes of padding, so the 16-byte operand reads of 16
@@ -85,7 +93,8 @@ struct Fwd16Smem {
   // 4 consecutive rows x 64 bytes per half wave; a row stride of 288 bytes
   // (d = 128) or 192 bytes (d = 64) spreads them over the banks (measured
   // on gfx950: 107 B/clk/CU against 62 B/clk/CU at a 272-byte stride).
-  static constexpr int kKRow = D + 8;
+  // (INT8 K, Q8 kernels: D + 16 bytes per row, i.e. D/2 + 8 elements)
+  static constexpr int kKRow = Q8 ? D / 2 + 8 : D + 8;
   // V rows of 288 bytes at d = 128 and 96, 192 bytes at d = 64
   static constexpr int kVRow = D == 64 ? D + 32 : 144;
   static constexpr int kKTile = kBN * kKRow;
@@ -101,18 +110,29 @@ enum Mode { kDense = 0, kBias = 1, kGen = 2 };
 // The block bias comes as its own restrict argument: its reads, uniform and
 // never written by the kernel, then compile to scalar loads, which do not
 // share the in-order vector-load counter with the K/V prefetch.
-template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, const float* __restrict__ bias) {
+//
+// Q8: the scores come from the 8-bit preparation instead (page 1,
+// "SageAttention": the first product in INT8 after K is mean-centred), as
+// S^T = Kq Qq^T on the 32x32x32 INT8 instruction with the accumulators
+// started from the bit pattern of 1.5 * 2^23 (|S| < 2^22, so the int32 result
+// read as fp32 is exactly 1.5 * 2^23 + S), dequantised per 64 x 64 block by
+// f = sq * sk * scale * log2(e) folded into the exponent; P and V stay in the
+// 16-bit input format for the second product, exactly as in the 16-bit path.
+template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE, bool Q8 = false>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, const float* __restrict__ bias,
+                                                                const float* __restrict__ sk) {
   constexpr bool GEN = MODE == kGen, HAS_BIAS = MODE == kBias;
+  static_assert(!(Q8 && GEN), "INT8 scores take the dense layout");
   using TL = Tiling<QS, NW>;
-  using S = Fwd16Smem<D, QS, NW>;
+  using S = Fwd16Smem<D, QS, NW, Q8>;
   constexpr int kWQ = TL::kWQ, kBM = TL::kBM, kThreads = TL::kThreads;
   constexpr int kKbuf = TL::kKbuf, kVbuf = TL::kVbuf;
   constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
   constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
   constexpr int kCpr = D / 8;  // 16-byte chunks of data per row
   constexpr int kDT = D / 32;  // 32-row tiles of O^T
-  constexpr int kKS = D / 16;  // k-steps of S^T = K Q^T
+  constexpr int kKS = D / 16;  // k-steps of S^T = K Q^T (Q8: D/32 of them)
+  constexpr int kChunksK = Q8 ? kBN * D / 16 : kBN * kCpr;  // 16-byte chunks of a K tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::kElems];
   uint16_t* const kbase_lds = smem;                   // kKbuf K tiles
   uint16_t* const vbase_lds = smem + kKbuf * kKTile;  // kVbuf V tiles
@@ -139,7 +159,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
   int bh_n = 0, tq_n = 0;
-  const bool has_next = DENSE && work_item(wq, round + 1, p.nq, bh_n, tq_n);
+  const bool has_next = DENSE && !Q8 && work_item(wq, round + 1, p.nq, bh_n, tq_n);
   const int qt = CAUSAL ? p.nq - 1 - tq : tq;  // heaviest tiles first
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kWQ;
@@ -174,7 +194,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // Q^T as the B operand of S^T = K Q^T: for query sub-tile qs the lane holds
   // Q[qw0 + 32qs + l32][16kk + 8hf .. +7].  Rows past N read row N-1 (their
   // results are never stored).
-  if (!(DENSE && pre)) {
+  // (Q8: the lane holds Qq[row][32kk + 16hf .. +15], one 32-deep step each)
+  const int8_t* __restrict__ Qq = Q8 ? p.qq + (size_t)bh * p.np * D : nullptr;
+  if constexpr (Q8) {
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      const int row = min(qw0 + 32 * qs + l32, N - 1);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) qf[qs][kk] = *(const u32x4_t*)(Qq + (size_t)row * D + 32 * kk + 16 * hf);
+    }
+  } else if (!(DENSE && pre)) {
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       const int row = min(qw0 + 32 * qs + l32, N - 1);
@@ -183,6 +212,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       for (int kk = 0; kk < kKS; ++kk) qf[qs][kk] = *(const u32x4_t*)(src + 16 * kk);
     }
   }
+  // Q8: the wave's queries lie in one 64-row block; its scale and the K
+  // block scales (scalar reads) dequantise the scores
+  const float sqw = Q8 ? p.sq[(size_t)bh * p.nblk + min(qw0, N - 1) / kBN] : 1.f;
+  const float* skrow = Q8 ? sk + (size_t)bh * p.nblk : nullptr;
 
   const int kend = CAUSAL ? min(N, q0 + kBM) : N;
   const int nkb = (kend + kBN - 1) / kBN;
@@ -197,7 +230,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // later), so every load is unconditional.
   // (general layout: key rows ksn / vsn elements apart, so each chunk has its
   // own per-lane offset and the block offset is kb*64 rows)
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K, (uint32_t)N * ksn * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      Q8 ? buffer_rsrc(p.kq + (size_t)bh * p.np * D, (uint32_t)p.np * D) : buffer_rsrc(K, (uint32_t)N * ksn * 2);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V, (uint32_t)N * vsn * 2);
   const uint32_t voff = 16u * tid;
   uint32_t kvo[kNst], vvo[kNst];
@@ -212,8 +246,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   auto load_k = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < kNst; ++i) {
-      if constexpr (GEN) kst[i] = buffer_load16(krs, kvo[i], (uint32_t)(kb * kBN) * ksn * 2);
-      else kst[i] = buffer_load16(krs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+      if constexpr (Q8) {
+        if (i * kThreads >= kChunksK) break;
+        if (kChunksK % kThreads != 0 && tid + i * kThreads >= kChunksK) continue;
+        kst[i] = buffer_load16(krs, voff, kb * kBN * D + 16 * i * kThreads);
+      } else if constexpr (GEN) {
+        kst[i] = buffer_load16(krs, kvo[i], (uint32_t)(kb * kBN) * ksn * 2);
+      } else {
+        kst[i] = buffer_load16(krs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+      }
     }
   };
   auto load_v = [&](int kb) {
@@ -227,8 +268,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
     uint16_t* ks = kbase_lds + buf * kKTile;
 #pragma unroll
     for (int i = 0; i < kNst; ++i) {
-      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
-      *(u32x4_t*)(ks + row * kKRow + ch * 8) = kst[i];
+      const int idx = tid + i * kThreads;
+      if constexpr (Q8) {
+        // INT8 rows of D bytes: D/16 chunks per row
+        if (i * kThreads >= kChunksK) break;
+        if (kChunksK % kThreads != 0 && idx >= kChunksK) continue;
+        const int row = idx / (D / 16), ch = idx % (D / 16);
+        *(u32x4_t*)(reinterpret_cast<uint8_t*>(ks) + row * kKRow * 2 + ch * 16) = kst[i];
+      } else {
+        const int row = idx / kCpr, ch = idx % kCpr;
+        *(u32x4_t*)(ks + row * kKRow + ch * 8) = kst[i];
+      }
     }
   };
   auto store_v = [&](int buf) {
@@ -262,6 +312,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
 
   // ---- S^T = K Q^T for one key block (two 32-key tiles x QS query tiles)
   auto qk = [&](int buf, f32x16_t (&s)[2][QS]) {
+    if constexpr (Q8) {
+      // S^T = Kq Qq^T on top of the offset, exact (A: 16 bytes of a K row per
+      // 32-deep step, B: the matching bytes of the Q row)
+      const uint8_t* Ks8 = reinterpret_cast<const uint8_t*>(kbase_lds + buf * kKTile) + l32 * kKRow * 2 + 16 * hf;
+      i32x16_t si[2][QS];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) si[T][qs][r] = kMagicBits;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+          const u32x4_t a = *(const u32x4_t*)(Ks8 + 32 * T * kKRow * 2 + 32 * kk);
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs)
+            si[T][qs] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
+                                                              __builtin_bit_cast(i32x4_t, qf[qs][kk]), si[T][qs],
+                                                              0, 0, 0);
+        }
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) s[T][qs] = __builtin_bit_cast(f32x16_t, si[T][qs]);
+      return;
+    }
     const uint16_t* Ks = kbase_lds + buf * kKTile + l32 * kKRow + 8 * hf;
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) s[0][qs] = s[1][qs] = f32x16_t{};
@@ -296,8 +374,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
 
   // ---- block maximum and lazy rescale of the running state; returns the
   // exponent offsets kc = bias - m (log2 units) of the block
-  auto block_max = [&](f32x16_t (&s)[2][QS], float (&kc)[QS], float braw) {
+  // (cf: the scale of the block's raw scores in log2 units, c, or for INT8
+  // scores c * sq * sk, with the offset 1.5 * 2^23 * cf taken off through g0)
+  auto block_max = [&](f32x16_t (&s)[2][QS], float (&kc)[QS], float braw, float cf) {
     const float bl = HAS_BIAS ? braw * kLog2e : 0.f;
+    const float g0 = Q8 ? fmaf(-kMagic, cf, bl) : bl;
     float m_blk[QS];
     bool need_any = false;
 #pragma unroll
@@ -314,7 +395,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
         for (int r = 1; r < 16; ++r) a0 = fminf(a0, fminf(s[0][qs][r], s[1][qs][r]));
         a0 = xor32_min(a0);
       }
-      m_blk[qs] = (a0 == sent) ? -INFINITY : fmaf(a0, c, bl);
+      m_blk[qs] = (a0 == sent) ? -INFINITY : fmaf(a0, cf, g0);
       need_any |= m_blk[qs] > m_run[qs] + kTau;
     }
     if (__any(need_any)) {
@@ -330,7 +411,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       }
     }
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) kc[qs] = bl - ((m_run[qs] == -INFINITY) ? 0.f : m_run[qs]);
+    for (int qs = 0; qs < QS; ++qs) kc[qs] = g0 - ((m_run[qs] == -INFINITY) ? 0.f : m_run[qs]);
   };
 
   // ---- P = exp2(c*S + bias - m) as the B operand of O^T += V^T P^T.  Masked
@@ -338,7 +419,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // passes the smallest normal float for a zero scale).  The row sum adds
   // the rounded P values the product uses.
   u32x4_t pb[4][QS];
-  auto softmax_p = [&](f32x16_t (&s)[2][QS], const float (&kc)[QS]) {
+  auto softmax_p = [&](f32x16_t (&s)[2][QS], const float (&kc)[QS], float cf) {
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       float lsum = 0.f;
@@ -348,8 +429,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int r = 8 * t + e;
-          const float p0 = exp2_approx(fmaf(s[T][qs][r], c, kc[qs]));
-          const float p1 = exp2_approx(fmaf(s[T][qs][r + 1], c, kc[qs]));
+          const float p0 = exp2_approx(fmaf(s[T][qs][r], cf, kc[qs]));
+          const float p1 = exp2_approx(fmaf(s[T][qs][r + 1], cf, kc[qs]));
           const uint32_t pk = pack2<BF16>(p0, p1);
           lsum = sum2_acc<BF16>(pk, lsum);
           pb[kk][qs][e >> 1] = pk;
@@ -395,9 +476,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
     if (wave_has_rows && jc <= wave_last && (!HAS_BIAS || braw != -INFINITY)) {
       qk(buf, sc);
       if (needs_mask(jc)) apply_mask(jc, sc);
+      const float cf = Q8 ? (sqw * skrow[jc]) * c : c;
       float kc[QS];
-      block_max(sc, kc, braw);
-      softmax_p(sc, kc);
+      block_max(sc, kc, braw, cf);
+      softmax_p(sc, kc, cf);
       pv(buf);
     }
     if (more) {
@@ -469,9 +551,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       }
       if (work) {
         if (needs_mask(jc)) apply_mask(jc, sc);
+        const float cf = Q8 ? (sqw * skrow[jc]) * c : c;
         float kc[QS];
-        block_max(sc, kc, 0.f);
-        softmax_p(sc, kc);
+        block_max(sc, kc, 0.f, cf);
+        softmax_p(sc, kc, cf);
         pv(buf);
       }
       __syncthreads();
@@ -485,9 +568,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
     const float l_tot = xor32_sum(l_run[qs]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int qi = qw0 + 32 * qs + l32;
+    // INT8 scores: centring K shifted every score of the row by
+    // scale * sq * (Qq . kmean); the LSE adds it back (the Q codes are read
+    // again here rather than kept live across the loop)
+    float shift = 0.f;
+    if constexpr (Q8) {
+      if (p.lse != nullptr) {
+        const float* kmh = p.kmean + (size_t)bh * D;
+        const int row = min(qi, N - 1);
+        float dot = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const u32x4_t qc = *(const u32x4_t*)(Qq + (size_t)row * D + 32 * kk + 16 * hf);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            dot = fmaf((float)(int)(int8_t)(qc[e >> 2] >> (8 * (e & 3))), kmh[32 * kk + 16 * hf + e], dot);
+        }
+        shift = c * (sqw * xor32_sum(dot));
+      }
+    }
     if (qi < N) {
       if (p.lse != nullptr && hf == 0)
-        p.lse[(size_t)bh * p.N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[(size_t)bh * p.N + qi] = l_tot > 0.f ? (m_run[qs] + __log2f(l_tot) + shift) * kLn2 : -INFINITY;
       const size_t orow = (size_t)ooff + (size_t)qi * osn;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
@@ -509,8 +611,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   }  // work items
 }
 
-template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE>
-hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
+// ws: the 8-bit preparation's workspace (Q8 only)
+template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE, bool Q8 = false>
+hipError_t launch_impl(const FwdArgs& a, hipStream_t stream, const void* ws = nullptr) {
   using TL = Tiling<QS, NW>;
   Fwd16Params p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -537,6 +640,21 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
     p.vs[i] = a.strides[6 + i];
     p.os[i] = a.strides[9 + i];
   }
+  const float* sk = nullptr;
+  p.qq = p.kq = nullptr;
+  p.sq = p.kmean = nullptr;
+  p.np = p.nblk = 0;
+  if constexpr (Q8) {
+    const Sage8Layout L = sage8_layout(a.B, a.H, a.N, D);
+    const char* w = static_cast<const char*>(ws);
+    p.qq = reinterpret_cast<const int8_t*>(w + L.qq);
+    p.kq = reinterpret_cast<const int8_t*>(w + L.kq);
+    p.sq = reinterpret_cast<const float*>(w + L.sq);
+    p.kmean = reinterpret_cast<const float*>(w + L.kmean);
+    sk = reinterpret_cast<const float*>(w + L.sk);
+    p.nblk = L.nblk;
+    p.np = L.nblk * kBN;
+  }
   // Causal tiles differ in cost, so a persistent grid with the balanced
   // heavy-first order pays where it applies (measured +7% at 4x32x4096,
   // d = 128); equal-cost non-causal tiles run one workgroup per item
@@ -544,11 +662,12 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream) {
   // (packed sequences of different lengths: one workgroup per tile; the
   // balance argument of the persistent queues assumes equal heads)
   const int grid = (CAUSAL && !(MODE == kGen && a.cu))
-                       ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE>),
+                       ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE, Q8>),
                                          TL::kThreads, p.nbh, p.nq)
                        : p.ntiles;
   if (grid <= 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE>), dim3(grid), dim3(TL::kThreads), 0, stream, p, a.bias);
+  hipLaunchKernelGGL((fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE, Q8>), dim3(grid), dim3(TL::kThreads), 0, stream, p,
+                     a.bias, sk);
   return hipGetLastError();
 }
 
@@ -572,6 +691,19 @@ template <bool BF16, bool CAUSAL>
 hipError_t launch_g(const FwdArgs& a, hipStream_t stream) {
   if (a.general) return launch_d<BF16, CAUSAL, kGen>(a, stream);
   return a.bias ? launch_d<BF16, CAUSAL, kBias>(a, stream) : launch_d<BF16, CAUSAL, kDense>(a, stream);
+}
+
+// INT8 scores with the 16-bit P V product: the tilings of the 16-bit path.
+template <bool BF16, bool CAUSAL, int MODE>
+hipError_t launch_q8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 64) return launch_impl<64, BF16, CAUSAL, 2, 4, MODE, true>(a, stream, ws);
+  if (a.d == 96) return launch_impl<96, BF16, CAUSAL, 1, 4, MODE, true>(a, stream, ws);
+  return launch_impl<128, BF16, CAUSAL, 1, 8, MODE, true>(a, stream, ws);
+}
+
+template <bool BF16, bool CAUSAL>
+hipError_t launch_q8_g(const void* ws, const FwdArgs& a, hipStream_t stream) {
+  return a.bias ? launch_q8_d<BF16, CAUSAL, kBias>(ws, a, stream) : launch_q8_d<BF16, CAUSAL, kDense>(ws, a, stream);
 }
 
 }  // namespace
@@ -627,6 +759,11 @@ int persistent_grid(const void* kernel, int threads, int nbh, int nq) {
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t stream) {
   if (bf16) return a.causal ? launch_g<true, true>(a, stream) : launch_g<true, false>(a, stream);
   return a.causal ? launch_g<false, true>(a, stream) : launch_g<false, false>(a, stream);
+}
+
+hipError_t launch_fwd_q8(const void* ws, const FwdArgs& a, bool bf16, hipStream_t stream) {
+  if (bf16) return a.causal ? launch_q8_g<true, true>(ws, a, stream) : launch_q8_g<true, false>(ws, a, stream);
+  return a.causal ? launch_q8_g<false, true>(ws, a, stream) : launch_q8_g<false, false>(ws, a, stream);
 }
 
 }  // namespace attn

@@ -89,6 +89,10 @@ Sage8Layout sage8_layout(int B, int H, int N, int d);
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H,
                              int N, int d, const int64_t* strides, const int* cu, void* ws, hipStream_t stream,
                              bool qk_fp8);
+// INT8 scores from the workspace of launch_sage8_prep (INT8 format) with the
+// 16-bit P V product: a.v is the 16-bit V [B,H,N,d] (fp16 unless bf16), O
+// contiguous [B,H,N,d]; a.q and a.k are unused.
+hipError_t launch_fwd_q8(const void* ws, const FwdArgs& a, bool bf16, hipStream_t stream);
 // O is written with the element strides a.strides[9..11] (batch, head,
 // token) when a.general, else contiguous [B,H,N,d].  With a.cu (packed
 // sequences, no bias) batch entry b writes its rows from token a.cu[b].

@@ -398,12 +398,6 @@ struct Fwd8Params {
 constexpr int kNW8 = 4;                // waves per workgroup
 constexpr int kBM8 = 32 * kNW8;        // queries per workgroup
 constexpr int kThreads8 = 64 * kNW8;
-// The INT8 accumulators start from the bit pattern of 1.5 * 2^23: with
-// |S| < 2^22 (true for d <= 128: 128 * 127^2 < 2^22) the int32 sum
-// 0x4B400000 + S read as fp32 is exactly 12582912 + S, so the scores leave
-// the matrix unit as floats and the offset is folded into the exponent.
-constexpr int kMagicBits = 0x4B400000;
-constexpr float kMagic = 12582912.0f;
 
 template <int D>
 struct Fwd8Smem {

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 typedef enum {
     ATTN_OK = 0,
@@ -216,6 +216,31 @@ attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* 
 attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int B,
                                  int H, int N, int d, int causal, float scale,
                                  const float* bias, int out_dtype, void* stream);
+
+/*
+ * attn_fwd_sage8_pv16 -- the 8-bit forward with INT8 scores and the 16-bit
+ * P V product: the first product of page 1 ("SageAttention", claim vs
+ * reality section: Q K^T in INT8 after K is mean-centred), while P and V
+ * stay in the inputs' 16-bit format for the second product, as in
+ * attn_fwd_bf16.  On the workloads measured this meets cos >= 0.999 and
+ * rel-L1 <= 2e-2 against exact attention, which the FP8 P and V of
+ * attn_fwd_sage8 do not (their rounding alone costs about 2-4% rel-L1).
+ *
+ *  workspace  written by attn_k_smooth_quant (INT8 format) for the same B,
+ *             H, N, d; only its Qq, Kq, scales and K mean are read.
+ *  v          the 16-bit V [B,H,N,d] contiguous that was prepared, in
+ *             v_dtype (ATTN_DTYPE_F16 or ATTN_DTYPE_BF16).
+ *  o          [B,H,N,d] in out_dtype: v_dtype or ATTN_DTYPE_F32.
+ *  lse, causal, scale, bias as for attn_fwd_bf16 (the LSE refers to the
+ *  scores before the centring of K).
+ *  S = Qq Kq^T in INT8 with int32 accumulation, dequantised with the two
+ *  block scales; online softmax in fp32 as in attn_fwd_bf16 (running
+ *  maximum raised lazily, P rounded to v_dtype for the product, fp32
+ *  accumulation, one output write).  ABI version 8.
+ */
+attn_status attn_fwd_sage8_pv16(const void* workspace, const void* v, int v_dtype, void* o,
+                                float* lse, int B, int H, int N, int d, int causal,
+                                float scale, const float* bias, int out_dtype, void* stream);
 
 /*
  * attn_k_smooth_quant_strided / attn_fwd_sage8_strided -- the 8-bit pair on

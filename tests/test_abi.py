@@ -31,10 +31,10 @@ def test_library_exports_every_declared_function():
             "attn_k_smooth_quant_fp8qk", "attn_fwd_sage8_fp8qk",
             "attn_k_smooth_quant_strided", "attn_fwd_sage8_strided",
             "attn_sage8_workspace_size", "attn_k_smooth_quant", "attn_sage8_workspace_layout",
-            "attn_fwd_sage8", "attn_status_str", "attn_abi_version"} <= set(names)
+            "attn_fwd_sage8", "attn_fwd_sage8_pv16", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 7
+    assert L.attn_abi_version() == 8
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -254,3 +254,27 @@ def test_strided_tail_rows_must_be_addressable():
     good = [0, 64, ts] * 4
     for name, dt in (("attn_fwd_strided_bf16", BF16), ("attn_fwd_strided_f16", F16)):
         assert _strided(getattr(L, name), good, N=N, out=dt) == E_SHAPE
+
+
+def test_sage8_pv16_validation():
+    """INT8 scores with the 16-bit P V product: workspace, V, dtypes and the
+    common checks, all before any device call."""
+    fn = attn.lib().attn_fwd_sage8_pv16
+
+    def f(ws=FAKE, v=FAKE, vdt=BF16, o=FAKE, N=100, d=64, causal=0, scale=0.1, bias=None, out=BF16):
+        return fn(ws, v, vdt, o, None, 1, 2, N, d, causal, scale, bias, out, None)
+
+    assert f(ws=None) == E_WS
+    assert f(v=None) == E_NULL
+    assert f(o=None) == E_NULL
+    assert f(d=80) == E_HEADDIM
+    assert f(N=0) == E_SHAPE
+    assert f(causal=2) == E_ARG
+    assert f(scale=float("nan")) == E_ARG
+    assert f(vdt=F32, out=F32) == E_DTYPE
+    assert f(vdt=F16, out=BF16) == E_DTYPE
+    assert f(out=9) == E_DTYPE
+    assert f(ws=FAKE + 16) == E_ALIGN
+    assert f(v=FAKE + 8) == E_ALIGN
+    assert f(o=FAKE + 4) == E_ALIGN
+    assert f(bias=FAKE, N=64 * 32768) == E_SHAPE

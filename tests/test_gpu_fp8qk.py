@@ -20,9 +20,15 @@ Bars, each against code under oracle/ only:
     measured at N = 129), so the count check is a loose sanity bar: at most
     10% of the rows (at least 2) leave the 1e-3 band.  The LSE (from the fp32 scores, before any
     e4m3 rounding) keeps the INT8 path's bar;
-  * forward against exact fp64 attention: within 0.01 rel-L1 and 5e-4 cosine
-    of the fp64 model of the same recipe on the same rows (the recipe's own
-    error: about 0.045 rel-L1 on these inputs, more than the INT8 recipe's).
+  * forward against exact fp64 attention: within REL_L1_MARGIN rel-L1 and
+    COS_MARGIN cosine of the fp64 model of the same recipe on the same rows
+    (the kernel-precision model measured at most 0.0013 rel-L1 and 8.1e-5
+    cosine from it on these inputs), and cosine >= 0.999 wherever that fp64
+    model reaches 0.999 + COS_MARGIN.  The recipe's own error is about
+    0.045-0.05 rel-L1 here, with cosine down to 0.9986 on the DiT-gated and
+    the longer non-causal rows: there no kernel faithful to FP8 scores meets
+    the 8-bit tolerance (pinned on the CPU in tests/test_oracle_fp8qk.py),
+    which is why the INT8 recipe stays the default.
 """
 import math
 
@@ -38,6 +44,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 EMU_ROW_ABS, EMU_LSE = 1e-3, 1e-4
+COS_MIN, REL_L1_MARGIN, COS_MARGIN = 0.999, 0.0025, 2e-4
 FLIPS, CODE_STEP = 2, 1.0 / 8.0
 
 
@@ -106,8 +113,10 @@ def _check(inp, causal, scale, rows=None, label="", check_oracle=True):
         m_ref = workloads.error_metrics(got, o_ref)
         m_model = workloads.error_metrics(o_model, o_ref)
         print(f"    vs fp64 attention: {m_ref}; fp64 model of the recipe: {m_model}", flush=True)
-        assert m_ref["rel_l1"] <= m_model["rel_l1"] + 0.01, (label, m_ref, m_model)
-        assert m_ref["cos"] >= m_model["cos"] - 5e-4, (label, m_ref, m_model)
+        assert m_ref["rel_l1"] <= m_model["rel_l1"] + REL_L1_MARGIN, (label, m_ref, m_model)
+        assert m_ref["cos"] >= m_model["cos"] - COS_MARGIN, (label, m_ref, m_model)
+        if m_model["cos"] >= COS_MIN + COS_MARGIN:
+            assert m_ref["cos"] >= COS_MIN, (label, m_ref, m_model)
     return o, rows
 
 

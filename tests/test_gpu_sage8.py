@@ -13,10 +13,17 @@ Three bars, each against code under oracle/ only:
     in 10^5; on a peaky row such a code moves O by up to about 1e-3), and the
     fp32 order of sums;
   * forward against the exact fp64 attention of the same rounded inputs:
-    cosine >= 0.999 per compared set of rows; rel-L1 is recorded and held
-    under REL_L1_FLOOR, the error of the 8-bit recipe itself (INT8 Q K^T,
-    e4m3 P and e4m3 V), which the fp64 model of the recipe reproduces on
-    the CPU.
+    cosine >= 0.999 per compared set of rows (the 8-bit tolerance), and
+    rel-L1 and cosine within REL_L1_MARGIN and COS_MARGIN of the fp64 model
+    of the recipe (oracle.sage8_emulate_rows) on the same rows.  The recipe
+    itself (INT8 Q K^T, e4m3 P and e4m3 V) sits at rel-L1 0.03-0.04 on these
+    i.i.d. inputs, above the 2e-2 asked of the 8-bit path (pinned on the CPU
+    by test_emulator_floor_on_outlier_workload; the INT8-score variant with
+    the 16-bit P V product, tests/test_gpu_sage8_pv16.py, meets 2e-2).  The
+    margins: the kernel-precision model (lazy maximum, P scale) measured at
+    most 0.0016 rel-L1 and 6.3e-5 cosine from the fp64 model over every
+    input of this file, and the kernel is held within EMU_MEAN_ABS of the
+    kernel-precision model (a few 1e-4 of rel-L1 at |O| ~ 0.1).
 """
 import math
 
@@ -32,7 +39,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 5e-5, 1e-4
-COS_MIN, REL_L1_FLOOR = 0.999, 0.05
+COS_MIN, REL_L1_MARGIN, COS_MARGIN = 0.999, 0.0025, 2e-4
 
 
 def _prep_both(inp):
@@ -82,9 +89,13 @@ def _check(inp, causal, scale, rows=None, out_dtype=torch.float32, label="", che
     if check_oracle:
         qn, kn, vn = (inp[n].float().numpy() for n in ("q", "k", "v"))
         o_ref, _ = oracle.attn_rows(qn, kn, vn, rows, causal=causal, scale=scale, bias=bn)
+        o_model, _ = oracle.sage8_emulate_rows(ref, rows, causal=causal, scale=scale, bias=bn)
         m_ref = workloads.error_metrics(got, o_ref)
-        print(f"    vs fp64 attention: {m_ref}", flush=True)
-        assert m_ref["cos"] >= COS_MIN and m_ref["rel_l1"] <= REL_L1_FLOOR, (label, m_ref)
+        m_model = workloads.error_metrics(o_model, o_ref)
+        print(f"    vs fp64 attention: {m_ref}; fp64 model of the recipe: {m_model}", flush=True)
+        assert m_ref["cos"] >= COS_MIN, (label, m_ref)
+        assert m_ref["rel_l1"] <= m_model["rel_l1"] + REL_L1_MARGIN, (label, m_ref, m_model)
+        assert m_ref["cos"] >= m_model["cos"] - COS_MARGIN, (label, m_ref, m_model)
     return prep, ref, o, lse, m_emu, m_ref
 
 

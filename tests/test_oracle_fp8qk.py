@@ -119,3 +119,23 @@ def test_fp8_fp32_emulator_tracks_fp64_model():
     rel32 = np.abs(o32 - o_ref).sum() / np.abs(o_ref).sum()
     assert abs(rel32 - rel64) < 0.3 * rel64, (rel32, rel64)
     assert rel64 < 0.08
+
+
+def test_fp8_scores_miss_the_cosine_bar_where_int8_scores_meet_it():
+    """On a scaled-down DiT-gated workload (non-causal, d = 64, gate bias)
+    the fp64 model of the FP8-QK recipe falls below cosine 0.999 against
+    exact attention, while the INT8 recipe's model stays above it on the same
+    rows: FP8 scores alone cost the 8-bit tolerance there (page 1,
+    "SageAttention", claim vs reality: INT8 for the first product)."""
+    inp = workloads.make_inputs(1, 2, 1024, 64, "bf16", seed=5, gate=True)
+    q, k, v = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    bias = inp["bias"].numpy()
+    rows = workloads.parity_rows(1, 2, 1024, seed=5, n_random=48)
+    o_ref, _ = oracle.attn_rows(q, k, v, rows, causal=False, scale=0.125, bias=bias)
+    res = {}
+    for qk in ("int8", "fp8"):
+        prep = oracle.sage8_prepare(q, k, v, qk=qk)
+        o, _ = oracle.sage8_emulate_rows(prep, rows, causal=False, scale=0.125, bias=bias)
+        res[qk] = workloads.error_metrics(o, o_ref)
+    assert res["fp8"]["cos"] < 0.999 <= res["int8"]["cos"], res
+    assert res["fp8"]["rel_l1"] > res["int8"]["rel_l1"], res

@@ -30,7 +30,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_strided", "fwd_varlen", "bwd", "attention", "sage8_prep", "sage8_prep_varlen", "fwd_sage8",
+__all__ = ["fwd", "fwd_strided", "fwd_varlen", "bwd", "bwd_noalloc", "attention", "sage8_prep", "sage8_prep_varlen", "fwd_sage8",
            "fwd_sage8_pv16", "sageattn_pv16", "sageattn", "sageattn_varlen", "AttnError", "Sage8Prepared", "sage8_workspace_views", "lib", "LIB_PATH",
            "status_str"]
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp, sz, vp]
         fn.restype = i
+    L.attn_bwd_noalloc.argtypes = [i, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
+    L.attn_bwd_noalloc.restype = i
     L.attn_sage8_workspace_size.argtypes = [i, i, i, i]
     L.attn_sage8_workspace_size.restype = sz
     L.attn_k_smooth_quant.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
@@ -185,6 +187,38 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, bias=None, grad_dtype=N
                 _ptr(dk), _ptr(dv),
                 _ptr(dbias), B, H, N, d, int(bool(causal)), float(scale), _ptr(bias),
                 _DTYPE_CODE.get(grad_dtype, -1), _ptr(ws), ws.numel(), _stream(q.device))
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+    return (dq, dk, dv, dbias) if return_dbias else (dq, dk, dv)
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, causal=False, scale=None, bias=None, grad_dtype=None, return_dbias=False):
+    """bwd() through attn_bwd_noalloc: the library takes its scratch from a
+    fixed device array instead of a workspace (for callers that cannot
+    allocate device memory; B*H*N at most ATTN_BWD_NOALLOC_MAX_ROWS, calls
+    on one GPU must not overlap).  The outputs are allocated here, as in
+    bwd(); the results are bwd()'s bit for bit."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    for name, t, dts in (("o", o, (q.dtype, torch.float32)), ("dout", dout, (q.dtype,))):
+        if not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype not in dts or t.device != q.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32 \
+            or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor on q's device")
+    bias = _check_bias(bias, B, H, N, q.device)
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) for _ in range(3))
+    nb = (N + 63) // 64
+    dbias = torch.empty((B, H, nb, nb), dtype=torch.float32, device=q.device) if return_dbias else None
+    fn = lib().attn_bwd_noalloc
+    with torch.cuda.device(q.device):
+        st = fn(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE_CODE[o.dtype], _ptr(dout), _ptr(lse),
+                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), B, H, N, d, int(bool(causal)), float(scale), _ptr(bias),
+                _DTYPE_CODE.get(grad_dtype, -1), _stream(q.device))
     if st != 0:
         raise AttnError(st, fn.__name__)
     return (dq, dk, dv, dbias) if return_dbias else (dq, dk, dv)

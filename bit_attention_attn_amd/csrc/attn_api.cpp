@@ -14,6 +14,15 @@
 
 #include "attn_internal.hpp"
 
+// ---- fixed scratch of attn_bwd_noalloc ---------------------------------
+// Callers that cannot allocate device memory use attn_bwd_noalloc, whose one
+// scratch buffer (D = rowsum(dO * O), one fp32 per query row, fully written
+// by the first kernel of every call before any kernel reads it) lives in
+// this fixed device array: one copy per GPU, held until the process ends.
+// Calls that overlap on one GPU share it and race.
+constexpr size_t kBwdScratchBytes = (size_t)ATTN_BWD_NOALLOC_MAX_ROWS * sizeof(float);  // 16 MiB
+static __device__ __align__(256) float scratch[kBwdScratchBytes / sizeof(float)];
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
@@ -131,10 +140,15 @@ attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v
   return ATTN_OK;
 }
 
+void* bwd_scratch();
+
+// noalloc: the workspace comes from the library's fixed device array (the
+// workspace arguments are ignored; shapes that need more than it holds are
+// ATTN_ERR_WORKSPACE)
 attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const void* o, int o_dtype,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dbias, int B, int H,
                   int N, int d, int causal, float scale, const float* bias, int grad_dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, void* stream, bool noalloc = false) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return ATTN_ERR_NULL;
@@ -147,19 +161,44 @@ attn_status bwd16(bool bf16, const void* q, const void* k, const void* v, const 
   if (grad_dtype != in_dtype && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
   if (o_dtype != in_dtype && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
   if ((bias != nullptr || dbias != nullptr) && check_bias_size(B, H, N) != ATTN_OK) return ATTN_ERR_SHAPE;
-  if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_size(B, H, N, d)) return ATTN_ERR_WORKSPACE;
+  if (noalloc) {
+    if (attn_bwd_workspace_size(B, H, N, d) > kBwdScratchBytes) return ATTN_ERR_WORKSPACE;
+  } else if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_size(B, H, N, d)) {
+    return ATTN_ERR_WORKSPACE;
+  }
   for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned(ptr, 16)) return ATTN_ERR_ALIGN;
-  if (!aligned(lse, 4) || !aligned(workspace, 256) || (bias && !aligned(bias, 4)) || (dbias && !aligned(dbias, 4)))
+  if (!aligned(lse, 4) || (!noalloc && !aligned(workspace, 256)) || (bias && !aligned(bias, 4)) ||
+      (dbias && !aligned(dbias, 4)))
     return ATTN_ERR_ALIGN;
   attn_status s = check_device();
   if (s != ATTN_OK) return s;
+  if (noalloc && (workspace = bwd_scratch()) == nullptr) return ATTN_ERR_HIP;
   attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dbias, bias, static_cast<float*>(workspace),
                   B, H, N, d, causal, scale,
                   grad_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16),
                   o_dtype == ATTN_DTYPE_F32};
   if (attn::launch_bwd16(a, bf16, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+// Device address of the current device's copy of `scratch` (host code must
+// not use the array's name, which is a host-side stand-in): looked up once
+// per device, with that device current, on its first use; nullptr on a HIP
+// error.
+std::atomic<void*> g_scratch_ptr[64];
+
+void* bwd_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < 64) {
+    void* known = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (known != nullptr) return known;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+  if (dev < 64) g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
 }
 
 attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int B, int H, int N, int d,
@@ -346,6 +385,15 @@ attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const voi
                           size_t workspace_bytes, void* stream) {
   return bwd16(true, q, k, v, o, o_dtype, dout, lse, dq, dk, dv, dbias, B, H, N, d, causal, scale, bias, grad_dtype,
                workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_noalloc(int in_dtype, const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dbias, int B,
+                             int H, int N, int d, int causal, float scale, const float* bias, int grad_dtype,
+                             void* stream) {
+  if (in_dtype != ATTN_DTYPE_F16 && in_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  return bwd16(in_dtype == ATTN_DTYPE_BF16, q, k, v, o, o_dtype, dout, lse, dq, dk, dv, dbias, B, H, N, d, causal,
+               scale, bias, grad_dtype, nullptr, 0, stream, true);
 }
 
 const char* attn_status_str(int status) {

@@ -337,6 +337,28 @@ attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const voi
                           const float* bias, int grad_dtype, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * attn_bwd_noalloc -- attn_bwd_f16 / attn_bwd_bf16 (in_dtype ATTN_DTYPE_F16
+ * or ATTN_DTYPE_BF16) for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The backward's scratch (one fp32 per query row) comes from a
+ * fixed device array inside the library instead of a workspace argument:
+ * ATTN_BWD_NOALLOC_MAX_ROWS rows (16 MiB), one copy per GPU, held until the
+ * process ends.  B*H*N above that limit is ATTN_ERR_WORKSPACE.  The call
+ * allocates nothing (the array's device address is looked up once per
+ * device, on the first call with that device current).  Every call on one
+ * GPU shares its array: calls that overlap on one GPU (different streams or
+ * host threads without ordering) race and must not be issued.  Other
+ * arguments, results and errors as attn_bwd_f16 / attn_bwd_bf16, which it
+ * matches bit for bit.
+ */
+#define ATTN_BWD_NOALLOC_MAX_ROWS 4194304
+attn_status attn_bwd_noalloc(int in_dtype, const void* q, const void* k, const void* v,
+                             const void* o, int o_dtype, const void* dout, const float* lse,
+                             void* dq, void* dk, void* dv, float* dbias, int B, int H, int N,
+                             int d, int causal, float scale, const float* bias, int grad_dtype,
+                             void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_status_str(int status);
 

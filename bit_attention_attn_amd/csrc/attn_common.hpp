@@ -138,6 +138,17 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// One 16-byte buffer load per lane straight into LDS: the wave's 64 chunks
+// land at lds + 16 * lane (lds wave-uniform: it goes to M0; verified on
+// gfx950).  The LDS write happens when the load returns; the vector-memory
+// counter covers it.  The intrinsic exists only in the device pass.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                  uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8) that waits for every outstanding vector memory
 // operation and for nothing else.  Placed after a kernel's prologue loads, it

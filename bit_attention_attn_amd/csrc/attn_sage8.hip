@@ -399,17 +399,40 @@ constexpr int kNW8 = 4;                // waves per workgroup
 constexpr int kBM8 = 32 * kNW8;        // queries per workgroup
 constexpr int kThreads8 = 64 * kNW8;
 
+// K tile: 64 keys x D bytes; V tile: D rows (channels) x 64 bytes, the
+// block's keys in operand order.  Both are unpadded and filled straight from
+// global memory by 16-byte buffer loads into LDS: one instruction writes the
+// 64 consecutive 16-byte chunks of a wave, so the layout is chosen by which
+// global chunk each lane fetches.  Within a row the 16-byte chunks are
+// rotated by a per-row amount (k_rot, v_rot), so the 16-byte operand reads
+// of 16 consecutive rows at one logical chunk fall on distinct banks
+// (rows of 128 bytes: banks repeat every 2 rows, so the rotation is row/2
+// mod 8; 64 bytes: every 4 rows, row/4 mod 4; 96 bytes: rows 8 apart share
+// banks, row/8 mod 2).  The rotation depends on the row's low bits only, so
+// rows 32 apart (the two 32-key halves) rotate alike.
 template <int D>
 struct Fwd8Smem {
-  // K tile: 64 keys x D bytes, rows padded by 16 bytes (16-byte operand reads
-  // of 16 consecutive rows on distinct banks).  V tile: D rows of 64 bytes
-  // (the block's keys in operand order), padded by 16 bytes.
-  static constexpr int kKRow = D + 16;
-  static constexpr int kVRow = kQB + 16;
-  static constexpr int kKTile = kQB * kKRow;
-  static constexpr int kVTile = D * kVRow;
+  static constexpr int kKC = D / 16;  // 16-byte chunks per K row
+  static constexpr int kKTile = kQB * D;
+  static constexpr int kVTile = D * kQB;
   static constexpr int kBytes = 2 * (kKTile + kVTile);
 };
+// rotation of K row r (mod kKC) and of V row r (mod 4)
+template <int D>
+__device__ __forceinline__ int k_rot(int r) {
+  return D == 128 ? (r >> 1) & 7 : D == 64 ? (r >> 2) & 3 : (r >> 3) & 1;
+}
+__device__ __forceinline__ int v_rot(int r) { return (r >> 2) & 3; }
+// LDS byte offset of logical chunk c of K row r
+template <int D>
+__device__ __forceinline__ uint32_t k_pos(int r, int c) {
+  constexpr int C = D / 16;
+  const int x = c + k_rot<D>(r);
+  return (uint32_t)(r * D + 16 * (x >= C ? x - C : x));
+}
+__device__ __forceinline__ uint32_t v_pos(int r, int c) { return (uint32_t)(r * kQB + 16 * ((c + v_rot(r)) & 3)); }
+
+
 
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -429,8 +452,7 @@ template <int D, bool CAUSAL, bool BIAS, bool QKFP8, bool VARLEN>
 __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const float* __restrict__ bias,
                                                             const float* __restrict__ sk) {
   using S = Fwd8Smem<D>;
-  constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
-  constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
+  constexpr int kKTile = S::kKTile, kVTile = S::kVTile, kKC = S::kKC;
   constexpr int kDT = D / 32;  // 32-row tiles of O^T
   constexpr int kKS = D / 32;  // 16-byte Q chunks per lane (INT8: one per 32-deep k-step;
                                // FP8: two per 64-deep k-step)
@@ -477,34 +499,47 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   const int wave_last = CAUSAL ? min(nkb - 1, qw0 / kQB) : nkb - 1;
   const bool wave_has_rows = qw0 < N;
 
-  // loader: K tile 64*D bytes and V tile D*64 bytes, 16-byte chunks; chunk
-  // tid + i*threads of block kb is at byte 16*tid + (kb*64*D + 16*i*threads)
-  // of the head (buffer loads: one per-lane offset, a uniform one)
+  // loader: K tile 64*D bytes and V tile D*64 bytes, 16-byte chunks written
+  // straight into LDS.  Round i of wave w fills LDS chunks i*256 + 64w ..
+  // +63 of a tile; lane l fetches the global chunk that belongs at LDS chunk
+  // i*256 + tid (row p / kKC, inverse rotation for K; row p / 4 for V).
+  // The per-lane byte offsets inside a block are fixed; the block offset
+  // kb*64*D is uniform (buffer loads: base and size in scalar registers).
   constexpr int kChunks = kQB * D / 16;  // 16-byte chunks per tile
   constexpr int kNld = (kChunks + kThreads8 - 1) / kThreads8;
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kq, (uint32_t)p.np * D);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vq, (uint32_t)p.np * D);
-  const uint32_t voff = 16u * tid;
-  u32x4_t kst[kNld], vst[kNld];
-  auto load_kv = [&](int kb) {
+  uint32_t kvo[kNld], vvo[kNld];
+#pragma unroll
+  for (int i = 0; i < kNld; ++i) {
+    const int pc = i * kThreads8 + tid;
+    const int kr = pc / kKC, kp = pc % kKC;
+    int kc = kp - k_rot<D>(kr);
+    kc = kc < 0 ? kc + kKC : kc;
+    kvo[i] = (uint32_t)(kr * D + 16 * kc);
+    const int vr = pc / 4;
+    vvo[i] = (uint32_t)(vr * kQB + 16 * ((pc - v_rot(vr)) & 3));
+  }
+  auto load_kv = [&](int kb, int buf) {
 #pragma unroll
     for (int i = 0; i < kNld; ++i) {
-      if (kChunks % kThreads8 != 0 && tid + i * kThreads8 >= kChunks) continue;
-      kst[i] = buffer_load16(krs, voff, kb * kQB * D + 16 * i * kThreads8);
-      vst[i] = buffer_load16(vrs, voff, kb * kQB * D + 16 * i * kThreads8);
+      if (kChunks % kThreads8 != 0 && i * kThreads8 + wave * 64 >= kChunks) continue;  // wave-uniform
+      const int c0 = 16 * (i * kThreads8 + wave * 64);
+      buffer_load16_lds(krs, kl + buf * kKTile + c0, kvo[i], kb * kQB * D);
+      buffer_load16_lds(vrs, vl + buf * kVTile + c0, vvo[i], kb * kQB * D);
     }
   };
-  auto store_kv = [&](int buf) {
+  // operand read offsets inside a tile: K rows 32T + l32 at the logical
+  // chunks of k-step kk (INT8: 2kk + hf; FP8: 4kk + 2hf and +1), V rows
+  // 32dt + l32 at chunks 2hf and 2hf + 1
+  // (row 32 + l32 rotates like row l32: the second 32-row half is 32*D
+  // bytes further)
+  uint32_t ko[kKS];
 #pragma unroll
-    for (int i = 0; i < kNld; ++i) {
-      const int idx = tid + i * kThreads8;
-      if (kChunks % kThreads8 != 0 && idx >= kChunks) continue;
-      const int kr = idx / (D / 16), kc = idx % (D / 16);
-      *(u32x4_t*)(kl + buf * kKTile + kr * kKRow + kc * 16) = kst[i];
-      const int vr = idx / (kQB / 16), vc = idx % (kQB / 16);
-      *(u32x4_t*)(vl + buf * kVTile + vr * kVRow + vc * 16) = vst[i];
-    }
-  };
+  for (int kk = 0; kk < kKS; ++kk)
+    ko[kk] = QKFP8 ? k_pos<D>(l32, 4 * (kk >> 1) + 2 * hf + (kk & 1)) : k_pos<D>(l32, 2 * kk + hf);
+  auto kofs = [&](int T, int kk) -> uint32_t { return ko[kk] + 32 * T * D; };
+  const uint32_t vo0 = v_pos(l32, 2 * hf), vo1 = v_pos(l32, 2 * hf + 1);
 
   f32x16_t o[kDT];
 #pragma unroll
@@ -527,20 +562,20 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   // staged in buffer buf, computes; braw is this wave's bias of block jc
   auto step = [&](int jc, int jn, int buf, float braw) {
     const bool more = jn < nkb;
-    if (more) load_kv(jn);
+    if (more) load_kv(jn, buf ^ 1);
     if (wave_has_rows && jc <= wave_last && (!BIAS || braw != -INFINITY)) {
       f32x16_t s[2];
       if constexpr (QKFP8) {
         // ---- S^T = Kq Qq^T in fp32 from e4m3 codes (A: 32 bytes of a K
         // row per 64-deep step, B: the matching 32 bytes of the Q row)
-        const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 32 * hf;
+        const uint8_t* Ks = kl + buf * kKTile;
         s[0] = s[1] = f32x16_t{};
 #pragma unroll
         for (int kk = 0; kk < kKS / 2; ++kk)
 #pragma unroll
           for (int T = 0; T < 2; ++T) {
-            const u32x4_t a0 = *(const u32x4_t*)(Ks + 32 * T * kKRow + 64 * kk);
-            const u32x4_t a1 = *(const u32x4_t*)(Ks + 32 * T * kKRow + 64 * kk + 16);
+            const u32x4_t a0 = *(const u32x4_t*)(Ks + kofs(T, 2 * kk));
+            const u32x4_t a1 = *(const u32x4_t*)(Ks + kofs(T, 2 * kk + 1));
             const u32x4_t b0 = qf[2 * kk], b1 = qf[2 * kk + 1];
             const i32x8_t aop = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                  (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
@@ -550,7 +585,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
           }
       } else {
         // ---- S^T = Kq Qq^T on top of the offset, exact
-        const uint8_t* Ks = kl + buf * kKTile + l32 * kKRow + 16 * hf;
+        const uint8_t* Ks = kl + buf * kKTile;
         i32x16_t si[2];
 #pragma unroll
         for (int T = 0; T < 2; ++T)
@@ -560,7 +595,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
         for (int kk = 0; kk < kKS; ++kk)
 #pragma unroll
           for (int T = 0; T < 2; ++T) {
-            const u32x4_t a = *(const u32x4_t*)(Ks + 32 * T * kKRow + 32 * kk);
+            const u32x4_t a = *(const u32x4_t*)(Ks + kofs(T, kk));
             si[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
                                                           __builtin_bit_cast(i32x4_t, qf[kk]), si[T], 0, 0, 0);
           }
@@ -623,17 +658,18 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
       const i32x8_t bop = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                            (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
       // ---- O^T += Vq^T P^T over the 64 keys (one FP8 instruction per d tile)
-      const uint8_t* Vs = vl + buf * kVTile + l32 * kVRow + 32 * hf;
+      const uint8_t* Vs = vl + buf * kVTile;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
-        const u32x4_t a0v = *(const u32x4_t*)(Vs + 32 * dt * kVRow);
-        const u32x4_t a1v = *(const u32x4_t*)(Vs + 32 * dt * kVRow + 16);
+        const u32x4_t a0v = *(const u32x4_t*)(Vs + 32 * dt * kQB + vo0);
+        const u32x4_t a1v = *(const u32x4_t*)(Vs + 32 * dt * kQB + vo1);
         const i32x8_t aop = {(int)a0v[0], (int)a0v[1], (int)a0v[2], (int)a0v[3],
                              (int)a1v[0], (int)a1v[1], (int)a1v[2], (int)a1v[3]};
         o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, o[dt], 0, 0, 0, 0, 0, 0);
       }
     }
-    if (more) store_kv(buf ^ 1);
+    // the next block's loads into LDS are complete before any wave reads them
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
   // The first block is staged unconditionally (a valid block even when every
@@ -644,8 +680,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   int j0 = 0;
   if constexpr (BIAS) j0 = gate.first();
   __builtin_amdgcn_sched_barrier(0);
-  load_kv(min(j0, nkb - 1));
-  store_kv(0);
+  load_kv(min(j0, nkb - 1), 0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   if constexpr (BIAS) {

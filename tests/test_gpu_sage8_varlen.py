@@ -153,3 +153,30 @@ def test_packed_rejects_bias_and_layout():
         attn.fwd_sage8(prep, bias=bias)
     with pytest.raises(ValueError):
         attn.sage8_prep_varlen(q, k, v, cu.long(), 65)
+
+
+def test_packed_against_oracle():
+    """One packed batch held to the oracle directly: each sequence's rows
+    against the kernel-precision model of the recipe fed the oracle's own
+    quantisation of that sequence alone (reading: each sequence is prepared
+    on its own; max abs 1e-3, the contiguous path's bar), and against the
+    exact fp64 attention of that sequence (cosine >= 0.999 where it has at
+    least 64 keys)."""
+    lens, H, d = [70, 1, 200, 129], 2, 128
+    q, k, v, cu = _packed(lens, H, d, "bf16", seed=29)
+    o = attn.sageattn_varlen(q, k, v, cu, max(lens), causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        qs, ks, vs = (_seq(x, cu, b).float().cpu().numpy() for x in (q, k, v))
+        ref = oracle.sage8_prepare(qs, ks, vs)
+        rows = np.array([(0, h, i) for h in range(H) for i in range(n)], dtype=np.int64)
+        o_emu, _ = oracle.sage8_emulate_rows_fp32(ref, rows, causal=True, scale=1 / d ** 0.5)
+        t0 = int(cu[b])
+        got = o[t0:t0 + n].transpose(0, 1).reshape(-1, d).double().cpu().numpy()
+        m = workloads.error_metrics(got, o_emu)
+        assert m["max_abs"] <= 1e-3 and m["mean_abs"] <= 5e-5, (b, m)
+        if n >= 64:
+            o_ref, _ = oracle.attn_rows(qs, ks, vs, rows, causal=True, scale=1 / d ** 0.5)
+            m_ref = workloads.error_metrics(got, o_ref)
+            print(f"    packed sequence {b} (n={n}) vs fp32 model: {m}; vs fp64 attention: {m_ref}", flush=True)
+            assert m_ref["cos"] >= 0.999, (b, m_ref)

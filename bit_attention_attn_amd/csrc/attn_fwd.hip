@@ -85,21 +85,52 @@ struct Fwd16Params {
   int np, nblk;
 };
 
+// K and V tiles of one 64-key block, unpadded and filled straight from
+// global memory by 16-byte buffer loads into LDS: one instruction writes the
+// 64 consecutive 16-byte chunks of a wave, so the layout is set by which
+// global chunk each lane fetches.  Within a row the 16-byte chunks are
+// rotated by a per-row amount so that the operand reads spread over the
+// banks:
+//   K (16-bit, read 16 bytes per lane, 16 consecutive rows at one logical
+//     chunk): rows of 256 bytes (d = 128) all start on bank 0, so the chunk
+//     rotates by r mod 16; rows of 128 bytes (d = 64) repeat every 2 rows,
+//     r/2; rows of 192 bytes (d = 96) every 4 rows, r/4.
+//   K (INT8, Q8 kernels): rows of D bytes, rotated by r/2 (d = 128), r/4
+//     (d = 64), r/8 (d = 96).
+//   V (16-bit, transposing reads: each group of 16 lanes reads 4 consecutive
+//     rows, 32 bytes each): rows of 256 bytes rotate by 4(r mod 4) chunks,
+//     rows of 128 bytes by 4((r/2) mod 2); rows of 192 bytes already start
+//     on different banks.
+// Every rotation is a function of the row's low bits only, so it is the same
+// for rows 32 apart (the two 32-key halves) and 8 or 16 apart (the two
+// halves of a transposing read, successive k-steps): one per-lane offset per
+// logical chunk serves all of them.
 template <int D, int QS, int NW, bool Q8 = false>
 struct Fwd16Smem {
   using T = Tiling<QS, NW>;
-  // Padded rows.  K: 16 bytes of padding, so the 16-byte operand reads of 16
-  // consecutive rows fall on distinct banks.  V: the transposing reads touch
-  // 4 consecutive rows x 64 bytes per half wave; a row stride of 288 bytes
-  // (d = 128) or 192 bytes (d = 64) spreads them over the banks (measured
-  // on gfx950: 107 B/clk/CU against 62 B/clk/CU at a 272-byte stride).
-  // (INT8 K, Q8 kernels: D + 16 bytes per row, i.e. D/2 + 8 elements)
-  static constexpr int kKRow = Q8 ? D / 2 + 8 : D + 8;
-  // V rows of 288 bytes at d = 128 and 96, 192 bytes at d = 64
-  static constexpr int kVRow = D == 64 ? D + 32 : 144;
-  static constexpr int kKTile = kBN * kKRow;
-  static constexpr int kVTile = kBN * kVRow;
-  static constexpr int kElems = T::kKbuf * kKTile + T::kVbuf * kVTile;
+  static constexpr int kKRowB = Q8 ? D : 2 * D;  // bytes per K row
+  static constexpr int kVRowB = 2 * D;           // bytes per V row
+  static constexpr int kKC = kKRowB / 16;        // 16-byte chunks per K row
+  static constexpr int kVC = kVRowB / 16;        // 16-byte chunks per V row
+  static constexpr int kKTile = kBN * kKRowB;    // bytes
+  static constexpr int kVTile = kBN * kVRowB;
+  static constexpr int kBytes = T::kKbuf * kKTile + T::kVbuf * kVTile;
+  __device__ static __forceinline__ int k_rot(int r) {
+    if constexpr (Q8) return D == 128 ? (r >> 1) & 7 : D == 64 ? (r >> 2) & 3 : (r >> 3) & 1;
+    else return D == 128 ? r & 15 : D == 64 ? (r >> 1) & 7 : (r >> 2) & 3;
+  }
+  __device__ static __forceinline__ int v_rot(int r) {
+    return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
+  }
+  // LDS byte offsets of logical 16-byte chunk c of row r
+  __device__ static __forceinline__ uint32_t k_pos(int r, int c) {
+    const int x = c + k_rot(r);
+    return (uint32_t)(r * kKRowB + 16 * (x >= kKC ? x - kKC : x));
+  }
+  __device__ static __forceinline__ uint32_t v_pos(int r, int c) {
+    const int x = c + v_rot(r);
+    return (uint32_t)(r * kVRowB + 16 * (x >= kVC ? x - kVC : x));
+  }
 };
 
 // Kernel variants by input layout: contiguous without a bias (the plain loop
@@ -126,16 +157,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   using TL = Tiling<QS, NW>;
   using S = Fwd16Smem<D, QS, NW, Q8>;
   constexpr int kWQ = TL::kWQ, kBM = TL::kBM, kThreads = TL::kThreads;
-  constexpr int kKbuf = TL::kKbuf, kVbuf = TL::kVbuf;
-  constexpr int kKRow = S::kKRow, kVRow = S::kVRow;
+  constexpr int kKbuf = TL::kKbuf;
   constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
   constexpr int kCpr = D / 8;  // 16-byte chunks of data per row
   constexpr int kDT = D / 32;  // 32-row tiles of O^T
   constexpr int kKS = D / 16;  // k-steps of S^T = K Q^T (Q8: D/32 of them)
-  constexpr int kChunksK = Q8 ? kBN * D / 16 : kBN * kCpr;  // 16-byte chunks of a K tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[S::kElems];
-  uint16_t* const kbase_lds = smem;                   // kKbuf K tiles
-  uint16_t* const vbase_lds = smem + kKbuf * kKTile;  // kVbuf V tiles
+  constexpr int kChunksK = kBN * S::kKC, kChunksV = kBN * S::kVC;  // 16-byte chunks per tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::kBytes];
+  uint8_t* const kbase_lds = smem;                   // kKbuf K tiles
+  uint8_t* const vbase_lds = smem + kKbuf * kKTile;  // kVbuf V tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,14 +177,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // balanced heavy-first order when the grid is persistent).
   const WorkQueue wq = work_queue(p.nbh, p.nq);
   constexpr bool DENSE = MODE == kDense;
-  constexpr int kNst = kBN * kCpr / kThreads;
+  constexpr int kNK = (kChunksK + kThreads - 1) / kThreads, kNV = kChunksV / kThreads;
+  static_assert(kChunksV % kThreads == 0, "V tiles split evenly over the threads");
   u32x4_t qf[QS][kKS];
-  u32x4_t kst[kNst], vst[kNst];
   // Dense layout without a bias: the next work item's Q rows and first K/V
   // block are loaded during the current item's last block, so a new item
-  // starts without waiting for global memory (pre: qf and kst/vst already
-  // hold this item's Q and block 0).
+  // starts without waiting for global memory (pre: qf and the LDS buffer b0
+  // already hold this item's Q and block 0).
   bool pre = false;
+  int b0 = 0;  // LDS buffer of the item's first block
   for (int round = 0;; ++round) {
   int bh, tq;
   if (!work_item(wq, round, p.nq, bh, tq)) break;
@@ -223,72 +254,60 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   const int wave_last = CAUSAL ? min(nkb - 1, qw0 / kBN) : nkb - 1;
   const bool wave_has_rows = qw0 < N;
 
-  // ---- loader: a 64 x D tile is 64*D/8 chunks of 16 bytes, staged through
-  // registers.  Chunk tid + i*threads of block kb sits at byte
-  // 16*tid + (kb*64*D*2 + 16*i*threads) of the head: a buffer load with one
-  // per-lane offset and a uniform one; key rows past N read zeros (masked
-  // later), so every load is unconditional.
-  // (general layout: key rows ksn / vsn elements apart, so each chunk has its
-  // own per-lane offset and the block offset is kb*64 rows)
+  // ---- loader: 16-byte buffer loads straight into LDS.  Round i of wave w
+  // fills LDS chunks i*threads + 64w .. +63 of a tile; lane l fetches the
+  // global chunk that belongs at LDS chunk p = i*threads + tid (row p / C,
+  // logical chunk by the inverse rotation).  The per-lane byte offsets inside
+  // a block are fixed; the block offset kb*64 rows is uniform.  Key rows past
+  // N read zeros (the buffer descriptor's range check), so every load is
+  // unconditional and the V rows past N hold zeros.
+  const int krb = Q8 ? D : 2 * ksn, vrb = 2 * vsn;  // global bytes between K / V rows
   const __amdgpu_buffer_rsrc_t krs =
       Q8 ? buffer_rsrc(p.kq + (size_t)bh * p.np * D, (uint32_t)p.np * D) : buffer_rsrc(K, (uint32_t)N * ksn * 2);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V, (uint32_t)N * vsn * 2);
-  const uint32_t voff = 16u * tid;
-  uint32_t kvo[kNst], vvo[kNst];
-  if constexpr (GEN) {
+  uint32_t kvo[kNK], vvo[kNV];
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
-      kvo[i] = (uint32_t)(row * ksn * 2 + ch * 16);
-      vvo[i] = (uint32_t)(row * vsn * 2 + ch * 16);
-    }
+  for (int i = 0; i < kNK; ++i) {
+    const int pc = i * kThreads + tid, row = pc / S::kKC;
+    int c = pc % S::kKC - S::k_rot(row);
+    c = c < 0 ? c + S::kKC : c;
+    kvo[i] = (uint32_t)(row * krb + 16 * c);
   }
-  auto load_k = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      if constexpr (Q8) {
-        if (i * kThreads >= kChunksK) break;
-        if (kChunksK % kThreads != 0 && tid + i * kThreads >= kChunksK) continue;
-        kst[i] = buffer_load16(krs, voff, kb * kBN * D + 16 * i * kThreads);
-      } else if constexpr (GEN) {
-        kst[i] = buffer_load16(krs, kvo[i], (uint32_t)(kb * kBN) * ksn * 2);
-      } else {
-        kst[i] = buffer_load16(krs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
-      }
-    }
-  };
-  auto load_v = [&](int kb) {
+  for (int i = 0; i < kNV; ++i) {
+    const int pc = i * kThreads + tid, row = pc / S::kVC;
+    int c = pc % S::kVC - S::v_rot(row);
+    c = c < 0 ? c + S::kVC : c;
+    vvo[i] = (uint32_t)(row * vrb + 16 * c);
+  }
+  auto load_kv = [&](int kb, int buf) {
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      if constexpr (GEN) vst[i] = buffer_load16(vrs, vvo[i], (uint32_t)(kb * kBN) * vsn * 2);
-      else vst[i] = buffer_load16(vrs, voff, kb * kBN * D * 2 + 16 * i * kThreads);
+    for (int i = 0; i < kNK; ++i) {
+      if (kChunksK % kThreads != 0 && i * kThreads + wave * 64 >= kChunksK) continue;  // wave-uniform
+      buffer_load16_lds(krs, kbase_lds + buf * kKTile + 16 * (i * kThreads + wave * 64), kvo[i],
+                        (uint32_t)(kb * kBN) * krb);
     }
-  };
-  auto store_k = [&](int buf) {
-    uint16_t* ks = kbase_lds + buf * kKTile;
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      const int idx = tid + i * kThreads;
-      if constexpr (Q8) {
-        // INT8 rows of D bytes: D/16 chunks per row
-        if (i * kThreads >= kChunksK) break;
-        if (kChunksK % kThreads != 0 && idx >= kChunksK) continue;
-        const int row = idx / (D / 16), ch = idx % (D / 16);
-        *(u32x4_t*)(reinterpret_cast<uint8_t*>(ks) + row * kKRow * 2 + ch * 16) = kst[i];
-      } else {
-        const int row = idx / kCpr, ch = idx % kCpr;
-        *(u32x4_t*)(ks + row * kKRow + ch * 8) = kst[i];
-      }
-    }
+    for (int i = 0; i < kNV; ++i)
+      buffer_load16_lds(vrs, vbase_lds + buf * kVTile + 16 * (i * kThreads + wave * 64), vvo[i],
+                        (uint32_t)(kb * kBN) * vrb);
   };
-  auto store_v = [&](int buf) {
-    uint16_t* vs = vbase_lds + buf * kVTile;
+
+  // operand read offsets inside a tile (the rotation depends on the row's
+  // low bits only): K row l32 at logical chunk 2kk + hf (16-bit: 8 elements
+  // per k-step of 16; INT8: 16 bytes per k-step of 32), the other 32-row
+  // half 32 rows further; V row vkey (the transposing read's row, k-step
+  // rows 16 further, the second half 8 further) at the chunk holding column
+  // 32dt + vcol.
+  const int g16 = lane >> 4, t16 = lane & 15;
+  const int vkey = 4 * hf + (t16 >> 2);
+  const int vcol = 16 * (g16 & 1) + 4 * (t16 & 3);
+  uint32_t ko[kKS];
 #pragma unroll
-    for (int i = 0; i < kNst; ++i) {
-      const int idx = tid + i * kThreads, row = idx / kCpr, ch = idx % kCpr;
-      *(u32x4_t*)(vs + row * kVRow + ch * 8) = vst[i];
-    }
-  };
+  for (int kk = 0; kk < kKS; ++kk) ko[kk] = S::k_pos(l32, 2 * kk + hf);
+  uint32_t vo[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) vo[dt] = S::v_pos(vkey, (32 * dt + vcol) / 8) + 2 * (vcol % 8);
 
   // ---- per-wave online-softmax state
   f32x16_t o[kDT][QS];
@@ -304,18 +323,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
 
-  // transposing-read coordinates for the V^T operand: this lane addresses row
-  // 16kk + vkey (and +8) at column 32dt + vcol
-  const int g16 = lane >> 4, t16 = lane & 15;
-  const int vkey = 4 * hf + (t16 >> 2);
-  const int vcol = 16 * (g16 & 1) + 4 * (t16 & 3);
 
   // ---- S^T = K Q^T for one key block (two 32-key tiles x QS query tiles)
   auto qk = [&](int buf, f32x16_t (&s)[2][QS]) {
     if constexpr (Q8) {
       // S^T = Kq Qq^T on top of the offset, exact (A: 16 bytes of a K row per
       // 32-deep step, B: the matching bytes of the Q row)
-      const uint8_t* Ks8 = reinterpret_cast<const uint8_t*>(kbase_lds + buf * kKTile) + l32 * kKRow * 2 + 16 * hf;
+      const uint8_t* Ks8 = kbase_lds + buf * kKTile;
       i32x16_t si[2][QS];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-          const u32x4_t a = *(const u32x4_t*)(Ks8 + 32 * T * kKRow * 2 + 32 * kk);
+          const u32x4_t a = *(const u32x4_t*)(Ks8 + ko[kk] + 32 * T * S::kKRowB);
 #pragma unroll
           for (int qs = 0; qs < QS; ++qs)
             si[T][qs] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
         for (int qs = 0; qs < QS; ++qs) s[T][qs] = __builtin_bit_cast(f32x16_t, si[T][qs]);
       return;
     }
-    const uint16_t* Ks = kbase_lds + buf * kKTile + l32 * kKRow + 8 * hf;
+    const uint8_t* Ks = kbase_lds + buf * kKTile;
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) s[0][qs] = s[1][qs] = f32x16_t{};
 #pragma unroll
@@ -348,7 +362,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         // row 32T + l32, columns 16kk + 8hf .. +7
-        const u32x4_t a = *(const u32x4_t*)(Ks + 32 * T * kKRow + 16 * kk);
+        const u32x4_t a = *(const u32x4_t*)(Ks + ko[kk] + 32 * T * S::kKRowB);
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) s[T][qs] = mfma32x32x16<BF16>(a, qf[qs][kk], s[T][qs]);
       }
@@ -440,14 +454,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
     }
   };
   auto pv = [&](int buf) {
-    const uint16_t* Vs = vbase_lds + buf * kVTile + vkey * kVRow + vcol;
+    const uint8_t* Vs = vbase_lds + buf * kVTile;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
-        const uint16_t* vp = Vs + 16 * kk * kVRow + 32 * dt;
+        const uint8_t* vp = Vs + vo[dt] + 16 * kk * S::kVRowB;
         const u32x2_t lo = lds_read_tr16(vp);
-        const u32x2_t hi = lds_read_tr16(vp + 8 * kVRow);
+        const u32x2_t hi = lds_read_tr16(vp + 8 * S::kVRowB);
         const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) o[dt][qs] = mfma32x32x16<BF16>(a, pb[kk][qs], o[dt][qs]);
@@ -469,10 +483,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   // staged in buffer buf, computes; braw is this wave's bias of block jc
   auto step = [&](int jc, int jn, int buf, float braw) {
     const bool more = jn < nkb;
-    if (more) {
-      load_k(jn);
-      load_v(jn);
-    }
+    if (more) load_kv(jn, buf ^ 1);
     if (wave_has_rows && jc <= wave_last && (!HAS_BIAS || braw != -INFINITY)) {
       qk(buf, sc);
       if (needs_mask(jc)) apply_mask(jc, sc);
@@ -482,10 +493,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       softmax_p(sc, kc, cf);
       pv(buf);
     }
-    if (more) {
-      store_k(buf ^ 1);
-      store_v(buf ^ 1);
-    }
+    // the next block's loads into LDS are complete before any wave reads them
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
   // The first block is staged unconditionally (a valid block even when every
@@ -497,11 +506,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   if constexpr (HAS_BIAS) j0 = gate.first();
   __builtin_amdgcn_sched_barrier(0);
   if (!(DENSE && pre)) {
-    load_k(min(j0, nkb - 1));
-    load_v(min(j0, nkb - 1));
+    b0 = 0;
+    load_kv(min(j0, nkb - 1), 0);
   }
-  store_k(0);
-  store_v(0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   if constexpr (HAS_BIAS) {
@@ -521,22 +528,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   } else {
     // every block is active (the plain counted loop schedules measurably
     // better than the general one)
-    for (int j = 0; j + 1 < nkb; ++j) step(j, j + 1, j & 1, 0.f);
+    for (int j = 0; j + 1 < nkb; ++j) step(j, j + 1, (b0 + j) & 1, 0.f);
     // the last block: the next item's Q rows and first K/V block are
     // loaded meanwhile (Q after this block's last use of it)
     {
-      const int jc = nkb - 1, buf = jc & 1;
+      const int jc = nkb - 1, buf = (b0 + jc) & 1;
       const int qt_n = CAUSAL ? p.nq - 1 - tq_n : tq_n;
       const int qw0_n = qt_n * kBM + wave * kWQ;
       const size_t off_n = (size_t)bh_n * N * D;
       if (has_next) {
+        // the next item's block 0 into the other buffer, free since this
+        // item's second-to-last block
         const __amdgpu_buffer_rsrc_t krn = buffer_rsrc(p.k + off_n, (uint32_t)N * D * 2);
         const __amdgpu_buffer_rsrc_t vrn = buffer_rsrc(p.v + off_n, (uint32_t)N * D * 2);
 #pragma unroll
-        for (int i = 0; i < kNst; ++i) {
-          kst[i] = buffer_load16(krn, voff, 16 * i * kThreads);
-          vst[i] = buffer_load16(vrn, voff, 16 * i * kThreads);
-        }
+        for (int i = 0; i < kNK; ++i)
+          buffer_load16_lds(krn, kbase_lds + (buf ^ 1) * kKTile + 16 * (i * kThreads + wave * 64), kvo[i], 0);
+#pragma unroll
+        for (int i = 0; i < kNV; ++i)
+          buffer_load16_lds(vrn, vbase_lds + (buf ^ 1) * kVTile + 16 * (i * kThreads + wave * 64), vvo[i], 0);
       }
       const bool work = wave_has_rows && jc <= wave_last;
       if (work) qk(buf, sc);
@@ -608,6 +618,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
     }
   }
   pre = has_next;
+  b0 = (b0 + nkb) & 1;
   }  // work items
 }
 

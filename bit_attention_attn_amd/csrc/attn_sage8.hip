@@ -258,7 +258,11 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   constexpr int kPass = kQB / kRows;      // passes over the 64-row block
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t vt[D][kQB];  // transposed, permuted V codes
-  const int blk = blockIdx.x, bh = blockIdx.y;
+  // heads in reverse order: the column statistics pass ran head by head, so
+  // its last heads' K and V are the ones most likely still in the device's
+  // last-level cache when this pass reads them again (measured: 3.8% less
+  // time at 1x32x32768 and 4x32x4096, d = 128)
+  const int blk = blockIdx.x, bh = gridDim.y - 1 - blockIdx.y;
   const int tid = threadIdx.x, ch = tid % kCpr, rg = tid / kCpr;
   const int b = bh / in.H, h = bh - b * in.H;
   int64_t qb0, kb0, vb0;

@@ -129,10 +129,11 @@ def _stats(ms):
     return dict(ms_avg=round(sum(ms) / len(ms), 4), ms_median=round(ms[len(ms) // 2], 4), ms_min=round(ms[0], 4))
 
 
-def prep_bytes(B, H, N, d):
+def prep_bytes(B, H, N, d, with_v=True):
     """Algorithmic bytes of the 8-bit preparation: Q, K, V (2 bytes) read
-    once, Qq, Kq, Vq (1 byte) written once; scales and means are < 0.1%."""
-    return B * H * N * d * (3 * 2 + 3 * 1)
+    once, Qq, Kq, Vq (1 byte) written once (without V: Q, K read, Qq, Kq
+    written); scales and means are < 0.1%."""
+    return B * H * N * d * ((3 * 2 + 3 * 1) if with_v else (2 * 2 + 2 * 1))
 
 
 def cpu_baseline(inp, cfg, seconds):
@@ -186,10 +187,10 @@ def profile_one(args):
         def fn():
             return attn.bwd(q, k, v, o, dout, lse, causal=cfg["causal"], bias=bias, return_dbias=bias is not None)
     elif args.path == "sage8pv16":
-        ws = attn.sage8_prep(q, k, v).workspace
+        ws = attn.sage8_prep(q, k, v, qk="int8_no_v").workspace
 
         def fn():
-            prep = attn.sage8_prep(q, k, v, workspace=ws)
+            prep = attn.sage8_prep(q, k, v, workspace=ws, qk="int8_no_v")
             return attn.fwd_sage8_pv16(prep, v, causal=cfg["causal"], bias=bias, out_dtype=out_dtype)
     else:
         ws = attn.sage8_prep(q, k, v).workspace
@@ -247,7 +248,7 @@ def sage8_paths(attn, q, k, v, causal, bias, F, t16_ms, stream):
     recipe), FP8 scores with FP8 P and V, INT8 scores with the 16-bit P V."""
     res = {}
     shape = tuple(q.shape)
-    for name, qk in (("int8_qk_fp8_pv", "int8"), ("fp8_qk_fp8_pv", "fp8"), ("int8_qk_16bit_pv", "int8")):
+    for name, qk in (("int8_qk_fp8_pv", "int8"), ("fp8_qk_fp8_pv", "fp8"), ("int8_qk_16bit_pv", "int8_no_v")):
         ws = attn.sage8_prep(q, k, v, qk=qk).workspace
         prep = attn.Sage8Prepared(ws, shape, q.dtype, qk=qk)
         fp = lambda: attn.sage8_prep(q, k, v, workspace=ws, qk=qk)  # noqa: E731
@@ -265,7 +266,8 @@ def sage8_paths(attn, q, k, v, causal, bias, F, t16_ms, stream):
         tfe = F / ((s8["ms_avg"] + sp["ms_avg"]) * 1e-3) / 1e12
         res[name] = {"attention": {**s8, "tflops": round(tf8, 2), "peak": round(peak, 1),
                                    "frac_of_peak": round(tf8 / peak, 4)},
-                     "prep": {**sp, "GBs": round(prep_bytes(*shape) / (sp["ms_avg"] * 1e-3) / 1e9, 1)},
+                     "prep": {**sp, "GBs": round(prep_bytes(*shape, with_v=qk != "int8_no_v") / (sp["ms_avg"] * 1e-3)
+                                                 / 1e9, 1)},
                      "tflops_prep_plus_attention": round(tfe, 2)}
         if t16_ms is not None:
             res[name]["speedup_vs_bf16_attention"] = round(t16_ms / s8["ms_avg"], 3)

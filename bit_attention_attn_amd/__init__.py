@@ -348,13 +348,14 @@ class Sage8Prepared:
         self.workspace = workspace
         self.shape = tuple(shape)
         self.in_dtype = in_dtype
-        self.qk = qk  # "int8", or "fp8" for the FP8-QK variant
+        self.qk = qk  # "int8", "fp8" (the FP8-QK variant) or "int8_no_v" (no V prepared)
         # packed sequences: the int32 [B+1] offsets and the packed token count
         self.cu_seqlens = cu_seqlens
         self.total = total
 
 
-_QK_FORMAT = {"int8": 0, "fp8": 1}
+# "int8_no_v": the INT8 Q and K only (for fwd_sage8_pv16, which reads no FP8 V)
+_QK_FORMAT = {"int8": 0, "fp8": 1, "int8_no_v": 2}
 
 
 def sage8_prep(q, k, v, workspace=None, qk="int8"):
@@ -362,10 +363,11 @@ def sage8_prep(q, k, v, workspace=None, qk="int8"):
     q, k, v are logical [B,H,N,d] tensors, contiguous or any layout with d
     contiguous (e.g. x.transpose(1, 2) of a token-major [B,N,H,d] tensor).
     qk="fp8" quantises Q and K to e4m3 blocks (the FP8-QK variant, d = 64 or
-    128) instead of INT8; fwd_sage8 then uses FP8 scores."""
+    128) instead of INT8; fwd_sage8 then uses FP8 scores.  qk="int8_no_v"
+    prepares the INT8 Q and K only (the same codes), for fwd_sage8_pv16."""
     if qk not in _QK_FORMAT:
-        raise ValueError('qk must be "int8" or "fp8"')
-    contiguous = all(isinstance(t, torch.Tensor) and t.is_contiguous() for t in (q, k, v))
+        raise ValueError('qk must be "int8", "fp8" or "int8_no_v"')
+    contiguous = qk != "int8_no_v" and all(isinstance(t, torch.Tensor) and t.is_contiguous() for t in (q, k, v))
     if contiguous:
         _check_qkv(q, k, v)
     else:
@@ -400,7 +402,7 @@ def sage8_prep_varlen(q, k, v, cu_seqlens, max_seqlen, workspace=None, qk="int8"
     cu_seqlens[b] .. cu_seqlens[b+1]-1), max_seqlen the longest length.  Each
     sequence is prepared on its own (its K mean, V scales and 64-row blocks),
     into slot b of a [B,H,max_seqlen,d] workspace."""
-    if qk not in _QK_FORMAT:
+    if qk not in ("int8", "fp8"):
         raise ValueError('qk must be "int8" or "fp8"')
     _check_views((q, k, v), 3)
     if k.shape != q.shape or v.shape != q.shape:
@@ -436,6 +438,8 @@ def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtyp
     packed = prep.cu_seqlens is not None
     if packed and (bias is not None or layout_like is not None):
         raise ValueError("packed sequences take neither a bias nor layout_like")
+    if prep.qk == "int8_no_v":
+        raise ValueError("this preparation holds no FP8 V: use fwd_sage8_pv16")
     bias = _check_bias(bias, B, H, N, dev)
     out_dtype = prep.in_dtype if out_dtype is None else out_dtype
     if scale is None:
@@ -491,8 +495,8 @@ def fwd_sage8_pv16(prep: Sage8Prepared, v, causal=False, scale=None, bias=None, 
     contiguous [B,H,N,d] V that was prepared.  O is contiguous [B,H,N,d]."""
     B, H, N, d = prep.shape
     dev = prep.workspace.device
-    if prep.qk != "int8" or prep.cu_seqlens is not None:
-        raise ValueError("the 16-bit P V variant takes a contiguous INT8 preparation")
+    if prep.qk not in ("int8", "int8_no_v") or prep.cu_seqlens is not None:
+        raise ValueError("the 16-bit P V variant takes an INT8 preparation of unpacked sequences")
     if (not isinstance(v, torch.Tensor) or tuple(v.shape) != (B, H, N, d) or not v.is_contiguous()
             or v.dtype != prep.in_dtype or v.device != dev):
         raise ValueError("v must be the contiguous [B,H,N,d] V of the preparation, in its dtype")
@@ -515,7 +519,7 @@ def sageattn_pv16(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, 
     """INT8 scores with the 16-bit P V product in one call: the 8-bit
     preparation of contiguous [B,H,N,d] q, k, v, then fwd_sage8_pv16."""
     _check_qkv(q, k, v)
-    prep = sage8_prep(q, k, v)
+    prep = sage8_prep(q, k, v, qk="int8_no_v")
     return fwd_sage8_pv16(prep, v, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
                           return_lse=return_lse)
 

@@ -203,11 +203,11 @@ void* bwd_scratch() {
 
 attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int B, int H, int N, int d,
                   const long long* strides, const int* cu_seqlens, void* workspace, size_t workspace_bytes,
-                  void* stream, bool qk_fp8) {
+                  void* stream, int fmt) {
   if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
   attn_status s = check_shape(B, H, N, d);
   if (s != ATTN_OK) return s;
-  if (qk_fp8 && d == 96) return ATTN_ERR_HEADDIM;
+  if (fmt == attn::kPrepFp8 && d == 96) return ATTN_ERR_HEADDIM;
   if (in_dtype != ATTN_DTYPE_F16 && in_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
   if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
@@ -224,7 +224,7 @@ attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int
   s = check_device();
   if (s != ATTN_OK) return s;
   if (attn::launch_sage8_prep(q, k, v, in_dtype == ATTN_DTYPE_BF16, B, H, N, d, strides ? st : nullptr, cu_seqlens,
-                              workspace, static_cast<hipStream_t>(stream), qk_fp8) != hipSuccess)
+                              workspace, static_cast<hipStream_t>(stream), fmt) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -323,12 +323,12 @@ int attn_sage8_workspace_layout(int B, int H, int N, int d, size_t* out, int n) 
 
 attn_status attn_k_smooth_quant(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
                                 int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
-  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, nullptr, workspace, workspace_bytes, stream, false);
+  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, nullptr, workspace, workspace_bytes, stream, attn::kPrepInt8);
 }
 
 attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* v, int in_dtype, int B, int H,
                                       int N, int d, void* workspace, size_t workspace_bytes, void* stream) {
-  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, nullptr, workspace, workspace_bytes, stream, true);
+  return prep8(q, k, v, in_dtype, B, H, N, d, nullptr, nullptr, workspace, workspace_bytes, stream, attn::kPrepFp8);
 }
 
 attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B, int H, int N, int d,
@@ -351,9 +351,10 @@ attn_status attn_k_smooth_quant_strided(const void* q, const void* k, const void
                                         int N, int d, const long long* strides, const int* cu_seqlens,
                                         int qk_format, void* workspace, size_t workspace_bytes, void* stream) {
   if (strides == nullptr) return ATTN_ERR_NULL;
-  if (qk_format != ATTN_QK_INT8 && qk_format != ATTN_QK_FP8) return ATTN_ERR_ARG;
-  return prep8(q, k, v, in_dtype, B, H, N, d, strides, cu_seqlens, workspace, workspace_bytes, stream,
-               qk_format == ATTN_QK_FP8);
+  if (qk_format != ATTN_QK_INT8 && qk_format != ATTN_QK_FP8 && qk_format != ATTN_QK_INT8_NO_V) return ATTN_ERR_ARG;
+  const int fmt = qk_format == ATTN_QK_FP8 ? attn::kPrepFp8
+                  : qk_format == ATTN_QK_INT8_NO_V ? attn::kPrepInt8NoV : attn::kPrepInt8;
+  return prep8(q, k, v, in_dtype, B, H, N, d, strides, cu_seqlens, workspace, workspace_bytes, stream, fmt);
 }
 
 attn_status attn_fwd_sage8_strided(const void* workspace, void* o, float* lse, int B, int H, int N, int d,

@@ -80,15 +80,18 @@ struct Sage8Layout {
   int nchunk;  // token chunks of the column reductions
 };
 Sage8Layout sage8_layout(int B, int H, int N, int d);
-// qk_fp8: Q and K in e4m3 blocks (the FP8-QK variant; d = 64 or 128) instead
-// of INT8; the forward must be told the format the preparation wrote.
+// fmt: kPrepInt8 (the INT8 recipe), kPrepFp8 (Q and K in e4m3 blocks, the
+// FP8-QK variant; d = 64 or 128) or kPrepInt8NoV (INT8 Q and K only, for the
+// 16-bit P V variant: V's statistics, codes and regions are not touched);
+// the forward must be told the format the preparation wrote.
 // strides: element strides (batch, head, token) of q, k, v with d
 // contiguous (9 values); nullptr for contiguous [B,H,N,d].
 // cu (nullable, device int32 [B+1]): packed sequences along the token axis
 // (the batch strides are then unused); each fills its own workspace slot.
+enum PrepFormat : int { kPrepInt8 = 0, kPrepFp8 = 1, kPrepInt8NoV = 2 };
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H,
                              int N, int d, const int64_t* strides, const int* cu, void* ws, hipStream_t stream,
-                             bool qk_fp8);
+                             int fmt);
 // INT8 scores from the workspace of launch_sage8_prep (INT8 format) with the
 // 16-bit P V product: a.v is the 16-bit V [B,H,N,d] (fp16 unless bf16), O
 // contiguous [B,H,N,d]; a.q and a.k are unused.

@@ -108,7 +108,9 @@ __device__ __forceinline__ int seq_span(const PrepIn& in, int b, int h, int N, i
   return max(0, min(in.cu[b + 1] - t0, N));
 }
 
-template <int D, bool BF16>
+// NOV: Q and K only (the INT8-score variant with the 16-bit P V product
+// reads no FP8 V): V is neither read nor summarised.
+template <int D, bool BF16, bool NOV>
 __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                       int N, double* __restrict__ kpart,
                                                       float* __restrict__ vpart, int nchunk, PrepIn in) {
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
   for (int i = 0; i < kChunk / kRows; ++i) {
     const uint32_t n = (uint32_t)(n0 + i * kRows);
     const u32x4_t kx = buffer_load16(krs, kvoff, n * ksn * 2);
-    const u32x4_t vx = buffer_load16(vrs, vvoff, n * vsn * 2);
+    const u32x4_t vx = NOV ? u32x4_t{0u, 0u, 0u, 0u} : buffer_load16(vrs, vvoff, n * vsn * 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint16_t kb = (uint16_t)(kx[e >> 1] >> (16 * (e & 1)));
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
       m = fmaxf(m, smax[g][tid]);
     }
     kpart[((size_t)bh * nchunk + chunk) * D + tid] = s;
-    vpart[((size_t)bh * nchunk + chunk) * D + tid] = m;
+    if (!NOV) vpart[((size_t)bh * nchunk + chunk) * D + tid] = m;
   }
 }
 
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
 // then the groups combine through LDS.  The fp64 partials are sums of fp16 /
 // bf16 values, which fp64 adds exactly at these magnitudes, so the order of
 // the additions does not change kmean.
-template <int D>
+template <int D, bool NOV>
 __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
                                                     int nchunk, int N, float* __restrict__ kmean,
                                                     float* __restrict__ sv, float* __restrict__ vinv, PrepIn in) {
@@ -190,12 +192,14 @@ __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__
   for (; ch + kG < nchunk; ch += 2 * kG) {
     s0 += kp[(size_t)ch * D];
     s1 += kp[(size_t)(ch + kG) * D];
-    m0 = fmaxf(m0, vp[(size_t)ch * D]);
-    m1 = fmaxf(m1, vp[(size_t)(ch + kG) * D]);
+    if (!NOV) {
+      m0 = fmaxf(m0, vp[(size_t)ch * D]);
+      m1 = fmaxf(m1, vp[(size_t)(ch + kG) * D]);
+    }
   }
   if (ch < nchunk) {
     s0 += kp[(size_t)ch * D];
-    m0 = fmaxf(m0, vp[(size_t)ch * D]);
+    if (!NOV) m0 = fmaxf(m0, vp[(size_t)ch * D]);
   }
   ssum[g][c] = s0 + s1;
   smax[g][c] = fmaxf(m0, m1);
@@ -211,8 +215,10 @@ __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__
     int64_t base;
     const int n = seq_span(in, bh / in.H, 0, N, 1, base);
     kmean[(size_t)bh * D + c] = n > 0 ? (float)(s / (double)n) : 0.f;
-    sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
-    vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
+    if (!NOV) {
+      sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+      vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
+    }
   }
 }
 
@@ -244,8 +250,8 @@ __device__ __forceinline__ uint32_t f8(float y, float inv) {
 
 // ---- quant: grid (nblk, B*H), prep_threads<D>() threads --------------------------------
 // QKFP8: Q and smoothed K go to e4m3 with scale amax / 448 per block (the
-// FP8-QK variant) instead of INT8 with amax / 127.
-template <int D, bool BF16, bool QKFP8>
+// FP8-QK variant) instead of INT8 with amax / 127.  NOV: V is not touched.
+template <int D, bool BF16, bool QKFP8, bool NOV>
 __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, int N, int np, int nblk,
                                                    const float* __restrict__ kmean, const float* __restrict__ vinv,
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     km[e] = kmean[(size_t)bh * D + ch * 8 + e];
-    vi[e] = vinv[(size_t)bh * D + ch * 8 + e];
+    vi[e] = NOV ? 0.f : vinv[(size_t)bh * D + ch * 8 + e];
   }
   float aq = 0.f, ak = 0.f;
 #pragma unroll
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
     if (n < n_seq) {
       qx = *(const u32x4_t*)(qh + n * in.s[2] + ch * 8);
       kx = *(const u32x4_t*)(kh + n * in.s[5] + ch * 8);
-      vx = *(const u32x4_t*)(vh + n * in.s[8] + ch * 8);
+      if (!NOV) vx = *(const u32x4_t*)(vh + n * in.s[8] + ch * 8);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -302,9 +308,11 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
       aq = fmaxf(aq, fabsf(xq[i][e]));
       ak = fmaxf(ak, fabsf(xk[i][e]));
       // V code, byte-scattered into the transposed tile
-      const float t = in_to_f32<BF16>(vb) * vi[e];
-      const uint32_t code = n < n_seq ? (__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false) & 0xFF) : 0u;
-      vt[ch * 8 + e][key_pos(r)] = (uint8_t)code;
+      if (!NOV) {
+        const float t = in_to_f32<BF16>(vb) * vi[e];
+        const uint32_t code = n < n_seq ? (__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false) & 0xFF) : 0u;
+        vt[ch * 8 + e][key_pos(r)] = (uint8_t)code;
+      }
     }
   }
   aq = block_max<kThreads / 64>(aq, red);
@@ -332,6 +340,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
     *(u32x2_t*)(qq + headp + (size_t)n * D + ch * 8) = wq;
     *(u32x2_t*)(kq + headp + (size_t)n * D + ch * 8) = wk;
   }
+  if (NOV) return;
   __syncthreads();
   // V tile: D rows of 64 bytes, contiguous per block -> 16-byte stores
   uint8_t* vdst = vq + headp + (size_t)blk * kQB * D;
@@ -341,7 +350,7 @@ __global__ __launch_bounds__(256) void sage8_quant(const uint16_t* __restrict__ 
   }
 }
 
-template <int D, bool BF16, bool QKFP8>
+template <int D, bool BF16, bool QKFP8, bool NOV>
 hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, int N, const int64_t* strides,
                      const int* cu, void* ws, hipStream_t stream) {
   const Sage8Layout L = sage8_layout(B, H, N, D);
@@ -356,14 +365,14 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
   char* w = static_cast<char*>(ws);
   const int bh = B * H;
   const int np = L.nblk * kQB;
-  hipLaunchKernelGGL((sage8_colstats<D, BF16>), dim3(L.nchunk, bh), dim3(prep_threads<D>()), 0, stream,
+  hipLaunchKernelGGL((sage8_colstats<D, BF16, NOV>), dim3(L.nchunk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N,
                      reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk, in);
-  hipLaunchKernelGGL((sage8_finalize<D>), dim3(bh), dim3((256 / D) * D), 0, stream,
+  hipLaunchKernelGGL((sage8_finalize<D, NOV>), dim3(bh), dim3((256 / D) * D), 0, stream,
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
                      reinterpret_cast<float*>(w + L.vinv), in);
-  hipLaunchKernelGGL((sage8_quant<D, BF16, QKFP8>), dim3(L.nblk, bh), dim3(prep_threads<D>()), 0, stream,
+  hipLaunchKernelGGL((sage8_quant<D, BF16, QKFP8, NOV>), dim3(L.nblk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), N, np, L.nblk,
                      reinterpret_cast<const float*>(w + L.kmean), reinterpret_cast<const float*>(w + L.vinv),
@@ -801,22 +810,23 @@ hipError_t fwd8_impl(const void* ws, const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 namespace {
-template <bool QKFP8>
+template <bool QKFP8, bool NOV>
 hipError_t prep_q(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
                   const int64_t* st, const int* cu, void* ws, hipStream_t stream) {
-  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream)
-                           : prep_impl<64, false, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream);
-  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream)
-                           : prep_impl<96, false, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream);
-  return bf16 ? prep_impl<128, true, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream)
-              : prep_impl<128, false, QKFP8>(q, k, v, B, H, N, st, cu, ws, stream);
+  if (d == 64) return bf16 ? prep_impl<64, true, QKFP8, NOV>(q, k, v, B, H, N, st, cu, ws, stream)
+                           : prep_impl<64, false, QKFP8, NOV>(q, k, v, B, H, N, st, cu, ws, stream);
+  if (d == 96) return bf16 ? prep_impl<96, true, QKFP8, NOV>(q, k, v, B, H, N, st, cu, ws, stream)
+                           : prep_impl<96, false, QKFP8, NOV>(q, k, v, B, H, N, st, cu, ws, stream);
+  return bf16 ? prep_impl<128, true, QKFP8, NOV>(q, k, v, B, H, N, st, cu, ws, stream)
+              : prep_impl<128, false, QKFP8, NOV>(q, k, v, B, H, N, st, cu, ws, stream);
 }
 }  // namespace
 
 hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool bf16, int B, int H, int N, int d,
-                             const int64_t* strides, const int* cu, void* ws, hipStream_t stream, bool qk_fp8) {
-  return qk_fp8 ? prep_q<true>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream)
-                : prep_q<false>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream);
+                             const int64_t* strides, const int* cu, void* ws, hipStream_t stream, int fmt) {
+  if (fmt == kPrepFp8) return prep_q<true, false>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream);
+  if (fmt == kPrepInt8NoV) return prep_q<false, true>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream);
+  return prep_q<false, false>(q, k, v, bf16, B, H, N, d, strides, cu, ws, stream);
 }
 
 namespace {

@@ -73,8 +73,11 @@ typedef enum {
 
 /* Number format of Q and K in the 8-bit path's workspace. */
 typedef enum {
-    ATTN_QK_INT8 = 0,  /* the INT8 recipe (attn_k_smooth_quant)            */
-    ATTN_QK_FP8 = 1    /* the FP8-QK variant (attn_k_smooth_quant_fp8qk)   */
+    ATTN_QK_INT8 = 0,      /* the INT8 recipe (attn_k_smooth_quant)            */
+    ATTN_QK_FP8 = 1,       /* the FP8-QK variant (attn_k_smooth_quant_fp8qk)   */
+    ATTN_QK_INT8_NO_V = 2  /* INT8 Q and K only, for attn_fwd_sage8_pv16: V
+                              is not read and the workspace's V regions are
+                              not written (preparation only)                  */
 } attn_qk_format;
 
 /*
@@ -226,7 +229,9 @@ attn_status attn_fwd_sage8_fp8qk(const void* workspace, void* o, float* lse, int
  * rel-L1 <= 2e-2 against exact attention, which the FP8 P and V of
  * attn_fwd_sage8 do not (their rounding alone costs about 2-4% rel-L1).
  *
- *  workspace  written by attn_k_smooth_quant (INT8 format) for the same B,
+ *  workspace  written by attn_k_smooth_quant (INT8 format), or by
+ *             attn_k_smooth_quant_strided with ATTN_QK_INT8_NO_V (no V
+ *             statistics or codes: less preparation work), for the same B,
  *             H, N, d; only its Qq, Kq, scales and K mean are read.
  *  v          the 16-bit V [B,H,N,d] contiguous that was prepared, in
  *             v_dtype (ATTN_DTYPE_F16 or ATTN_DTYPE_BF16).
@@ -272,7 +277,11 @@ attn_status attn_fwd_sage8_pv16(const void* workspace, const void* v, int v_dtyp
  *  The LSE stays [B,H,N] contiguous (row b,h,i for i below sequence b's
  *  length).  Other arguments and errors as for attn_k_smooth_quant and
  *  attn_fwd_sage8; a NULL stride array is ATTN_ERR_NULL, an unknown
- *  qk_format ATTN_ERR_ARG, a misaligned cu_seqlens ATTN_ERR_ALIGN.
+ *  qk_format ATTN_ERR_ARG, a misaligned cu_seqlens ATTN_ERR_ALIGN.  The
+ *  preparation also takes ATTN_QK_INT8_NO_V: the INT8 Q and K of
+ *  attn_k_smooth_quant bit for bit, V untouched (a workspace for
+ *  attn_fwd_sage8_pv16, which reads no FP8 V; the forward here rejects that
+ *  format with ATTN_ERR_ARG).
  */
 attn_status attn_k_smooth_quant_strided(const void* q, const void* k, const void* v,
                                         int in_dtype, int B, int H, int N, int d,

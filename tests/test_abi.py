@@ -192,7 +192,8 @@ def test_sage8_strided_validation():
 
     assert p(None) == E_NULL
     assert p(contig, q=None) == E_NULL
-    assert p(contig, fmt=2) == E_ARG
+    assert p(contig, fmt=3) == E_ARG
+    assert p(contig, fmt=2, dd=80) == E_HEADDIM      # INT8 Q/K only: checked like the INT8 format
     assert p(contig, fmt=1, dd=96) == E_HEADDIM      # FP8 scores: d = 64 or 128
     assert p(contig, nb=need - 1) == E_WS
     assert p(nhd[:2] + [d - 8] + nhd[3:]) == E_ARG    # token stride below d
@@ -210,6 +211,7 @@ def test_sage8_strided_validation():
     assert f(None) == E_NULL
     assert f([N * H * d, d, H * d], o=None) == E_NULL
     assert f([N * H * d, d, H * d], fmt=5) == E_ARG
+    assert f([N * H * d, d, H * d], fmt=2) == E_ARG  # a Q/K-only workspace has no FP8 V
     assert f([N * H * d, d, 8]) == E_ARG              # token stride below d
     assert f([N * H * d, d + 2, H * d]) == E_ALIGN
     assert f([N * H * d, d, H * d], fmt=1, dd=96) == E_HEADDIM

@@ -36,7 +36,7 @@ def _check(inp, causal, scale, rows=None, out_dtype=torch.float32, label="", che
     print(f"[gpu] pv16 {label} shape={(B, H, N, d)} {inp['q'].dtype} causal={causal}", flush=True)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     bias = inp["bias"].to(DEV) if inp["bias"] is not None else None
-    prep = attn.sage8_prep(q, k, v)
+    prep = attn.sage8_prep(q, k, v, qk="int8_no_v")  # INT8 Q and K only, as sageattn_pv16 prepares
     o, lse = attn.fwd_sage8_pv16(prep, v, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype,
                                  return_lse=True)
     torch.cuda.synchronize()
@@ -138,6 +138,34 @@ def test_rejects_other_preparations():
         attn.fwd_sage8_pv16(attn.sage8_prep(q, k, v, qk="fp8"), v)
     with pytest.raises(ValueError):
         attn.fwd_sage8_pv16(attn.sage8_prep(q, k, v), v.float())
+    with pytest.raises(ValueError):  # no FP8 V in a Q/K-only preparation
+        attn.fwd_sage8(attn.sage8_prep(q, k, v, qk="int8_no_v"))
+
+
+@pytest.mark.parametrize("N", [1, 65, 300, 1000])
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_qk_only_prep_is_the_int8_prep(N, d):
+    """The Q/K-only preparation writes exactly the INT8 preparation's Q and K
+    codes, block scales and K mean (and the oracle's quantisers), and the
+    variant gives the same output from either."""
+    inp = workloads.make_inputs(2, 2, N, d, "bf16", seed=N + 3 * d, outliers=True)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    full = attn.sage8_prep(q, k, v)
+    qko = attn.sage8_prep(q, k, v, qk="int8_no_v")
+    vf, vo = attn.sage8_workspace_views(full), attn.sage8_workspace_views(qko)
+    torch.cuda.synchronize()
+    nb = (N + 63) // 64
+    for name in ("qq", "kq", "kmean"):
+        assert torch.equal(vf[name], vo[name]), name
+    for name in ("sq", "sk"):
+        assert torch.equal(vf[name][:, :, :nb].view(torch.int32), vo[name][:, :, :nb].view(torch.int32)), name
+    ref = oracle.sage8_prepare(*(inp[n].float().numpy() for n in ("q", "k", "v")))
+    assert np.array_equal(vo["qq"][:, :, :N].cpu().numpy(), ref["qq"])
+    assert np.array_equal(vo["kq"][:, :, :N].cpu().numpy(), ref["kq"])
+    o1 = attn.fwd_sage8_pv16(full, v, causal=True)
+    o2 = attn.fwd_sage8_pv16(qko, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
 
 
 @pytest.mark.parametrize("cfg_id", [4, 5, 2, 3])

@@ -447,8 +447,10 @@ __device__ __forceinline__ uint32_t v_pos(int r, int c) { return (uint32_t)(r * 
 
 
 
+// (the first conversion's high half is overwritten by the second, so any
+// register serves as its old value: a's bits, which need no extra move)
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_uint(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -631,16 +633,17 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
       }
       const float bl = BIAS ? braw * kLog2e : 0.f;
       const float g = QKFP8 ? bl : fmaf(-kMagic, f, bl);
+      // (three-input max / min: one instruction per two scores)
       float a0;
       if (pos) {
         a0 = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) a0 = fmaxf(a0, fmaxf(s[0][r], s[1][r]));
+        for (int r = 1; r < 16; ++r) a0 = fmaxf(fmaxf(a0, s[0][r]), s[1][r]);
         a0 = xor32_max(a0);
       } else {
         a0 = fminf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) a0 = fminf(a0, fminf(s[0][r], s[1][r]));
+        for (int r = 1; r < 16; ++r) a0 = fminf(fminf(a0, s[0][r]), s[1][r]);
         a0 = xor32_min(a0);
       }
       const float m_blk = (a0 == sent) ? -INFINITY : fmaf(a0, f, g);

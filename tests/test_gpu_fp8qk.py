@@ -8,9 +8,9 @@ Bars, each against code under oracle/ only:
   * forward against the fp32-decision model of the blocked forward with
     e4m3 scores, fed the oracle's quantised data.  The model adds the exact
     FP8 products of a score and rounds once; gfx950's FP8 matrix instruction
-    does not: measured on one 32x32x64 tile of these codes, its sums sit up
-    to about 2^-14.6 of the largest product away from the exact sum, and most
-    outputs differ from the correctly rounded one.  A score that close to an
+    does not: on 32x32x64 tiles of these codes its sums sit up to about
+    2^-12.3 of the largest product away from the exact sum, and most outputs
+    differ from the correctly rounded one (tests/test_gpu_fp8_mfma.py).  A score that close to an
     e4m3 rounding boundary of P^ = e4m3(448*2^(t-m-2)) then takes the other
     code (a few elements in 10^3), and one code is at most 1/8 of that P^.
     The per-row bar is therefore 1e-3 plus two such flips on the row's

@@ -23,7 +23,8 @@ Three bars, each against code under oracle/ only:
     margins: the kernel-precision model (lazy maximum, P scale) measured at
     most 0.0016 rel-L1 and 6.3e-5 cosine from the fp64 model over every
     input of this file, and the kernel is held within EMU_MEAN_ABS of the
-    kernel-precision model (a few 1e-4 of rel-L1 at |O| ~ 0.1).
+    kernel-precision model (2e-4 of rel-L1 at |O| ~ 0.1; measured at most
+    1.8e-5 on fp32 outputs, on the peaky scale = 0.5 rows).
 """
 import math
 
@@ -38,7 +39,7 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 5e-5, 1e-4
+EMU_MAX_ABS, EMU_MEAN_ABS, EMU_LSE = 1e-3, 2e-5, 1e-4
 COS_MIN, REL_L1_MARGIN, COS_MARGIN = 0.999, 0.0025, 2e-4
 
 

@@ -133,5 +133,5 @@ def test_token_major_against_oracle():
     o_ref, _ = oracle.attn_rows(qn, kn, vn, rows, causal=True, scale=1 / d ** 0.5)
     m_ref = workloads.error_metrics(got, o_ref)
     print(f"    token-major vs fp32 model: {m_emu}; vs fp64 attention: {m_ref}", flush=True)
-    assert m_emu["max_abs"] <= 1e-3 and m_emu["mean_abs"] <= 5e-5, m_emu
+    assert m_emu["max_abs"] <= 1e-3 and m_emu["mean_abs"] <= 2e-5, m_emu
     assert m_ref["cos"] >= 0.999, m_ref

@@ -174,7 +174,7 @@ def test_packed_against_oracle():
         t0 = int(cu[b])
         got = o[t0:t0 + n].transpose(0, 1).reshape(-1, d).double().cpu().numpy()
         m = workloads.error_metrics(got, o_emu)
-        assert m["max_abs"] <= 1e-3 and m["mean_abs"] <= 5e-5, (b, m)
+        assert m["max_abs"] <= 1e-3 and m["mean_abs"] <= 2e-5, (b, m)
         if n >= 64:
             o_ref, _ = oracle.attn_rows(qs, ks, vs, rows, causal=True, scale=1 / d ** 0.5)
             m_ref = workloads.error_metrics(got, o_ref)

@@ -48,11 +48,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # HBM traffic per launch (bytes) of a kernel on a workload, from rocprofv3
 # --pmc FETCH_SIZE / WRITE_SIZE runs, scaled by the same counters on a plain
 # 1 GiB device copy (FETCH_SIZE reads half the copied bytes: factor 2;
-# WRITE_SIZE reads them exactly: factor 1); profiles/*_hbm-traffic.txt.
+# WRITE_SIZE reads them exactly: factor 1); profiles/fwd16_long-context_hbm-traffic.txt.
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    ("fwd16", 3): {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": None, "sha256": ""},
+    # 1043443 KiB fetched (x2) + 262144 KiB written, mean of 7 dispatches
+    ("fwd16", 3): {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 2405406135,
+                   "sha256": "06548e0c1774c724b83298cb6d43dd375342efd53452bbb60c850db4e92abb2b"},
 }
 
 

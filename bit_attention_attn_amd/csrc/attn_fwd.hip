@@ -22,9 +22,20 @@
 //   softmax in base 2: the scale is folded into c = scale*log2(e); the bias
 //       (natural-log units) is one scalar per 64x64 block, so the block
 //       maximum of c*S + bias is c*max(S) + bias.
-//   The running maximum is raised only when a block maximum exceeds it by
-//       more than kTau (P then stays <= 2^kTau, exact in fp16/bf16 range),
-//       which skips most rescales of the output accumulator.
+//   Lazy rescale: P stays <= 2^kTau (well inside the fp16/bf16 range)
+//       against a running maximum m that is raised only when needed, which
+//       skips most rescales of the output accumulator.  Two forms:
+//     - block maximum first (d = 96, 128): m is raised when the block
+//       maximum exceeds it by more than kTau;
+//     - speculative (d = 64, two query tiles per wave): P is computed against
+//       m as it stands, with no block maximum.  P >= 0, so if every lane's
+//       partial sum of the block's P stays <= 2^kTau no single P exceeds it
+//       and the block is done; otherwise (and on a row's first block, where m
+//       is still -inf) the block maximum is taken, m is raised to it, the
+//       running state rescaled and P recomputed.  This saves the maximum
+//       tree on most blocks but keeps the P V products from starting before
+//       the last exponential; measured on MI355X, +6% at d = 64 (twice the
+//       softmax work per matrix instruction) and -2% at d = 128.
 //   O^T += V^T P^T: P^T comes straight from the S^T accumulator registers as
 //       the B operand (the key order inside a lane is a permutation applied
 //       to both operands); V^T is read from the row-major V tile with the
@@ -43,7 +54,8 @@ namespace attn {
 namespace {
 
 constexpr int kBN = 64;       // keys per block
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr float kTau = 8.0f;  // lazy-rescale bound, log2 units: P <= 2^kTau
+constexpr float kSumCap = 256.0f;  // 2^kTau
 
 // Tiling: QS query tiles of 32 per wave, NW waves per workgroup.  Block
 // j+1 (K and V) is loaded during block j into the other of two buffers.
@@ -321,6 +333,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   }
   const float c = p.c;
   const bool pos = c > 0.f;
+  constexpr bool kSpec = QS == 2;  // speculative softmax (the d = 64 tiling)
   const float sent = pos ? -INFINITY : INFINITY;
 
 
@@ -386,13 +399,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
   };
   auto needs_mask = [&](int j) { return (CAUSAL && j == wave_last) || (j + 1) * kBN > N; };
 
-  // ---- block maximum and lazy rescale of the running state; returns the
-  // exponent offsets kc = bias - m (log2 units) of the block
-  // (cf: the scale of the block's raw scores in log2 units, c, or for INT8
-  // scores c * sq * sk, with the offset 1.5 * 2^23 * cf taken off through g0)
-  auto block_max = [&](f32x16_t (&s)[2][QS], float (&kc)[QS], float braw, float cf) {
-    const float bl = HAS_BIAS ? braw * kLog2e : 0.f;
-    const float g0 = Q8 ? fmaf(-kMagic, cf, bl) : bl;
+  // ---- block maximum: raises the running maximum to it where it is larger
+  // by more than tau, rescales the running state, and returns the exponent
+  // offsets
+  // kc = g0 - m (log2 units) of the block.  g0: the block's additive term
+  // (the bias in log2 units; for INT8 scores also the offset 1.5 * 2^23 * cf
+  // taken off); cf: the scale of the block's raw scores in log2 units (c, or
+  // for INT8 scores c * sq * sk).
+  auto block_max = [&](f32x16_t (&s)[2][QS], float (&kc)[QS], float g0, float cf, float tau) {
     float m_blk[QS];
     bool need_any = false;
 #pragma unroll
@@ -410,12 +424,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
         a0 = xor32_min(a0);
       }
       m_blk[qs] = (a0 == sent) ? -INFINITY : fmaf(a0, cf, g0);
-      need_any |= m_blk[qs] > m_run[qs] + kTau;
+      need_any |= m_blk[qs] > m_run[qs] + tau;
     }
     if (__any(need_any)) {
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
-        const bool need = m_blk[qs] > m_run[qs] + kTau;
+        const bool need = m_blk[qs] > m_run[qs] + tau;
         const float m_new = need ? m_blk[qs] : m_run[qs];
         const float alpha = need ? exp2_approx(m_run[qs] - m_new) : 1.f;
         l_run[qs] *= alpha;
@@ -430,10 +444,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
 
   // ---- P = exp2(c*S + bias - m) as the B operand of O^T += V^T P^T.  Masked
   // scores are +-inf, so c*S is -inf and P is 0 (c is never 0: the host
-  // passes the smallest normal float for a zero scale).  The row sum adds
-  // the rounded P values the product uses.
+  // passes the smallest normal float for a zero scale).  ls: the lane's sum
+  // of the rounded P values the product uses.
   u32x4_t pb[4][QS];
-  auto softmax_p = [&](f32x16_t (&s)[2][QS], const float (&kc)[QS], float cf) {
+  auto softmax_p = [&](f32x16_t (&s)[2][QS], const float (&kc)[QS], float cf, float (&ls)[QS]) {
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       float lsum = 0.f;
@@ -450,8 +464,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
           pb[kk][qs][e >> 1] = pk;
         }
       }
-      l_run[qs] += lsum;
+      ls[qs] = lsum;
     }
+  };
+  // ---- the block's P: the block maximum first, or (speculative form) P
+  // against the running maximum and the block maximum only when a lane's
+  // partial sum shows a P above 2^kTau could be present (or m is still -inf)
+  auto softmax_block = [&](f32x16_t (&s)[2][QS], float braw, float cf) {
+    const float bl = HAS_BIAS ? braw * kLog2e : 0.f;
+    const float g0 = Q8 ? fmaf(-kMagic, cf, bl) : bl;
+    float kc[QS], ls[QS];
+    if constexpr (!kSpec) {
+      block_max(s, kc, g0, cf, kTau);
+      softmax_p(s, kc, cf, ls);
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) l_run[qs] += ls[qs];
+      return;
+    }
+    bool slow = false;
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      kc[qs] = g0 - m_run[qs];
+      slow |= m_run[qs] == -INFINITY;
+    }
+    if (!__any(slow)) {
+      softmax_p(s, kc, cf, ls);
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) slow |= ls[qs] > kSumCap;
+    }
+    if (__any(slow)) {
+      block_max(s, kc, g0, cf, 0.f);
+      softmax_p(s, kc, cf, ls);
+    }
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) l_run[qs] += ls[qs];
   };
   auto pv = [&](int buf) {
     const uint8_t* Vs = vbase_lds + buf * kVTile;
@@ -488,9 +534,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       qk(buf, sc);
       if (needs_mask(jc)) apply_mask(jc, sc);
       const float cf = Q8 ? (sqw * skrow[jc]) * c : c;
-      float kc[QS];
-      block_max(sc, kc, braw, cf);
-      softmax_p(sc, kc, cf);
+      softmax_block(sc, braw, cf);
       pv(buf);
     }
     // the next block's loads into LDS are complete before any wave reads them
@@ -562,9 +606,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(Fwd16Params p, c
       if (work) {
         if (needs_mask(jc)) apply_mask(jc, sc);
         const float cf = Q8 ? (sqw * skrow[jc]) * c : c;
-        float kc[QS];
-        block_max(sc, kc, 0.f, cf);
-        softmax_p(sc, kc, cf);
+        softmax_block(sc, 0.f, cf);
         pv(buf);
       }
       __syncthreads();

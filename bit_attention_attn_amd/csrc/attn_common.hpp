@@ -157,6 +157,27 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void
 // would also wait for the loads that prefetch the next block).
 constexpr int kWaitVm0 = 0x0F70;
 
+// The INT8 score accumulators' start value, kMagicBits in all 16 registers
+// of a 32x32 tile, built from one vector register pair made once per
+// kernel.  From a splat of the constant the compiler rebuilds the 16-register
+// tuple in scalar registers and copies it over at every key block; from a
+// loop-invariant register pair it keeps one tuple live and feeds it to the
+// first product of every block as its C operand (no per-block moves).
+__device__ __forceinline__ unsigned long long magic_pair() {
+  unsigned long long v = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("v_mov_b64 %0, %1" : "=v"(v) : "s"(((unsigned long long)kMagicBits << 32) | (unsigned)kMagicBits));
+#endif
+  return v;
+}
+__device__ __forceinline__ i32x16_t magic_tile(unsigned long long pair) {
+  typedef unsigned long long u64x8_t __attribute__((ext_vector_type(8)));
+  u64x8_t m;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) m[r] = pair;
+  return __builtin_bit_cast(i32x16_t, m);
+}
+
 // Block-sparse gating by a per-head [nb x nb] block bias (fp32, natural-log
 // units; -inf gates a 64 x 64 block off).  A workgroup tile spans kRows
 // query blocks starting at qb_lo; a key block is visited when its bias is

@@ -560,6 +560,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
+  const unsigned long long magic_v = magic_pair();  // (loop-invariant: see magic_tile)
   const float c = p.c;
   const bool pos = c > 0.f;
   const float sent = pos ? -INFINITY : INFINITY;
@@ -603,9 +604,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
         const uint8_t* Ks = kl + buf * kKTile;
         i32x16_t si[2];
 #pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) si[T][r] = kMagicBits;
+        for (int T = 0; T < 2; ++T) si[T] = magic_tile(magic_v);
 #pragma unroll
         for (int kk = 0; kk < kKS; ++kk)
 #pragma unroll

@@ -168,6 +168,18 @@ def test_qk_only_prep_is_the_int8_prep(N, d):
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_long_sequence_tiling(causal, with_bias):
+    """At d = 128 and N >= 16384 the kernel runs 4-wave workgroups three to a
+    CU instead of 8-wave ones: a ragged length, with and without the causal
+    mask and a block bias, on sampled rows."""
+    N = 16384 + 77
+    inp = workloads.make_inputs(1, 2, N, 128, "bf16", seed=71 + causal + 2 * with_bias, gate=with_bias)
+    rows = workloads.parity_rows(1, 2, N, seed=7, n_random=16)
+    _check(inp, causal, 1 / math.sqrt(128), rows=rows, out_dtype=torch.bfloat16, label=f"long N={N}")
+
+
 @pytest.mark.parametrize("cfg_id", [4, 5, 2, 3])
 def test_workload_sampled_rows(cfg_id):
     """Full-size workloads in the launch configuration the benchmark times:

@@ -16,7 +16,9 @@ forward, 20 launches each after warm-up; INT8 scores with FP8 P and V, the
 FP8-QK variant, and INT8 scores with the 16-bit P V) and reported under ``paths``
 with its speedup over the bf16 forward, attention alone and with the
 preparation.  Other workloads follow under ``workloads`` and ``backward``;
-none of them is part of ``value``.
+none of them is part of ``value``.  With the CPU baseline (the oracle timed
+on the host cores) comes ``accuracy``: every path's output on sampled rows
+of the same workload against the oracle's exact attention, with the bars.
 
 Prints ONE JSON line.  Only one GPU is supported: --gpus above 1 exits.
 
@@ -163,6 +165,39 @@ def cpu_baseline(inp, cfg, seconds):
                 cpu_model=cpu_model(),
                 sample=f"{done_rows} random query rows of the {cfg['name']} workload, fp64 three-loop oracle "
                        f"(OpenMP over rows) for {elapsed:.1f} s; flops counted as 4*d per visible key, as on the GPU")
+
+
+def path_rows(attn, workloads, q, k, v, causal, rows):
+    """Every path's output on the given (b,h,i) rows of one call on the
+    workload (device outputs gathered to the host as fp64)."""
+    out = {"bf16": workloads.gather_rows(attn.fwd(q, k, v, causal=causal), rows)}
+    for name, qk in (("int8_qk_fp8_pv", "int8"), ("fp8_qk_fp8_pv", "fp8"), ("int8_qk_16bit_pv", "int8_no_v")):
+        prep = attn.sage8_prep(q, k, v, qk=qk)
+        o = attn.fwd_sage8_pv16(prep, v, causal=causal) if qk == "int8_no_v" else attn.fwd_sage8(prep, causal=causal)
+        out[name] = workloads.gather_rows(o, rows)
+        del prep, o
+    return out
+
+
+def accuracy(inp, cfg, rows, got):
+    """The paths' outputs on the sampled rows against the fp64 oracle's exact
+    attention of the same rounded inputs (the oracle runs here, in the CPU
+    baseline leg, untimed)."""
+    import numpy as np
+    import oracle
+    import workloads
+    q, k, v = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    ref, _ = oracle.attn_rows(q, k, v, rows, causal=cfg["causal"], scale=1 / math.sqrt(cfg["d"]))
+    res = {"rows": f"{len(rows)} rows (fixed block-edge rows and seeded random rows of heads 0, H/2, H-1)",
+           "bars": {"bf16": "max_abs <= 1e-2 and mean_abs <= 1e-3", "8-bit": "cos >= 0.999 and rel_l1 <= 2e-2"}}
+    for name, g in got.items():
+        m = workloads.error_metrics(g, ref)
+        res[name] = {key: float(f"{val:.4g}") for key, val in m.items()}
+        if name == "bf16":
+            res[name]["meets_bar"] = bool(m["max_abs"] <= 1e-2 and m["mean_abs"] <= 1e-3)
+        else:
+            res[name]["meets_bar"] = bool(m["cos"] >= 0.999 and m["rel_l1"] <= 2e-2)
+    return res
 
 
 def profile_one(args):
@@ -368,6 +403,9 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)")
         out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+        log("accuracy of every path on sampled rows against the oracle")
+        rows = workloads.parity_rows(B, H, N, seed=3)
+        out["accuracy"] = accuracy(inp, cfg, rows, path_rows(attn, workloads, q, k, v, causal, rows))
     print(json.dumps(out), flush=True)
 
 

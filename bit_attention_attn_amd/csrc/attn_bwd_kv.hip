@@ -258,8 +258,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKPara
     __builtin_amdgcn_sched_barrier(0);
     load_q(jq0);
     store_q(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
+  // on every path, so that the compiler's wait tracking knows the K and V
+  // row loads are complete: a wait for them left inside the loop would also
+  // wait for the next block's prefetch, the vector-memory counter being in
+  // order (measured +0.6% at 1x32x32768, +2.5% at 4x32x4096)
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   // The query loop in three segments, each with one body: the blocks on
   // the causal diagonal of the workgroup's keys (masked), the blocks past

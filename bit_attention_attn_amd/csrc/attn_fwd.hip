@@ -163,9 +163,15 @@ enum Mode { kDense = 0, kBias = 1, kGen = 2 };
 // read as fp32 is exactly 1.5 * 2^23 + S), dequantised per 64 x 64 block by
 // f = sq * sk * scale * log2(e) folded into the exponent; P and V stay in the
 // 16-bit input format for the second product, exactly as in the 16-bit path.
+// Workgroups per CU the register budget is set for: 8 waves per CU (two per
+// SIMD), or three 4-wave workgroups for the INT8-score instance at d = 128.
+template <int D, int NW, bool Q8>
+constexpr int kMinBlocks = (Q8 && D == 128 && NW == 4) ? 3 : 8 / NW;
+
 template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE, bool Q8 = false>
-__global__ __launch_bounds__(64 * NW, (Q8 && D == 128 && NW == 4) ? 3 : 8 / NW) void fwd16_kernel(Fwd16Params p, const float* __restrict__ bias,
-                                                                const float* __restrict__ sk) {
+__global__ __launch_bounds__(64 * NW, (kMinBlocks<D, NW, Q8>)) void fwd16_kernel(Fwd16Params p,
+                                                                                  const float* __restrict__ bias,
+                                                                                  const float* __restrict__ sk) {
   constexpr bool GEN = MODE == kGen, HAS_BIAS = MODE == kBias;
   static_assert(!(Q8 && GEN), "INT8 scores take the dense layout");
   using TL = Tiling<QS, NW>;
@@ -413,11 +419,10 @@ __global__ __launch_bounds__(64 * NW, (Q8 && D == 128 && NW == 4) ? 3 : 8 / NW) 
 
   // ---- block maximum: raises the running maximum to it where it is larger
   // by more than tau, rescales the running state, and returns the exponent
-  // offsets
-  // kc = g0 - m (log2 units) of the block.  g0: the block's additive term
-  // (the bias in log2 units; for INT8 scores also the offset 1.5 * 2^23 * cf
-  // taken off); cf: the scale of the block's raw scores in log2 units (c, or
-  // for INT8 scores c * sq * sk).
+  // offsets kc = g0 - m (log2 units) of the block.  g0: the block's additive
+  // term (the bias in log2 units; for INT8 scores also the offset
+  // 1.5 * 2^23 * cf taken off); cf: the scale of the block's raw scores in
+  // log2 units (c, or for INT8 scores c * sq * sk).
   auto block_max = [&](f32x16_t (&s)[2][QS], float (&kc)[QS], float g0, float cf, float tau) {
     float m_blk[QS];
     bool need_any = false;

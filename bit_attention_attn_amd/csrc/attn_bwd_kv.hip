@@ -170,10 +170,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdKPara
     const uint16_t* Ds = dl + buf * kTile + (32 * u + l32) * kRow + 8 * hf;
     s = f32x16_t{};
     dp = f32x16_t{};
+    // all of the half's Q and dO operands read before its first product (one
+    // wave per SIMD: no other wave covers the LDS latency; measured +1.0 to
+    // +1.7% on three workloads, bit-identical)
+    u32x4_t qa[kKS], da[kKS];
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
-      s = mfma32x32x16<BF16>(*(const u32x4_t*)(Qs + 16 * kk), kf[kk], s);
-      dp = mfma32x32x16<BF16>(*(const u32x4_t*)(Ds + 16 * kk), vf[kk], dp);
+      qa[kk] = *(const u32x4_t*)(Qs + 16 * kk);
+      da[kk] = *(const u32x4_t*)(Ds + 16 * kk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      s = mfma32x32x16<BF16>(qa[kk], kf[kk], s);
+      dp = mfma32x32x16<BF16>(da[kk], vf[kk], dp);
     }
   };
   // P and dS of half u packed as the B operands (step t holds queries

@@ -171,53 +171,56 @@ __global__ __launch_bounds__(256) void sage8_colstats(const uint16_t* __restrict
   }
 }
 
-// ---- finalize: grid B*H, (256/D)*D threads.  Thread (g, c) adds the partials of
-// chunks g, g + 256/D, ... for channel c with two independent accumulators,
-// then the groups combine through LDS.  The fp64 partials are sums of fp16 /
-// bf16 values, which fp64 adds exactly at these magnitudes, so the order of
-// the additions does not change kmean.
+// ---- finalize: grid (B*H, D/32), 256 threads.  Block (bh, y) owns channels
+// 32y .. 32y+31; thread (g, c) adds the partials of chunks g, g + 8, ... of
+// channel 32y + c with four independent accumulators (the loads of a thread
+// are independent, so they overlap), then the 8 groups combine through LDS.
+// The fp64 partials are sums of fp16 / bf16 values, which fp64 adds exactly
+// at these magnitudes, so the order of the additions does not change kmean.
 template <int D, bool NOV>
 __global__ __launch_bounds__(256) void sage8_finalize(const double* __restrict__ kpart, const float* __restrict__ vpart,
                                                     int nchunk, int N, float* __restrict__ kmean,
                                                     float* __restrict__ sv, float* __restrict__ vinv, PrepIn in) {
-  constexpr int kG = 256 / D;  // chunk groups; the block has kG * D threads
-  __shared__ double ssum[kG][D];
-  __shared__ float smax[kG][D];
-  const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
+  constexpr int kG = 8;  // chunk groups of 32 threads
+  __shared__ double ssum[kG][32];
+  __shared__ float smax[kG][32];
+  const int bh = blockIdx.x, cl = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int c = 32 * blockIdx.y + cl;
   const double* kp = kpart + (size_t)bh * nchunk * D + c;
   const float* vp = vpart + (size_t)bh * nchunk * D + c;
-  double s0 = 0.0, s1 = 0.0;
-  float m0 = 0.f, m1 = 0.f;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
   int ch = g;
-  for (; ch + kG < nchunk; ch += 2 * kG) {
-    s0 += kp[(size_t)ch * D];
-    s1 += kp[(size_t)(ch + kG) * D];
-    if (!NOV) {
-      m0 = fmaxf(m0, vp[(size_t)ch * D]);
-      m1 = fmaxf(m1, vp[(size_t)(ch + kG) * D]);
+  for (; ch + 3 * kG < nchunk; ch += 4 * kG) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s[u] += kp[(size_t)(ch + u * kG) * D];
+      if (!NOV) m[u] = fmaxf(m[u], vp[(size_t)(ch + u * kG) * D]);
     }
   }
-  if (ch < nchunk) {
-    s0 += kp[(size_t)ch * D];
-    if (!NOV) m0 = fmaxf(m0, vp[(size_t)ch * D]);
-  }
-  ssum[g][c] = s0 + s1;
-  smax[g][c] = fmaxf(m0, m1);
+#pragma unroll
+  for (int u = 0; u < 3; ++u)  // at most three chunks remain
+    if (ch + u * kG < nchunk) {
+      s[u] += kp[(size_t)(ch + u * kG) * D];
+      if (!NOV) m[u] = fmaxf(m[u], vp[(size_t)(ch + u * kG) * D]);
+    }
+  ssum[g][cl] = (s[0] + s[1]) + (s[2] + s[3]);
+  smax[g][cl] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
   __syncthreads();
   if (g == 0) {
-    double s = 0.0;
-    float m = 0.f;
+    double t = 0.0;
+    float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < kG; ++i) {
-      s += ssum[i][c];
-      m = fmaxf(m, smax[i][c]);
+      t += ssum[i][cl];
+      mx = fmaxf(mx, smax[i][cl]);
     }
     int64_t base;
     const int n = seq_span(in, bh / in.H, 0, N, 1, base);
-    kmean[(size_t)bh * D + c] = n > 0 ? (float)(s / (double)n) : 0.f;
+    kmean[(size_t)bh * D + c] = n > 0 ? (float)(t / (double)n) : 0.f;
     if (!NOV) {
-      sv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
-      vinv[(size_t)bh * D + c] = m > 0.f ? __fdiv_rn(448.0f, m) : 1.0f;
+      sv[(size_t)bh * D + c] = mx > 0.f ? __fdiv_rn(mx, 448.0f) : 1.0f;
+      vinv[(size_t)bh * D + c] = mx > 0.f ? __fdiv_rn(448.0f, mx) : 1.0f;
     }
   }
 }
@@ -368,7 +371,7 @@ hipError_t prep_impl(const void* q, const void* k, const void* v, int B, int H, 
   hipLaunchKernelGGL((sage8_colstats<D, BF16, NOV>), dim3(L.nchunk, bh), dim3(prep_threads<D>()), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N,
                      reinterpret_cast<double*>(w + L.kpart), reinterpret_cast<float*>(w + L.vpart), L.nchunk, in);
-  hipLaunchKernelGGL((sage8_finalize<D, NOV>), dim3(bh), dim3((256 / D) * D), 0, stream,
+  hipLaunchKernelGGL((sage8_finalize<D, NOV>), dim3(bh, D / 32), dim3(256), 0, stream,
                      reinterpret_cast<const double*>(w + L.kpart), reinterpret_cast<const float*>(w + L.vpart),
                      L.nchunk, N, reinterpret_cast<float*>(w + L.kmean), reinterpret_cast<float*>(w + L.sv),
                      reinterpret_cast<float*>(w + L.vinv), in);

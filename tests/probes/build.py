@@ -7,7 +7,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["fp8_mfma_probe.hip"]
+SOURCES = ["fp8_mfma_probe.hip", "issue_rate_probe.hip"]
 LIB = os.path.join(HERE, "libprobes.so")
 
 

@@ -1,0 +1,170 @@
+// Test probe (not part of the library): issue costs of the instructions the
+// softmax and the two products of the attention kernels are made of, on
+// gfx950, and the shader clock under a full-chip matrix load.
+//
+// rate_kernel: every wave runs `iters` rounds of one instruction kind on
+// independent chains (8 VALU chains, or 4 matrix accumulators, so that no
+// instruction waits for the one before it) and writes the shader cycle
+// counter (s_memtime) before and after the loop to cyc[2 wave], cyc[2 wave +
+// 1].  Cycles per instruction = (after - before) / count
+// with count = iters * 64 for the VALU kinds (8 rounds of 8 chains) and
+// iters * 32 for the matrix kinds (8 rounds of 4 accumulators).  kinds:
+//   0 v_fma_f32            1 v_exp_f32          2 v_cvt_pk_fp8_f32
+//   3 MFMA 32x32x16 bf16   4 MFMA 32x32x32 i8   5 MFMA 32x32x64 f8f6f4 (e4m3)
+//   6 one bf16 MFMA + 8 v_fma_f32 per step (the overlap of the two pipes)
+//   8 v_exp_f32 and v_fma_f32 alternating on separate chains (8 of each per
+//     step: whether the transcendental unit runs beside the FMA)
+// clock_kernel: every wave runs bf16 MFMA chains for `iters` rounds and
+// writes its shader cycles and its 100 MHz real-time ticks (s_memrealtime),
+// so cycles / ticks * 100 MHz is the clock the chip ran at under that load.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int KIND>
+__device__ __forceinline__ void run_rounds(int iters, float a, float b, float* out) {
+  if constexpr (KIND == 8) {
+    float x[8], y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = a + (float)i * b;
+      y[i] = b + (float)i * a;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)  // one asm statement per pair keeps them alternating
+          asm volatile("v_exp_f32 %0, %0\n\tv_fma_f32 %1, %1, %2, %3" : "+v"(x[i]), "+v"(y[i]) : "v"(a), "v"(b));
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += x[i] + y[i];
+    *out = s;
+  } else if constexpr (KIND <= 2) {
+    float x[8];
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = a + (float)i * b;
+      w[i] = __float_as_uint(x[i]);
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if constexpr (KIND == 0) x[i] = __builtin_fmaf(x[i], a, b);
+          if constexpr (KIND == 1) x[i] = __builtin_amdgcn_exp2f(x[i]);
+          if constexpr (KIND == 2) w[i] = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[i]), b, w[i], false);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += KIND == 2 ? __uint_as_float(w[i]) : x[i];
+    *out = s;
+  } else {
+    f32x16 acc[4];
+    i32x16 iacc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[c][r] = a;
+        iacc[c][r] = c;
+      }
+    bf16x8 av, bv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      av[e] = (__bf16)a;
+      bv[e] = (__bf16)b;
+    }
+    const i32x4 ai = {1, 2, 3, 4}, bi = {5, 6, 7, (int)threadIdx.x};
+    const i32x8 a8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      (int)threadIdx.x};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = a + (float)i * b;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (KIND == 3 || KIND == 6)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[c], 0, 0, 0);
+          if constexpr (KIND == 4) iacc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bi, iacc[c], 0, 0, 0);
+          if constexpr (KIND == 5)
+            acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, acc[c], 0, 0, 0, 0, 0, 0);
+          if constexpr (KIND == 6) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], a, b);
+          }
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s += acc[c][0] + (float)iacc[c][0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += x[i];
+    *out = s;
+  }
+}
+
+template <int KIND>
+__global__ void rate_kernel(int iters, float a, float b, unsigned long long* cyc, float* sink) {
+  const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  float s;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  run_rounds<KIND>(iters, a, b, &s);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if ((threadIdx.x & 63) == 0) {
+    cyc[2 * wave] = t0;
+    cyc[2 * wave + 1] = t1;
+    sink[wave] = s;
+  }
+}
+
+__global__ void clock_kernel(int iters, float a, float b, unsigned long long* out, float* sink) {
+  const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  float s;
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  run_rounds<3>(iters, a, b, &s);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0) {
+    out[2 * wave] = t1 - t0;
+    out[2 * wave + 1] = r1 - r0;
+    sink[wave] = s;
+  }
+}
+
+// cyc: device array of 2 * wgs * waves_per_wg entries;
+// sink: device array of wgs * waves_per_wg floats.  kind 7 = clock_kernel.
+extern "C" int issue_rate_probe_run(int kind, int wgs, int waves_per_wg, int iters, void* cyc, void* sink,
+                                    void* stream) {
+  if (wgs < 1 || waves_per_wg < 1 || waves_per_wg > 16 || iters < 1) return -1;
+  const dim3 grid(wgs), block(64 * waves_per_wg);
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* c = (unsigned long long*)cyc;
+  float* k = (float*)sink;
+  const float a = 0.999f, b = 1e-3f;
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(rate_kernel<0>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 1: hipLaunchKernelGGL(rate_kernel<1>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 2: hipLaunchKernelGGL(rate_kernel<2>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 3: hipLaunchKernelGGL(rate_kernel<3>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 4: hipLaunchKernelGGL(rate_kernel<4>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 5: hipLaunchKernelGGL(rate_kernel<5>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 6: hipLaunchKernelGGL(rate_kernel<6>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 7: hipLaunchKernelGGL(clock_kernel, grid, block, 0, s, iters, a, b, c, k); break;
+    case 8: hipLaunchKernelGGL(rate_kernel<8>, grid, block, 0, s, iters, a, b, c, k); break;
+    default: return -1;
+  }
+  return (int)hipGetLastError();
+}

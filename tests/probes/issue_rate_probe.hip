@@ -7,13 +7,18 @@
 // instruction waits for the one before it) and writes the shader cycle
 // counter (s_memtime) before and after the loop to cyc[2 wave], cyc[2 wave +
 // 1].  Cycles per instruction = (after - before) / count
-// with count = iters * 64 for the VALU kinds (8 rounds of 8 chains) and
+// with count = iters * 64 for the VALU kinds (4 rounds of 16 chains) and
 // iters * 32 for the matrix kinds (8 rounds of 4 accumulators).  kinds:
 //   0 v_fma_f32            1 v_exp_f32          2 v_cvt_pk_fp8_f32
 //   3 MFMA 32x32x16 bf16   4 MFMA 32x32x32 i8   5 MFMA 32x32x64 f8f6f4 (e4m3)
-//   6 one bf16 MFMA + 8 v_fma_f32 per step (the overlap of the two pipes)
-//   8 v_exp_f32 and v_fma_f32 alternating on separate chains (8 of each per
-//     step: whether the transcendental unit runs beside the FMA)
+//   6 one bf16 MFMA + 8 v_fma_f32 (8 chains) per step (the overlap of the
+//     two pipes)
+//   8 v_exp_f32 and v_fma_f32 alternating on separate chains (16 of each:
+//     whether the transcendental unit runs beside the FMA)
+// lds_kernel: every wave streams 16-byte LDS reads (ds_read_b128, kind 9) or
+//   8-byte transposing reads (ds_read_b64_tr_b16, kind 10) from consecutive
+//   addresses of a 64 KB tile, 8 in flight; the workgroup's span over the bytes
+//   its waves read is the CU's LDS read bandwidth.
 // clock_kernel: every wave runs bf16 MFMA chains for `iters` rounds and
 // writes its shader cycles and its 100 MHz real-time ticks (s_memrealtime),
 // so cycles / ticks * 100 MHz is the clock the chip ran at under that load.
@@ -29,36 +34,38 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <int KIND>
 __device__ __forceinline__ void run_rounds(int iters, float a, float b, float* out) {
   if constexpr (KIND == 8) {
-    float x[8], y[8];
+    float x[16], y[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       x[i] = a + (float)i * b;
       y[i] = b + (float)i * a;
     }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)  // one asm statement per pair keeps them alternating
+        for (int i = 0; i < 16; ++i)  // one asm statement per pair keeps them alternating
           asm volatile("v_exp_f32 %0, %0\n\tv_fma_f32 %1, %1, %2, %3" : "+v"(x[i]), "+v"(y[i]) : "v"(a), "v"(b));
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += x[i] + y[i];
+    for (int i = 0; i < 16; ++i) s += x[i] + y[i];
     *out = s;
   } else if constexpr (KIND <= 2) {
-    float x[8];
-    uint32_t w[8];
+    // 16 chains: a wave64 VALU result is ready only several instructions
+    // later, and a single wave must not wait for it
+    float x[16];
+    uint32_t w[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       x[i] = a + (float)i * b;
       w[i] = __float_as_uint(x[i]);
     }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 16; ++i) {
           if constexpr (KIND == 0) x[i] = __builtin_fmaf(x[i], a, b);
           if constexpr (KIND == 1) x[i] = __builtin_amdgcn_exp2f(x[i]);
           if constexpr (KIND == 2) w[i] = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[i]), b, w[i], false);
@@ -66,7 +73,7 @@ __device__ __forceinline__ void run_rounds(int iters, float a, float b, float* o
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += KIND == 2 ? __uint_as_float(w[i]) : x[i];
+    for (int i = 0; i < 16; ++i) s += KIND == 2 ? __uint_as_float(w[i]) : x[i];
     *out = s;
   } else {
     f32x16 acc[4];
@@ -129,6 +136,52 @@ __global__ void rate_kernel(int iters, float a, float b, unsigned long long* cyc
   }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short __attribute__((address_space(3))) lds_short;
+typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+
+template <bool TR>
+__global__ void lds_kernel(int iters, unsigned long long* cyc, float* sink) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[16384];  // 64 KB
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) tile[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t acc = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    uint32_t v[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (TR) {
+        // 512 consecutive bytes per instruction, 128 windows: byte offsets < 65536
+        const int off = (((it * 8 + u) & 127) * 512 + lane * 8) / 4;
+        const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
+        const uint2 w = __builtin_bit_cast(uint2, r);
+        v[u][0] = w.x;
+        v[u][1] = w.y;
+        v[u][2] = v[u][3] = 0u;
+      } else {
+        // 1 KB consecutive bytes per instruction, 64 windows: byte offsets < 65536
+        const int off = (((it * 8 + u) & 63) * 1024 + lane * 16) / 4;
+        const uint4 w = *(const uint4*)(tile + off);
+        v[u][0] = w.x;
+        v[u][1] = w.y;
+        v[u][2] = w.z;
+        v[u][3] = w.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) {
+    cyc[2 * wave] = t0;
+    cyc[2 * wave + 1] = t1;
+  }
+  sink[wave * 64 + lane] = (float)acc;
+}
+
 __global__ void clock_kernel(int iters, float a, float b, unsigned long long* out, float* sink) {
   const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
   float s;
@@ -145,7 +198,7 @@ __global__ void clock_kernel(int iters, float a, float b, unsigned long long* ou
 }
 
 // cyc: device array of 2 * wgs * waves_per_wg entries;
-// sink: device array of wgs * waves_per_wg floats.  kind 7 = clock_kernel.
+// sink: device array of 64 * wgs * waves_per_wg floats.  kind 7 = clock_kernel.
 extern "C" int issue_rate_probe_run(int kind, int wgs, int waves_per_wg, int iters, void* cyc, void* sink,
                                     void* stream) {
   if (wgs < 1 || waves_per_wg < 1 || waves_per_wg > 16 || iters < 1) return -1;
@@ -164,6 +217,8 @@ extern "C" int issue_rate_probe_run(int kind, int wgs, int waves_per_wg, int ite
     case 6: hipLaunchKernelGGL(rate_kernel<6>, grid, block, 0, s, iters, a, b, c, k); break;
     case 7: hipLaunchKernelGGL(clock_kernel, grid, block, 0, s, iters, a, b, c, k); break;
     case 8: hipLaunchKernelGGL(rate_kernel<8>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 9: hipLaunchKernelGGL(lds_kernel<false>, grid, block, 0, s, iters, c, k); break;
+    case 10: hipLaunchKernelGGL(lds_kernel<true>, grid, block, 0, s, iters, c, k); break;
     default: return -1;
   }
   return (int)hipGetLastError();

@@ -102,7 +102,10 @@ def _check(inp, causal, scale, rows=None, out_dtype=torch.float32, label="", che
 
 # ---------------------------------------------------------------- preparation
 
-PREP_N = [1, 63, 64, 65, 200, 256, 300, 1000]
+# (6400 and 8269: 25 and 33 column-statistics chunks of 256 tokens, so the K
+# mean and V scales combine chunk partials in the unrolled loop of the
+# finalisation as well as in its tail)
+PREP_N = [1, 63, 64, 65, 200, 256, 300, 1000, 6400, 8269]
 
 
 @pytest.mark.parametrize("N", PREP_N)

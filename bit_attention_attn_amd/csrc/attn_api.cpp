@@ -207,7 +207,6 @@ attn_status prep8(const void* q, const void* k, const void* v, int in_dtype, int
   if (q == nullptr || k == nullptr || v == nullptr) return ATTN_ERR_NULL;
   attn_status s = check_shape(B, H, N, d);
   if (s != ATTN_OK) return s;
-  if (fmt == attn::kPrepFp8 && d == 96) return ATTN_ERR_HEADDIM;
   if (in_dtype != ATTN_DTYPE_F16 && in_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
   if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
@@ -235,7 +234,6 @@ attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N
   if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
   attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
   if (s != ATTN_OK) return s;
-  if (qk_fp8 && d == 96) return ATTN_ERR_HEADDIM;
   if (out_dtype != ATTN_DTYPE_F16 && out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32)
     return ATTN_ERR_DTYPE;
   if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;

@@ -474,7 +474,10 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   constexpr int kDT = D / 32;  // 32-row tiles of O^T
   constexpr int kKS = D / 32;  // 16-byte Q chunks per lane (INT8: one per 32-deep k-step;
                                // FP8: two per 64-deep k-step)
-  static_assert(!QKFP8 || D % 64 == 0, "FP8 scores need d a multiple of 64");
+  // FP8: D / 64 full 64-deep steps; at d = 96 a last step covers channels
+  // 64..95 with half of each lane's 32 operand bytes zero (kHalf8)
+  constexpr int kFull8 = D / 64;
+  constexpr bool kHalf8 = QKFP8 && D % 64 != 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::kBytes];
   uint8_t* const kl = smem;               // 2 K tiles
   uint8_t* const vl = smem + 2 * kKTile;  // 2 V tiles
@@ -502,12 +505,13 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
   const uint8_t* __restrict__ Vq = p.vq + headp;
 
   // Qq^T as the B operand: lane holds Qq[qw0 + l32][32kk + 16hf .. +15]
-  // (INT8), or bytes 64(kk/2) + 32hf + 16(kk%2) .. +15 (FP8, 32 bytes per
-  // 64-deep step); rows up to the padded length are valid zero codes.
+  // (INT8, and the half FP8 step), or bytes 64(kk/2) + 32hf + 16(kk%2) ..
+  // +15 (a full FP8 step, 32 bytes per 64-deep step); rows up to the padded
+  // length are valid zero codes.
   u32x4_t qf[kKS];
 #pragma unroll
   for (int kk = 0; kk < kKS; ++kk) {
-    const int col = QKFP8 ? 64 * (kk >> 1) + 32 * hf + 16 * (kk & 1) : 32 * kk + 16 * hf;
+    const int col = (QKFP8 && kk < 2 * kFull8) ? 64 * (kk >> 1) + 32 * hf + 16 * (kk & 1) : 32 * kk + 16 * hf;
     qf[kk] = *(const u32x4_t*)(Qq + (size_t)(qw0 + l32) * D + col);
   }
   const float sqw = p.sq[(size_t)bh * p.nblk + qw0 / kQB];
@@ -548,14 +552,16 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
     }
   };
   // operand read offsets inside a tile: K rows 32T + l32 at the logical
-  // chunks of k-step kk (INT8: 2kk + hf; FP8: 4kk + 2hf and +1), V rows
+  // chunks of k-step kk (INT8 and the half FP8 step: 2kk + hf; a full FP8
+  // step: 4kk + 2hf and +1), V rows
   // 32dt + l32 at chunks 2hf and 2hf + 1
   // (row 32 + l32 rotates like row l32: the second 32-row half is 32*D
   // bytes further)
   uint32_t ko[kKS];
 #pragma unroll
   for (int kk = 0; kk < kKS; ++kk)
-    ko[kk] = QKFP8 ? k_pos<D>(l32, 4 * (kk >> 1) + 2 * hf + (kk & 1)) : k_pos<D>(l32, 2 * kk + hf);
+    ko[kk] = (QKFP8 && kk < 2 * kFull8) ? k_pos<D>(l32, 4 * (kk >> 1) + 2 * hf + (kk & 1))
+                                         : k_pos<D>(l32, 2 * kk + hf);
   auto kofs = [&](int T, int kk) -> uint32_t { return ko[kk] + 32 * T * D; };
   const uint32_t vo0 = v_pos(l32, 2 * hf), vo1 = v_pos(l32, 2 * hf + 1);
 
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
         const uint8_t* Ks = kl + buf * kKTile;
         s[0] = s[1] = f32x16_t{};
 #pragma unroll
-        for (int kk = 0; kk < kKS / 2; ++kk)
+        for (int kk = 0; kk < kFull8; ++kk)
 #pragma unroll
           for (int T = 0; T < 2; ++T) {
             const u32x4_t a0 = *(const u32x4_t*)(Ks + kofs(T, 2 * kk));
@@ -602,6 +608,19 @@ __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const 
                                  (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
             s[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, s[T], 0, 0, 0, 0, 0, 0);
           }
+        if constexpr (kHalf8) {
+          // channels 64..95: lane half hf gives channels 64 + 16hf .. +15 as
+          // its k-slice's first 16 bytes, zeros (e4m3 +0) as the other 16, in
+          // both operands, so the padding adds exact zeros
+          const u32x4_t b0 = qf[2 * kFull8];
+#pragma unroll
+          for (int T = 0; T < 2; ++T) {
+            const u32x4_t a0 = *(const u32x4_t*)(Ks + kofs(T, 2 * kFull8));
+            const i32x8_t aop = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], 0, 0, 0, 0};
+            const i32x8_t bop = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], 0, 0, 0, 0};
+            s[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, s[T], 0, 0, 0, 0, 0, 0);
+          }
+        }
       } else {
         // ---- S^T = Kq Qq^T on top of the offset, exact
         const uint8_t* Ks = kl + buf * kKTile;
@@ -847,7 +866,11 @@ hipError_t fwd8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream, bool qk_fp8) {
-  if (qk_fp8) return a.d == 64 ? fwd8_d<64, true>(ws, a, stream) : fwd8_d<128, true>(ws, a, stream);
+  if (qk_fp8) {
+    if (a.d == 64) return fwd8_d<64, true>(ws, a, stream);
+    if (a.d == 96) return fwd8_d<96, true>(ws, a, stream);
+    return fwd8_d<128, true>(ws, a, stream);
+  }
   if (a.d == 64) return fwd8_d<64, false>(ws, a, stream);
   if (a.d == 96) return fwd8_d<96, false>(ws, a, stream);
   return fwd8_d<128, false>(ws, a, stream);

@@ -210,7 +210,8 @@ attn_status attn_fwd_sage8(const void* workspace, void* o, float* lse, int B,
  * layout; Qq and Kq hold e4m3 bytes) must be written by
  * attn_k_smooth_quant_fp8qk for attn_fwd_sage8_fp8qk and by
  * attn_k_smooth_quant for attn_fwd_sage8; the library cannot tell them
- * apart.  d must be 64 or 128.  Other arguments as for the INT8 pair.
+ * apart.  At d = 96 the last 64-deep product covers channels 64..95 with
+ * zero codes for the rest.  Other arguments as for the INT8 pair.
  */
 attn_status attn_k_smooth_quant_fp8qk(const void* q, const void* k, const void* v,
                                       int in_dtype, int B, int H, int N, int d,
@@ -254,7 +255,7 @@ attn_status attn_fwd_sage8_pv16(const void* workspace, const void* v, int v_dtyp
  * tensors as the 16-bit strided forward.  The computation and the workspace
  * are exactly those of the contiguous pair for the same logical [B,H,N,d]
  * data; qk_format (ATTN_QK_INT8 or ATTN_QK_FP8) selects the recipe (INT8, or
- * the FP8-QK variant with d = 64 or 128) and must match between the two.
+ * the FP8-QK variant) and must match between the two.
  *
  *  strides    host array of 9 element strides: (batch, head, token) of q,
  *             then k, then v.  Each a multiple of 8 and >= 0, token strides

@@ -166,12 +166,12 @@ def test_fp8qk_validation():
     need = L.attn_sage8_workspace_size(1, 2, 100, 64)
     prep = L.attn_k_smooth_quant_fp8qk
     assert prep(None, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need, None) == E_NULL
-    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 96, FAKE, need, None) == E_HEADDIM  # d = 96: INT8 only
+    assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 80, FAKE, need, None) == E_HEADDIM  # d = 64, 96 or 128
     assert prep(FAKE, FAKE, FAKE, F32, 1, 2, 100, 64, FAKE, need, None) == E_DTYPE
     assert prep(FAKE, FAKE, FAKE, BF16, 1, 2, 100, 64, FAKE, need - 1, None) == E_WS
     fwd8 = L.attn_fwd_sage8_fp8qk
     assert fwd8(None, FAKE, None, 1, 2, 100, 64, 0, 0.1, None, BF16, None) == E_WS
-    assert fwd8(FAKE, FAKE, None, 1, 2, 100, 96, 0, 0.1, None, BF16, None) == E_HEADDIM
+    assert fwd8(FAKE, FAKE, None, 1, 2, 100, 80, 0, 0.1, None, BF16, None) == E_HEADDIM
     assert fwd8(FAKE, FAKE, None, 1, 2, 100, 64, 3, 0.1, None, BF16, None) == E_ARG
 
 
@@ -194,7 +194,7 @@ def test_sage8_strided_validation():
     assert p(contig, q=None) == E_NULL
     assert p(contig, fmt=3) == E_ARG
     assert p(contig, fmt=2, dd=80) == E_HEADDIM      # INT8 Q/K only: checked like the INT8 format
-    assert p(contig, fmt=1, dd=96) == E_HEADDIM      # FP8 scores: d = 64 or 128
+    assert p(contig, fmt=1, dd=80) == E_HEADDIM      # FP8 scores: d = 64, 96 or 128
     assert p(contig, nb=need - 1) == E_WS
     assert p(nhd[:2] + [d - 8] + nhd[3:]) == E_ARG    # token stride below d
     assert p(nhd[:1] + [d + 4] + nhd[2:]) == E_ALIGN  # not a multiple of 8 elements
@@ -214,7 +214,7 @@ def test_sage8_strided_validation():
     assert f([N * H * d, d, H * d], fmt=2) == E_ARG  # a Q/K-only workspace has no FP8 V
     assert f([N * H * d, d, 8]) == E_ARG              # token stride below d
     assert f([N * H * d, d + 2, H * d]) == E_ALIGN
-    assert f([N * H * d, d, H * d], fmt=1, dd=96) == E_HEADDIM
+    assert f([N * H * d, d, H * d], fmt=1, dd=80) == E_HEADDIM
     assert f([0, d, H * d], cu=FAKE, bias=FAKE) == E_ARG  # packed sequences take no bias
     assert f([0, d, H * d], cu=FAKE + 2) == E_ALIGN
 

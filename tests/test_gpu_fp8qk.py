@@ -121,7 +121,7 @@ def _check(inp, causal, scale, rows=None, label="", check_oracle=True):
 
 
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 200, 300])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_prep_bit_exact(N, d, dtype):
     inp = workloads.make_inputs(2, 2, N, d, dtype, seed=5 * N + d, outliers=(N % 2 == 0))
@@ -141,7 +141,7 @@ def test_prep_bit_exact(N, d, dtype):
 
 
 @pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 300])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_small_sweep(N, d, causal, with_bias):
@@ -149,10 +149,11 @@ def test_small_sweep(N, d, causal, with_bias):
     _check(inp, causal, 1 / math.sqrt(d), label=f"sweep N={N} d={d} bias={with_bias}", check_oracle=N >= 64)
 
 
-def test_outliers_long_rows():
-    inp = workloads.make_inputs(1, 2, 2048, 128, "bf16", seed=23, outliers=True)
-    rows = workloads.parity_rows(1, 2, 2048, seed=23, n_random=32)
-    _check(inp, True, 1 / math.sqrt(128), rows=rows, label="outliers N=2048")
+@pytest.mark.parametrize("d", [96, 128])
+def test_outliers_long_rows(d):
+    inp = workloads.make_inputs(1, 2, 2048 + 37, d, "bf16", seed=23 + d, outliers=True)
+    rows = workloads.parity_rows(1, 2, 2048 + 37, seed=23, n_random=32)
+    _check(inp, True, 1 / math.sqrt(d), rows=rows, label=f"outliers N=2085 d={d}")
 
 
 def test_block_sparse_and_scale_edges():

@@ -37,8 +37,6 @@ def _inputs(B, H, N, d, dtype, seed, outliers=False):
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("qk", ["int8", "fp8"])
 def test_token_major_prep_and_forward(N, d, qk):
-    if qk == "fp8" and d == 96:
-        pytest.skip("FP8 scores take d = 64 or 128")
     print(f"[gpu] sage8 strided token-major N={N} d={d} qk={qk}", flush=True)
     q, k, v = _inputs(2, 3, N, d, "bf16", seed=N + d, outliers=True)
     # token-major storage, viewed as [B,H,N,d]

@@ -97,8 +97,6 @@ def _run(lens, H, d, dtype, qk, seed, out_dtype=None):
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("qk", ["int8", "fp8"])
 def test_packed_equals_separate(lens, d, qk):
-    if qk == "fp8" and d == 96:
-        pytest.skip("FP8 scores take d = 64 or 128")
     print(f"[gpu] sage8 varlen lens={lens} d={d} qk={qk}", flush=True)
     _run(lens, 3, d, "bf16", qk, seed=sum(lens) + d)
 

@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
     ll_p = ctypes.POINTER(ctypes.c_longlong)
     for name in ("attn_fwd_strided_f16", "attn_fwd_strided_bf16"):
         fn = getattr(L, name)
-        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, ll_p, vp, i, f, i, vp]
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, ll_p, vp, i, f, vp, i, vp]
         fn.restype = i
     L.attn_bwd_workspace_size.argtypes = [i, i, i, i]
     L.attn_bwd_workspace_size.restype = sz
@@ -248,12 +248,12 @@ def attention(q, k, v, causal=False, scale=None, bias=None):
     return _Attention.apply(q, k, v, bias, bool(causal), scale)
 
 
-def _strided_call(q, k, v, o, lse, B, H, N, d, strides, cu, causal, scale, out_dtype):
+def _strided_call(q, k, v, o, lse, B, H, N, d, strides, cu, causal, scale, out_dtype, bias=None):
     fn = lib().attn_fwd_strided_bf16 if q.dtype == torch.bfloat16 else lib().attn_fwd_strided_f16
     arr = (ctypes.c_longlong * 12)(*[int(x) for x in strides])
     with torch.cuda.device(q.device):
         st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, arr, _ptr(cu), int(bool(causal)),
-                float(scale), _DTYPE_CODE.get(out_dtype, -1), _stream(q.device))
+                float(scale), _ptr(bias), _DTYPE_CODE.get(out_dtype, -1), _stream(q.device))
     if st != 0:
         raise AttnError(st, fn.__name__)
 
@@ -269,15 +269,16 @@ def _check_views(ts, ndim):
         raise ValueError("q, k, v must be on one device")
 
 
-def fwd_strided(q, k, v, causal=False, scale=None, out_dtype=None, return_lse=False):
+def fwd_strided(q, k, v, causal=False, scale=None, out_dtype=None, return_lse=False, bias=None):
     """Fused attention forward on logical [B,H,N,d] tensors of any layout
     with d contiguous (e.g. x.transpose(1, 2) of a [B,N,H,d] tensor, or
     views of a fused QKV projection).  O has q's layout (empty_like); LSE is
-    [B,H,N] fp32."""
+    [B,H,N] fp32; bias as for fwd ([B,H,nb,nb] fp32)."""
     _check_views((q, k, v), 4)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same logical shape")
     B, H, N, d = q.shape
+    bias = _check_bias(bias, B, H, N, q.device)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -286,7 +287,7 @@ def fwd_strided(q, k, v, causal=False, scale=None, out_dtype=None, return_lse=Fa
     strides = []
     for t in (q, k, v, o):
         strides += [t.stride(0), t.stride(1), t.stride(2)]
-    _strided_call(q, k, v, o, lse, B, H, N, d, strides, None, causal, scale, out_dtype)
+    _strided_call(q, k, v, o, lse, B, H, N, d, strides, None, causal, scale, out_dtype, bias)
     return (o, lse) if return_lse else o
 
 
@@ -316,18 +317,22 @@ def _check_cu(cu_seqlens, device, max_seqlen=None, total=None):
         raise ValueError(f"a sequence is longer than max_seqlen ({int(lens.max())} > {int(max_seqlen)})")
 
 
-def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False):
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False,
+               bias=None):
     """Fused attention forward on packed sequences: q, k, v [total,H,d] (d
     contiguous), cu_seqlens int32 [B+1] on the device (sequence b is tokens
     cu_seqlens[b] .. cu_seqlens[b+1]-1, attending only within itself),
     max_seqlen the longest length.  O is [total,H,d] like q; LSE is
-    [B,H,max_seqlen] fp32."""
+    [B,H,max_seqlen] fp32.  bias: [B,H,nb,nb] fp32 with nb =
+    ceil(max_seqlen/64); sequence b takes bias[b,h,i,j] for its query block i
+    and key block j, counted from its own first token."""
     _check_views((q, k, v), 3)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
     total, H, d = q.shape
     _check_cu(cu_seqlens, q.device, max_seqlen, total)
     B = cu_seqlens.numel() - 1
+    bias = _check_bias(bias, B, H, int(max_seqlen), q.device)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -336,7 +341,7 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dt
     strides = []
     for t in (q, k, v, o):
         strides += [0, t.stride(1), t.stride(0)]
-    _strided_call(q, k, v, o, lse, B, H, int(max_seqlen), d, strides, cu_seqlens, causal, scale, out_dtype)
+    _strided_call(q, k, v, o, lse, B, H, int(max_seqlen), d, strides, cu_seqlens, causal, scale, out_dtype, bias)
     return (o, lse) if return_lse else o
 
 
@@ -431,13 +436,14 @@ def fwd_sage8(prep: Sage8Prepared, causal=False, scale=None, bias=None, out_dtyp
     """8-bit fused forward from a prepared workspace.  O is contiguous
     [B,H,N,d], or has the layout of the logical [B,H,N,d] tensor layout_like
     (torch.empty_like, so a token-major view gives a token-major O).  After
-    sage8_prep_varlen, O is packed [total,H,d] and takes no bias; the LSE is
-    [B,H,max_seqlen] either way."""
+    sage8_prep_varlen, O is packed [total,H,d] and the LSE [B,H,max_seqlen];
+    a bias [B,H,nb,nb] then gives sequence b the blocks bias[b,h,i,j]
+    counted from its own first token."""
     B, H, N, d = prep.shape
     dev = prep.workspace.device
     packed = prep.cu_seqlens is not None
-    if packed and (bias is not None or layout_like is not None):
-        raise ValueError("packed sequences take neither a bias nor layout_like")
+    if packed and layout_like is not None:
+        raise ValueError("packed sequences take no layout_like")
     if prep.qk == "int8_no_v":
         raise ValueError("this preparation holds no FP8 V: use fwd_sage8_pv16")
     bias = _check_bias(bias, B, H, N, dev)
@@ -525,12 +531,13 @@ def sageattn_pv16(q, k, v, causal=False, scale=None, bias=None, out_dtype=None, 
 
 
 def sageattn_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out_dtype=None, return_lse=False,
-                    qk="int8"):
+                    qk="int8", bias=None):
     """8-bit attention on packed sequences in one call: q, k, v [total,H,d],
     cu_seqlens int32 [B+1] on the device, max_seqlen the longest length.  O
-    is [total,H,d]; each sequence attends only within itself."""
+    is [total,H,d]; each sequence attends only within itself; bias as for
+    fwd_varlen."""
     prep = sage8_prep_varlen(q, k, v, cu_seqlens, max_seqlen, qk=qk)
-    return fwd_sage8(prep, causal=causal, scale=scale, out_dtype=out_dtype, return_lse=return_lse)
+    return fwd_sage8(prep, causal=causal, scale=scale, bias=bias, out_dtype=out_dtype, return_lse=return_lse)
 
 
 def sage8_workspace_views(prep: Sage8Prepared) -> dict:

@@ -116,9 +116,9 @@ attn_status check_strides(const long long* st, int n, int N, int d, int extra) {
 
 attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int H, int N, int d, const long long* strides, const int* cu_seqlens, int causal,
-                          float scale, int out_dtype, void* stream) {
+                          float scale, const float* bias, int out_dtype, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || strides == nullptr) return ATTN_ERR_NULL;
-  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, nullptr);
+  attn_status s = check_common(o, lse, B, H, N, d, causal, scale, bias);
   if (s != ATTN_OK) return s;
   const int in_dtype = bf16 ? ATTN_DTYPE_BF16 : ATTN_DTYPE_F16;
   if (out_dtype != in_dtype && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
@@ -131,7 +131,7 @@ attn_status fwd16_strided(bool bf16, const void* q, const void* k, const void* v
   if (s != ATTN_OK) return s;
   s = check_device();
   if (s != ATTN_OK) return s;
-  attn::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, d, causal, scale,
+  attn::FwdArgs a{q, k, v, o, lse, bias, B, H, N, d, causal, scale,
                   out_dtype == ATTN_DTYPE_F32 ? attn::kOutF32 : (bf16 ? attn::kOutBF16 : attn::kOutF16)};
   a.general = true;
   for (int i = 0; i < 12; ++i) a.strides[i] = strides[i];
@@ -237,7 +237,6 @@ attn_status fwd8(const void* workspace, void* o, float* lse, int B, int H, int N
   if (out_dtype != ATTN_DTYPE_F16 && out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32)
     return ATTN_ERR_DTYPE;
   if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
-  if (cu_seqlens != nullptr && bias != nullptr) return ATTN_ERR_ARG;
   if (cu_seqlens != nullptr && !aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
   if (o_strides != nullptr) {
     s = check_strides(o_strides, 1, N, d, 0);
@@ -295,14 +294,16 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
 
 attn_status attn_fwd_strided_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int N, int d, const long long* strides, const int* cu_seqlens, int causal,
-                                 float scale, int out_dtype, void* stream) {
-  return fwd16_strided(false, q, k, v, o, lse, B, H, N, d, strides, cu_seqlens, causal, scale, out_dtype, stream);
+                                 float scale, const float* bias, int out_dtype, void* stream) {
+  return fwd16_strided(false, q, k, v, o, lse, B, H, N, d, strides, cu_seqlens, causal, scale, bias, out_dtype,
+                       stream);
 }
 
 attn_status attn_fwd_strided_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                   int N, int d, const long long* strides, const int* cu_seqlens, int causal,
-                                  float scale, int out_dtype, void* stream) {
-  return fwd16_strided(true, q, k, v, o, lse, B, H, N, d, strides, cu_seqlens, causal, scale, out_dtype, stream);
+                                  float scale, const float* bias, int out_dtype, void* stream) {
+  return fwd16_strided(true, q, k, v, o, lse, B, H, N, d, strides, cu_seqlens, causal, scale, bias, out_dtype,
+                       stream);
 }
 
 size_t attn_sage8_workspace_size(int B, int H, int N, int d) {

@@ -149,8 +149,11 @@ struct Fwd16Smem {
 
 // Kernel variants by input layout: contiguous without a bias (the plain loop
 // over key blocks), contiguous with a block bias (adds the block-sparse skip)
-// and the general strided / packed-sequence layout (no bias).
-enum Mode { kDense = 0, kBias = 1, kGen = 2 };
+// and the general strided / packed-sequence layout without and with a block
+// bias.  A packed sequence takes its bias blocks from [b, h] of the
+// [B,H,nb,nb] bias, counted from its own first token (nb from the longest
+// length).
+enum Mode { kDense = 0, kBias = 1, kGen = 2, kGenBias = 3 };
 
 // The block bias comes as its own restrict argument: its reads, uniform and
 // never written by the kernel, then compile to scalar loads, which do not
@@ -172,7 +175,7 @@ template <int D, bool BF16, bool CAUSAL, int QS, int NW, int MODE, bool Q8 = fal
 __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, NW, Q8>)) void fwd16_kernel(Fwd16Params p,
                                                                                   const float* __restrict__ bias,
                                                                                   const float* __restrict__ sk) {
-  constexpr bool GEN = MODE == kGen, HAS_BIAS = MODE == kBias;
+  constexpr bool GEN = MODE == kGen || MODE == kGenBias, HAS_BIAS = MODE == kBias || MODE == kGenBias;
   static_assert(!(Q8 && GEN), "INT8 scores take the dense layout");
   using TL = Tiling<QS, NW>;
   using S = Fwd16Smem<D, QS, NW, Q8>;
@@ -731,7 +734,7 @@ hipError_t launch_impl(const FwdArgs& a, hipStream_t stream, const void* ws = nu
   // (persistent was 5% slower).
   // (packed sequences of different lengths: one workgroup per tile; the
   // balance argument of the persistent queues assumes equal heads)
-  const int grid = (CAUSAL && !(MODE == kGen && a.cu))
+  const int grid = (CAUSAL && !((MODE == kGen || MODE == kGenBias) && a.cu))
                        ? persistent_grid(reinterpret_cast<const void*>(&fwd16_kernel<D, BF16, CAUSAL, QS, NW, MODE, Q8>),
                                          TL::kThreads, p.nbh, p.nq)
                        : p.ntiles;
@@ -759,7 +762,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 
 template <bool BF16, bool CAUSAL>
 hipError_t launch_g(const FwdArgs& a, hipStream_t stream) {
-  if (a.general) return launch_d<BF16, CAUSAL, kGen>(a, stream);
+  if (a.general) return a.bias ? launch_d<BF16, CAUSAL, kGenBias>(a, stream) : launch_d<BF16, CAUSAL, kGen>(a, stream);
   return a.bias ? launch_d<BF16, CAUSAL, kBias>(a, stream) : launch_d<BF16, CAUSAL, kDense>(a, stream);
 }
 

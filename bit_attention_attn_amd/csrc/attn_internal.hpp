@@ -98,7 +98,8 @@ hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool b
 hipError_t launch_fwd_q8(const void* ws, const FwdArgs& a, bool bf16, hipStream_t stream);
 // O is written with the element strides a.strides[9..11] (batch, head,
 // token) when a.general, else contiguous [B,H,N,d].  With a.cu (packed
-// sequences, no bias) batch entry b writes its rows from token a.cu[b].
+// sequences) batch entry b writes its rows from token a.cu[b], and a block
+// bias is read at [b, h] with block indices counted from that token.
 hipError_t launch_fwd_sage8(const void* ws, const FwdArgs& a, hipStream_t stream, bool qk_fp8);
 
 }  // namespace attn

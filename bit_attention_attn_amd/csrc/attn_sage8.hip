@@ -856,7 +856,10 @@ hipError_t launch_sage8_prep(const void* q, const void* k, const void* v, bool b
 namespace {
 template <int D, bool QKFP8>
 hipError_t fwd8_d(const void* ws, const FwdArgs& a, hipStream_t stream) {
-  // packed sequences take no block bias (rejected by the caller)
+  // packed sequences: the bias blocks of sequence b are [b, h] of the
+  // [B,H,nb,nb] bias, counted from its first token
+  if (a.cu && a.bias) return a.causal ? fwd8_impl<D, true, true, QKFP8, true>(ws, a, stream)
+                                      : fwd8_impl<D, false, true, QKFP8, true>(ws, a, stream);
   if (a.cu) return a.causal ? fwd8_impl<D, true, false, QKFP8, true>(ws, a, stream)
                             : fwd8_impl<D, false, false, QKFP8, true>(ws, a, stream);
   if (a.bias) return a.causal ? fwd8_impl<D, true, true, QKFP8>(ws, a, stream)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 8
+#define ATTN_ABI_VERSION 9
 
 typedef enum {
     ATTN_OK = 0,
@@ -126,17 +126,25 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
  *             device and not validated: they must be non-decreasing with
  *             every length <= N (longer lengths are clamped to N).
  *  lse        nullable fp32 [B,H,N] (row b,h,i for i < the sequence length).
- *  Other arguments as attn_fwd_f16 / attn_fwd_bf16; there is no block bias
- *  on this entry point.  The arithmetic is that of attn_fwd_f16/bf16.
+ *  bias       nullable fp32 [B,H,nb,nb] contiguous, nb = ceil(N/64): the
+ *             block bias of attn_fwd_f16 / attn_fwd_bf16 (page 5, "SAS",
+ *             log-form gate).  With cu_seqlens, sequence b takes
+ *             bias[b,h,i,j] for its query block i and key block j, both
+ *             counted from its own first token (N, and so nb, from the
+ *             longest length).
+ *  Other arguments as attn_fwd_f16 / attn_fwd_bf16.  The arithmetic is that
+ *  of attn_fwd_f16/bf16.  (ABI version 9 added the bias argument.)
  */
 attn_status attn_fwd_strided_f16(const void* q, const void* k, const void* v, void* o,
                                  float* lse, int B, int H, int N, int d,
                                  const long long* strides, const int* cu_seqlens,
-                                 int causal, float scale, int out_dtype, void* stream);
+                                 int causal, float scale, const float* bias, int out_dtype,
+                                 void* stream);
 attn_status attn_fwd_strided_bf16(const void* q, const void* k, const void* v, void* o,
                                   float* lse, int B, int H, int N, int d,
                                   const long long* strides, const int* cu_seqlens,
-                                  int causal, float scale, int out_dtype, void* stream);
+                                  int causal, float scale, const float* bias, int out_dtype,
+                                  void* stream);
 
 /*
  * attn_sage8_workspace_size -- bytes of device workspace that
@@ -273,8 +281,10 @@ attn_status attn_fwd_sage8_pv16(const void* workspace, const void* v, int v_dtyp
  *             rows of O are bit for bit those of a separate call on it.  The
  *             values are read on the device and not validated (non-decreasing,
  *             lengths <= N; longer lengths are clamped to N); a length of 0 is
- *             allowed.  Both calls must get the same array; the forward then
- *             takes no bias (ATTN_ERR_ARG).
+ *             allowed.  Both calls must get the same array.  A bias is read
+ *             as for attn_fwd_strided_f16: sequence b takes bias[b,h,i,j]
+ *             for its query block i and key block j counted from its first
+ *             token, nb = ceil(N/64).
  *  The LSE stays [B,H,N] contiguous (row b,h,i for i below sequence b's
  *  length).  Other arguments and errors as for attn_k_smooth_quant and
  *  attn_fwd_sage8; a NULL stride array is ATTN_ERR_NULL, an unknown

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
             "attn_fwd_sage8", "attn_fwd_sage8_pv16", "attn_status_str", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 8
+    assert L.attn_abi_version() == 9
     for s in range(10):
         assert len(attn.status_str(s)) > 4
 
@@ -106,9 +106,9 @@ def test_python_binding_rejects_cpu_tensors():
         attn.sage8_prep_varlen(qp, qp, qp, cu, 8, qk="int4")
 
 
-def _strided(fn, strides, q=FAKE, o=FAKE, cu=None, B=1, H=2, N=64, d=64, causal=0, out=BF16):
+def _strided(fn, strides, q=FAKE, o=FAKE, cu=None, B=1, H=2, N=64, d=64, causal=0, out=BF16, bias=None):
     arr = None if strides is None else (ctypes.c_longlong * 12)(*strides)
-    return fn(q, FAKE, FAKE, o, None, B, H, N, d, arr, cu, causal, 0.125, out, None)
+    return fn(q, FAKE, FAKE, o, None, B, H, N, d, arr, cu, causal, 0.125, bias, out, None)
 
 
 @pytest.mark.parametrize("name,dt", [("attn_fwd_strided_bf16", BF16), ("attn_fwd_strided_f16", F16)])
@@ -130,6 +130,7 @@ def test_strided_validation(name, dt):
     assert _strided(fn, bad, N=1 << 12, out=dt) == E_SHAPE  # byte offsets beyond 32 bits
     assert _strided(fn, good, cu=FAKE + 2, out=dt) == E_ALIGN
     assert _strided(fn, good, causal=3, out=dt) == E_ARG
+    assert _strided(fn, good, bias=FAKE + 2, out=dt) == E_ALIGN  # bias not 4-byte aligned
 
 
 def _bwd(fn, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, dbias=None, B=1, H=2, N=100, d=64, causal=0,
@@ -215,7 +216,7 @@ def test_sage8_strided_validation():
     assert f([N * H * d, d, 8]) == E_ARG              # token stride below d
     assert f([N * H * d, d + 2, H * d]) == E_ALIGN
     assert f([N * H * d, d, H * d], fmt=1, dd=80) == E_HEADDIM
-    assert f([0, d, H * d], cu=FAKE, bias=FAKE) == E_ARG  # packed sequences take no bias
+    assert f([0, d, H * d], cu=FAKE, bias=FAKE + 2) == E_ALIGN  # packed sequences: the bias is checked too
     assert f([0, d, H * d], cu=FAKE + 2) == E_ALIGN
 
 
@@ -236,6 +237,11 @@ def test_bias_size_bounds():
         assert _fwd(fn, bias=FAKE, H=3, N=n_max, d=64, out=BF16 if fn is L.attn_fwd_bf16 else F16) == E_SHAPE
         # without a bias the same shape is not limited by it
         assert _fwd(fn, N=n_over, d=64, causal=2, out=BF16 if fn is L.attn_fwd_bf16 else F16) == E_ARG
+    good = [n_over * 64, n_over * 64, 64] * 4
+    for name, dt in (("attn_fwd_strided_bf16", BF16), ("attn_fwd_strided_f16", F16)):
+        fn = getattr(L, name)
+        assert _strided(fn, good, N=n_over, bias=FAKE, out=dt) == E_SHAPE
+        assert _strided(fn, good, N=n_max, bias=FAKE, causal=2, out=dt) == E_ARG
     for fwd8 in (L.attn_fwd_sage8, L.attn_fwd_sage8_fp8qk):
         assert fwd8(FAKE, FAKE, None, 1, 1, n_over, 64, 0, 0.1, FAKE, BF16, None) == E_SHAPE
         assert fwd8(FAKE, FAKE, None, 1, 1, n_max, 64, 2, 0.1, FAKE, BF16, None) == E_ARG

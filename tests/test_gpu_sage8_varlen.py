@@ -143,12 +143,13 @@ def test_sageattn_varlen_long_mix():
         assert torch.equal(o[t0:t0 + n], o_ref[0].transpose(0, 1)), b
 
 
-def test_packed_rejects_bias_and_layout():
+def test_packed_rejects_bad_bias_and_layout():
     q, k, v, cu = _packed([65, 10], 2, 64, "bf16", seed=1)
     prep = attn.sage8_prep_varlen(q, k, v, cu, 65)
-    bias = torch.zeros((2, 2, 2, 2), device=DEV)
+    with pytest.raises(ValueError):  # nb must come from max_seqlen: ceil(65/64) = 2
+        attn.fwd_sage8(prep, bias=torch.zeros((2, 2, 1, 1), device=DEV))
     with pytest.raises(ValueError):
-        attn.fwd_sage8(prep, bias=bias)
+        attn.fwd_sage8(prep, layout_like=torch.zeros((2, 2, 65, 64), device=DEV))
     with pytest.raises(ValueError):
         attn.sage8_prep_varlen(q, k, v, cu.long(), 65)
 
@@ -178,3 +179,38 @@ def test_packed_against_oracle():
             m_ref = workloads.error_metrics(got, o_ref)
             print(f"    packed sequence {b} (n={n}) vs fp32 model: {m}; vs fp64 attention: {m_ref}", flush=True)
             assert m_ref["cos"] >= 0.999, (b, m_ref)
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("qk", ["int8", "fp8"])
+@pytest.mark.parametrize("keep", [None, 0.3])
+def test_packed_with_block_bias(d, qk, keep):
+    """A block bias [B,H,nb,nb] (nb from the longest length) on packed
+    sequences: sequence b takes bias[b,h,i,j] for its blocks counted from its
+    own first token, so its rows of O and its LSE are bit for bit those of
+    the contiguous forward on it alone with the bias slice
+    bias[b:b+1, :, :nb_b, :nb_b] (gates with and without gated-off blocks)."""
+    lens = [130, 0, 64, 257, 1, 200]
+    H = 2
+    q, k, v, cu = _packed(lens, H, d, "bf16", seed=900 + d)
+    N = max(lens)
+    nb = (N + 63) // 64
+    g = torch.randn((len(lens), H, nb, nb), generator=torch.Generator("cpu").manual_seed(77 + d))
+    bias = workloads.gate_bias(g, keep=keep).to(DEV)
+    print(f"[gpu] sage8 varlen bias d={d} qk={qk} keep={keep}", flush=True)
+    prep = attn.sage8_prep_varlen(q, k, v, cu, N, qk=qk)
+    for causal in (False, True):
+        o, lse = attn.fwd_sage8(prep, causal=causal, bias=bias, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all()
+        for b, n in enumerate(lens):
+            if n == 0:
+                continue
+            ref = attn.sage8_prep(_seq(q, cu, b), _seq(k, cu, b), _seq(v, cu, b), qk=qk)
+            nbb = (n + 63) // 64
+            bb = bias[b:b + 1, :, :nbb, :nbb].contiguous()
+            o_ref, l_ref = attn.fwd_sage8(ref, causal=causal, bias=bb, return_lse=True)
+            t0 = int(cu[b])
+            assert torch.equal(o[t0:t0 + n], o_ref[0].transpose(0, 1)), (b, causal)
+            assert torch.equal(lse[b, :, :n], l_ref[0]), (b, causal)
+

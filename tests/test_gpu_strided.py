@@ -95,6 +95,62 @@ def test_packed_sequences(d, causal):
                1 / math.sqrt(d), f"seq {b} (n={n})")
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("keep", [None, 0.3])
+def test_packed_sequences_with_block_bias(d, causal, keep):
+    """A block bias [B,H,nb,nb] (nb from the longest length) on packed
+    sequences: sequence b takes bias[b,h,i,j] for its blocks counted from its
+    own first token.  Each sequence against the oracle with its bias slice
+    bias[b:b+1, :, :nb_b, :nb_b], and bit for bit against the contiguous
+    forward on it alone with that slice (gates with and without gated-off
+    blocks; the diagonal block is always kept)."""
+    lens = [1, 63, 64, 200, 513, 0, 77]
+    H = 2
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total, N = int(cu[-1]), max(lens)
+    nb = (N + 63) // 64
+    g = torch.Generator("cpu").manual_seed(31 + d + causal)
+    x = [torch.randn((total, H, d), generator=g).to(torch.bfloat16) for _ in range(3)]
+    bias = workloads.gate_bias(torch.randn((len(lens), H, nb, nb), generator=g), keep=keep)
+    q, k, v = (t.to(DEV) for t in x)
+    print(f"[gpu] varlen bias d={d} causal={causal} keep={keep}", flush=True)
+    o, lse = attn.fwd_varlen(q, k, v, torch.from_numpy(cu).to(DEV), N, causal=causal, return_lse=True,
+                             bias=bias.to(DEV))
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        nbb = (n + 63) // 64
+        bb = bias[b:b + 1, :, :nbb, :nbb].contiguous()
+        seq = [t[s0:s1].transpose(0, 1).unsqueeze(0) for t in x]  # [1,H,n,d]
+        qn, kn, vn = (t.float().contiguous().numpy() for t in seq)
+        o_ref, l_ref = oracle.attn_full(qn, kn, vn, causal=causal, scale=1 / math.sqrt(d), bias=bb.numpy())
+        got = o[s0:s1].transpose(0, 1).unsqueeze(0).double().cpu().numpy()
+        err = np.abs(got - o_ref)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (b, n, err.max(), err.mean())
+        assert np.abs(lse[b:b + 1, :, :n].double().cpu().numpy() - l_ref).max() <= LSE_TOL, (b, n)
+        o1, l1 = attn.fwd(*(t.to(DEV).contiguous() for t in seq), causal=causal, bias=bb.to(DEV),
+                          return_lse=True)
+        assert torch.equal(o[s0:s1], o1[0].transpose(0, 1)), (b, n)
+        assert torch.equal(lse[b, :, :n], l1[0]), (b, n)
+
+
+def test_strided_with_bias_matches_contiguous_entry():
+    """A token-major layout with a gate bias gives the contiguous entry's
+    result with the same bias, bit for bit."""
+    inp = workloads.make_inputs(2, 3, 333, 128, "bf16", seed=9, gate=True, gate_keep=0.5)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    bias = inp["bias"].to(DEV)
+    qt, kt, vt = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    for causal in (False, True):
+        o1 = attn.fwd(q, k, v, causal=causal, bias=bias)
+        o2 = attn.fwd_strided(qt, kt, vt, causal=causal, bias=bias)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2.contiguous())
+
+
 def test_packed_sequences_empty_and_padded_lse():
     """A zero-length sequence in the middle is allowed; O rows of the other
     sequences are unaffected."""

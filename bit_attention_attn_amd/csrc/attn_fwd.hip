@@ -182,7 +182,6 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, NW, Q8>)) void fwd16_kernel
   constexpr int kWQ = TL::kWQ, kBM = TL::kBM, kThreads = TL::kThreads;
   constexpr int kKbuf = TL::kKbuf;
   constexpr int kKTile = S::kKTile, kVTile = S::kVTile;
-  constexpr int kCpr = D / 8;  // 16-byte chunks of data per row
   constexpr int kDT = D / 32;  // 32-row tiles of O^T
   constexpr int kKS = D / 16;  // k-steps of S^T = K Q^T (Q8: D/32 of them)
   constexpr int kChunksK = kBN * S::kKC, kChunksV = kBN * S::kVC;  // 16-byte chunks per tile

@@ -19,6 +19,11 @@
 //   8-byte transposing reads (ds_read_b64_tr_b16, kind 10) from consecutive
 //   addresses of a 64 KB tile, 8 in flight; the workgroup's span over the bytes
 //   its waves read is the CU's LDS read bandwidth.
+// feed_kernel: every wave runs rounds of 16 bf16 32x32x16 products whose A
+//   operand comes from LDS, read two products ahead (kind 11: one 16-byte
+//   read per product; kind 12: two 8-byte transposing reads), the order
+//   pinned by scheduling barriers: how busy LDS-fed products keep the matrix
+//   unit.
 // clock_kernel: every wave runs bf16 MFMA chains for `iters` rounds and
 // writes its shader cycles and its 100 MHz real-time ticks (s_memrealtime),
 // so cycles / ticks * 100 MHz is the clock the chip ran at under that load.
@@ -182,6 +187,54 @@ __global__ void lds_kernel(int iters, unsigned long long* cyc, float* sink) {
   sink[wave * 64 + lane] = (float)acc;
 }
 
+template <bool TR>
+__global__ void feed_kernel(int iters, unsigned long long* cyc, float* sink) {
+  constexpr int kDepth = 2;
+  __shared__ __attribute__((aligned(16))) uint32_t tile[16384];  // 64 KB
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) tile[i] = 0x3f803f80u ^ (uint32_t)(i & 7);
+  __syncthreads();
+  const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63, w4 = (threadIdx.x / 64) & 3;
+  f32x16 acc[2] = {};
+  bf16x8 bv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bv[e] = (__bf16)(0.001f * (float)lane);
+  int it = 0;
+  // operand of product k in round it: rows move with it, so no read is loop-invariant
+  auto rd = [&](int k) -> uint4 {
+    if constexpr (TR) {
+      // byte offsets < 15 * 1024 + 504 + 512 + 8 <= 65536
+      const int o1 = (((k + it) & 15) * 1024 + lane * 8) / 4, o2 = o1 + 512 / 4;
+      const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + o1)));
+      const uint2 y = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + o2)));
+      return uint4{x.x, x.y, y.x, y.y};
+    } else {
+      // byte offsets < 15 * 1024 + 1008 + 16 + 3 * 16384 <= 65536
+      return *(const uint4*)(tile + (((k + it) & 15) * 1024 + lane * 16) / 4 + w4 * 4096);
+    }
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (it = 0; it < iters; ++it) {
+    uint4 buf[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) buf[i] = rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      acc[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, buf[k % kDepth]), bv, acc[k & 1],
+                                                           0, 0, 0);
+      if (k + kDepth < 16) buf[k % kDepth] = rd(k + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) {
+    cyc[2 * wave] = t0;
+    cyc[2 * wave + 1] = t1;
+  }
+  sink[wave * 64 + lane] = acc[0][0] + acc[1][5];
+}
+
 __global__ void clock_kernel(int iters, float a, float b, unsigned long long* out, float* sink) {
   const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
   float s;
@@ -219,6 +272,8 @@ extern "C" int issue_rate_probe_run(int kind, int wgs, int waves_per_wg, int ite
     case 8: hipLaunchKernelGGL(rate_kernel<8>, grid, block, 0, s, iters, a, b, c, k); break;
     case 9: hipLaunchKernelGGL(lds_kernel<false>, grid, block, 0, s, iters, c, k); break;
     case 10: hipLaunchKernelGGL(lds_kernel<true>, grid, block, 0, s, iters, c, k); break;
+    case 11: hipLaunchKernelGGL(feed_kernel<false>, grid, block, 0, s, iters, c, k); break;
+    case 12: hipLaunchKernelGGL(feed_kernel<true>, grid, block, 0, s, iters, c, k); break;
     default: return -1;
   }
   return (int)hipGetLastError();

@@ -7,7 +7,7 @@ these figures; the probe kernels (tests/probes/issue_rate_probe.hip, built by
 __graft_entry__.build()) measure them with the shader cycle counter on
 independent instruction chains, so no instruction waits for the previous one,
 and the LDS read bandwidth of one CU with the two read forms the kernels use
-for their matrix operands.
+for their matrix operands, alone and feeding a stream of products.
 The assertions hold only what the published peak rates fix (at most 32 fp32
 FMA lanes per SIMD and cycle, so a wave64 VALU instruction of one SIMD takes
 at least 2 cycles; a matrix instruction cannot beat the datasheet peak:
@@ -129,6 +129,24 @@ def test_lds_read_bandwidth(kind):
         bpc = waves * iters * 8 * per_instr / span
         print(f"    {name}, {waves} waves on one CU: {bpc:.1f} bytes per shader cycle", flush=True)
         assert 0.0 < bpc <= 512.0
+
+
+@pytest.mark.parametrize("kind", [11, 12])
+def test_lds_fed_product_stream(kind):
+    """Back-to-back bf16 32x32x16 products whose A operand comes from LDS,
+    read two products ahead (kind 11: 16-byte reads; kind 12: two 8-byte
+    transposing reads per product), with two and four waves per SIMD: the
+    cycles per product of each SIMD (32 would keep the matrix unit busy)."""
+    name = {11: "ds_read_b128", 12: "2x ds_read_b64_tr_b16"}[kind]
+    iters = 500
+    for per_simd in (2, 4):
+        waves = 4 * per_simd
+        _run(kind, 1, waves, 20)
+        t = _run(kind, 1, waves, iters)
+        cpp = float(t[:, 1].max() - t[:, 0].min()) / (per_simd * iters * 16)
+        print(f"    products fed by {name}, {per_simd} waves per SIMD: {cpp:.1f} cycles per product "
+              f"({100 * 32 / cpp:.0f}% of the matrix unit)", flush=True)
+        assert 31.0 <= cpp <= 96.0
 
 
 def test_clock_under_full_matrix_load():

@@ -54,9 +54,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 # Valid only for the kernel sources it was taken on: the sha256 of the listed
 # sources must match, else traffic is reported as null.
 TRAFFIC = {
-    # 1042721 KiB fetched (x2) + 262144 KiB written, mean of 7 dispatches
-    ("fwd16", 3): {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 2403927771,
-                   "sha256": "9e4bde153e751ff45113dcbc9e4ac7d728ced54a6d8c2a38d8561753b9b269f0"},
+    # 1053830 KiB fetched (x2) + 262144 KiB written, mean of 7 dispatches
+    ("fwd16", 3): {"sources": ["attn_fwd.hip", "attn_common.hpp"], "bytes": 2426679387,
+                   "sha256": "8a76a9050c47898d71f5d669c1fd47e77ecdba57e87f32829e47272d46a7185f"},
 }
 
 

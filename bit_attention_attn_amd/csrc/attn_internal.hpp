@@ -81,7 +81,7 @@ struct Sage8Layout {
 };
 Sage8Layout sage8_layout(int B, int H, int N, int d);
 // fmt: kPrepInt8 (the INT8 recipe), kPrepFp8 (Q and K in e4m3 blocks, the
-// FP8-QK variant; d = 64 or 128) or kPrepInt8NoV (INT8 Q and K only, for the
+// FP8-QK variant) or kPrepInt8NoV (INT8 Q and K only, for the
 // 16-bit P V variant: V's statistics, codes and regions are not touched);
 // the forward must be told the format the preparation wrote.
 // strides: element strides (batch, head, token) of q, k, v with d

@@ -37,7 +37,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ATTN_ORACLE_LIB: another build of the same sources (the tests' sanitizer build)
+_LIB_PATH = os.environ.get("ATTN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _i64 = ctypes.c_int64

@@ -16,6 +16,22 @@ CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 
+# Host sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer) for the
+# tests: single-threaded (no OpenMP), every undefined-behaviour report fatal.
+SAN_CFLAGS = ["-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+              "-Wall", "-Wextra", "-Wno-unknown-pragmas", "-fno-omit-frame-pointer",
+              "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(out_path: str, verbose: bool = False) -> str:
+    srcs = [os.path.join(HERE, s) for s in SOURCES]
+    cmd = ["gcc", *SAN_CFLAGS, *srcs, "-o", out_path, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(HERE, s) for s in SOURCES]
     tmp = LIB + ".tmp"

@@ -90,3 +90,8 @@ def test_graph_packed_sequences():
     # (no LSE here: its rows past a sequence's length are never written)
     _check_graph(lambda: attn.fwd_varlen(q, k, v, cu, N, causal=True), "fwd16 packed")
     _check_graph(lambda: attn.sageattn_varlen(q, k, v, cu, N, causal=True), "sage8 packed")
+    nb = (N + 63) // 64
+    bias = workloads.gate_bias(torch.randn((len(lens), H, nb, nb), generator=torch.Generator("cpu").manual_seed(6)),
+                               keep=0.5).to(DEV)
+    _check_graph(lambda: attn.fwd_varlen(q, k, v, cu, N, causal=True, bias=bias), "fwd16 packed + bias")
+    _check_graph(lambda: attn.sageattn_varlen(q, k, v, cu, N, causal=True, bias=bias), "sage8 packed + bias")

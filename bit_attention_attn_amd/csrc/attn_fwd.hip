@@ -43,8 +43,10 @@
 //       to both operands); V^T is read from the row-major V tile with the
 //       transposing LDS read.
 // The output is normalised once and stored straight from the accumulators.
-// The grid is persistent: as many workgroups as fit on the device at once,
-// each looping over work items in a balanced heavy-first order.
+// Causal launches whose tiles balance over the resident slots use a
+// persistent grid (as many workgroups as fit on the device at once, each
+// looping over work items in a balanced heavy-first order); the others run
+// one workgroup per work item.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 

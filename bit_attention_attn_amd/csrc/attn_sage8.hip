@@ -465,7 +465,8 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // runs on the FP8 32x32x64 instruction, with no offset on the accumulators.
 // VARLEN: batch entry b is the packed sequence of tokens cu[b] .. cu[b+1]-1
 // (its workspace slot prepared from that sequence alone): its length bounds
-// the keys and rows, and its rows of O start at token cu[b].
+// the keys and rows, its rows of O start at token cu[b], and with BIAS its
+// blocks are those of [b, h] of the bias, counted from that token.
 template <int D, bool CAUSAL, bool BIAS, bool QKFP8, bool VARLEN>
 __global__ __launch_bounds__(kThreads8, 3) void fwd8_kernel(Fwd8Params p, const float* __restrict__ bias,
                                                             const float* __restrict__ sk) {

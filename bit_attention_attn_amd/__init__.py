@@ -18,9 +18,10 @@ raised.
     sageattn_varlen(q, k, v, cu_seqlens, max_seqlen, ...)  # 8-bit, packed sequences
 
 Tensors are [B, H, N, d] contiguous CUDA (HIP) tensors, d in {64, 96, 128}
-(the 8-bit path and its FP8-QK variant: INT8 scores at 64, 96, 128; FP8 at 64, 128).
+on every path (INT8 or FP8 scores alike).
 ``bias`` is fp32 [B, H, ceil(N/64), ceil(N/64)]: an additive logit per
-64-query x 64-key block in natural-log units.
+64-query x 64-key block in natural-log units (packed sequences: N is the
+longest length and sequence b takes bias[b] counted from its first token).
 """
 from __future__ import annotations
 

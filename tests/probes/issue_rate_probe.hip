@@ -15,6 +15,10 @@
 //     two pipes)
 //   8 v_exp_f32 and v_fma_f32 alternating on separate chains (16 of each:
 //     whether the transcendental unit runs beside the FMA)
+//  13 MFMA 32x32x16 bf16 on one accumulator: each product adds onto the
+//     previous one's result (the dependent issue rate)
+//  14 one bf16 MFMA + 4 v_exp_f32 (8 chains) per step: whether exponentials
+//     run beside the products as FMAs do
 // lds_kernel: every wave streams 16-byte LDS reads (ds_read_b128, kind 9) or
 //   8-byte transposing reads (ds_read_b64_tr_b16, kind 10) from consecutive
 //   addresses of a 64 KB tile, 8 in flight; the workgroup's span over the bytes
@@ -109,6 +113,12 @@ __device__ __forceinline__ void run_rounds(int iters, float a, float b, float* o
         for (int c = 0; c < 4; ++c) {
           if constexpr (KIND == 3 || KIND == 6)
             acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[c], 0, 0, 0);
+          if constexpr (KIND == 13) acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[0], 0, 0, 0);
+          if constexpr (KIND == 14) {
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[c], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[4 * (c & 1) + i] = __builtin_amdgcn_exp2f(x[4 * (c & 1) + i]);
+          }
           if constexpr (KIND == 4) iacc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bi, iacc[c], 0, 0, 0);
           if constexpr (KIND == 5)
             acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, acc[c], 0, 0, 0, 0, 0, 0);
@@ -274,6 +284,8 @@ extern "C" int issue_rate_probe_run(int kind, int wgs, int waves_per_wg, int ite
     case 10: hipLaunchKernelGGL(lds_kernel<true>, grid, block, 0, s, iters, c, k); break;
     case 11: hipLaunchKernelGGL(feed_kernel<false>, grid, block, 0, s, iters, c, k); break;
     case 12: hipLaunchKernelGGL(feed_kernel<true>, grid, block, 0, s, iters, c, k); break;
+    case 13: hipLaunchKernelGGL(rate_kernel<13>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 14: hipLaunchKernelGGL(rate_kernel<14>, grid, block, 0, s, iters, a, b, c, k); break;
     default: return -1;
   }
   return (int)hipGetLastError();

@@ -35,6 +35,7 @@ KINDS = {
     3: ("mfma 32x32x16 bf16", 32, 31.0, 100.0),
     4: ("mfma 32x32x32 i8", 32, 31.0, 100.0),
     5: ("mfma 32x32x64 fp8", 32, 62.0, 200.0),
+    13: ("mfma 32x32x16 bf16, each onto the previous result", 32, 31.0, 200.0),
 }
 
 
@@ -101,6 +102,19 @@ def test_matrix_and_valu_overlap():
     print(f"    one product + 8 fma: {mix:.1f} cycles per step (product alone {mf:.1f}, "
           f"8 fma alone {8 * fma:.1f}, both in series {serial:.1f}); "
           f"{100 * (serial - mix) / (8 * fma):.0f}% of the VALU time hidden", flush=True)
+    assert 0.95 * mf <= mix <= serial * 1.1
+
+
+def test_matrix_and_exp_overlap():
+    """One bf16 32x32x16 product plus four v_exp_f32 per step (independent
+    registers): whether the exponentials hide behind the products."""
+    mix = _alone(14, 1000) * 64 / 32
+    mf = _alone(3, 1000)
+    ex = _alone(1, 4000)
+    serial = mf + 4 * ex
+    print(f"    one product + 4 exp: {mix:.1f} cycles per step (product alone {mf:.1f}, "
+          f"4 exp alone {4 * ex:.1f}, both in series {serial:.1f}); "
+          f"{100 * (serial - mix) / (4 * ex):.0f}% of the exponential time hidden", flush=True)
     assert 0.95 * mf <= mix <= serial * 1.1
 
 

@@ -52,7 +52,7 @@
 
 #include <math.h>
 
-#include <atomic>
+#include <mutex>
 
 namespace attn {
 namespace {
@@ -789,23 +789,32 @@ hipError_t launch_q8_g(const void* ws, const FwdArgs& a, hipStream_t stream) {
 
 // Workgroups of `kernel` resident at once on the current device (a multiple
 // of 8 when at least 8), cached per kernel and device; -1 on a HIP error.
+// The cache is shared by every host thread that launches: entries are
+// looked up and added under one lock (the occupancy query itself runs
+// outside it; two threads that miss together both query and the first
+// stores the same value).
 int resident_slots(const void* kernel, int threads) {
   struct Entry { const void* k; int dev; int slots; };
   static Entry cache[64];
-  static std::atomic<int> used{0};
+  static int used = 0;
+  static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  const int n = used.load(std::memory_order_acquire);
-  for (int i = 0; i < n && i < 64; ++i)
-    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].slots;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].slots;
+  }
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   int slots = per_cu * cus;
   if (slots >= 8) slots &= ~7;
   if (slots <= 0) return -1;
-  const int i = used.fetch_add(1, std::memory_order_acq_rel);
-  if (i < 64) cache[i] = Entry{kernel, dev, slots};
+  std::lock_guard<std::mutex> lock(mu);
+  bool known = false;
+  for (int i = 0; i < used; ++i) known = known || (cache[i].k == kernel && cache[i].dev == dev);
+  if (!known && used < 64) cache[used++] = Entry{kernel, dev, slots};
   return slots;
 }
 

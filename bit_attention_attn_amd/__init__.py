@@ -368,8 +368,8 @@ def sage8_prep(q, k, v, workspace=None, qk="int8"):
     """K smoothing and 8-bit quantisation of Q, K, V into a device workspace.
     q, k, v are logical [B,H,N,d] tensors, contiguous or any layout with d
     contiguous (e.g. x.transpose(1, 2) of a token-major [B,N,H,d] tensor).
-    qk="fp8" quantises Q and K to e4m3 blocks (the FP8-QK variant, d = 64 or
-    128) instead of INT8; fwd_sage8 then uses FP8 scores.  qk="int8_no_v"
+    qk="fp8" quantises Q and K to e4m3 blocks (the FP8-QK variant, any of
+    d = 64, 96, 128) instead of INT8; fwd_sage8 then uses FP8 scores.  qk="int8_no_v"
     prepares the INT8 Q and K only (the same codes), for fwd_sage8_pv16."""
     if qk not in _QK_FORMAT:
         raise ValueError('qk must be "int8", "fp8" or "int8_no_v"')

@@ -149,11 +149,13 @@ def test_lds_read_bandwidth(kind):
 def test_lds_fed_product_stream(kind):
     """Back-to-back bf16 32x32x16 products whose A operand comes from LDS,
     read two products ahead (kind 11: 16-byte reads; kind 12: two 8-byte
-    transposing reads per product), with two and four waves per SIMD: the
-    cycles per product of each SIMD (32 would keep the matrix unit busy)."""
+    transposing reads per product), with one, two and four waves per SIMD:
+    the cycles per product of each SIMD (32 would keep the matrix unit busy).
+    One wave alone cannot hide its own read latency; a second wave on the
+    SIMD covers it."""
     name = {11: "ds_read_b128", 12: "2x ds_read_b64_tr_b16"}[kind]
     iters = 500
-    for per_simd in (2, 4):
+    for per_simd in (1, 2, 4):
         waves = 4 * per_simd
         _run(kind, 1, waves, 20)
         t = _run(kind, 1, waves, iters)

@@ -28,6 +28,13 @@
 //   read per product; kind 12: two 8-byte transposing reads), the order
 //   pinned by scheduling barriers: how busy LDS-fed products keep the matrix
 //   unit.
+// split_kernel (kind 15): the first half of a workgroup's waves run the bf16
+//   product rounds of kind 3, the second half three times as many rounds of
+//   kind 1 (exponentials), so each product wave shares its SIMD with
+//   exponential waves for its whole run; every wave also writes the SIMD it
+//   ran on (bits 5:4 of the hardware ID register) to sink[n + wave], n the
+//   number of waves: whether exponentials on one wave slow another wave's
+//   products.
 // clock_kernel: every wave runs bf16 MFMA chains for `iters` rounds and
 // writes its shader cycles and its 100 MHz real-time ticks (s_memrealtime),
 // so cycles / ticks * 100 MHz is the clock the chip ran at under that load.
@@ -245,6 +252,25 @@ __global__ void feed_kernel(int iters, unsigned long long* cyc, float* sink) {
   sink[wave * 64 + lane] = acc[0][0] + acc[1][5];
 }
 
+__global__ void split_kernel(int iters, float a, float b, unsigned long long* cyc, float* sink) {
+  const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int n = gridDim.x * (blockDim.x / 64);
+  const bool products = (int)(threadIdx.x / 64) < (int)(blockDim.x / 128);  // wave-uniform
+  float s;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  if (products) run_rounds<3>(iters, a, b, &s);
+  else run_rounds<1>(3 * iters, a, b, &s);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  // HW_ID register, all 32 bits: (31 << 11) | (0 << 6) | 4
+  const unsigned hwid = __builtin_amdgcn_s_getreg(0xF804);
+  if ((threadIdx.x & 63) == 0) {
+    cyc[2 * wave] = t0;
+    cyc[2 * wave + 1] = t1;
+    sink[wave] = s;
+    sink[n + wave] = (float)((hwid >> 4) & 3);
+  }
+}
+
 __global__ void clock_kernel(int iters, float a, float b, unsigned long long* out, float* sink) {
   const int wave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
   float s;
@@ -286,6 +312,10 @@ extern "C" int issue_rate_probe_run(int kind, int wgs, int waves_per_wg, int ite
     case 12: hipLaunchKernelGGL(feed_kernel<true>, grid, block, 0, s, iters, c, k); break;
     case 13: hipLaunchKernelGGL(rate_kernel<13>, grid, block, 0, s, iters, a, b, c, k); break;
     case 14: hipLaunchKernelGGL(rate_kernel<14>, grid, block, 0, s, iters, a, b, c, k); break;
+    case 15:
+      if (waves_per_wg % 2 != 0) return -1;
+      hipLaunchKernelGGL(split_kernel, grid, block, 0, s, iters, a, b, c, k);
+      break;
     default: return -1;
   }
   return (int)hipGetLastError();

@@ -118,6 +118,37 @@ def test_matrix_and_exp_overlap():
     assert 0.95 * mf <= mix <= serial * 1.1
 
 
+def test_exp_on_another_wave_of_the_simd():
+    """Eight waves: the first four run bf16 products, the other four run
+    exponentials for longer (three times the rounds), and each wave reports
+    the SIMD it ran on.  The product waves' cycles per product against one
+    product wave alone: whether exponentials on one wave slow the product
+    stream of another wave on the same SIMD (within one wave they do not
+    overlap, test_matrix_and_exp_overlap)."""
+    L = _lib()
+    iters = 1000
+    alone = _alone(3, iters)
+    ex = _alone(1, 4000)
+    n = 8
+    cyc = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(64 * n, dtype=torch.float32, device="cuda")
+    for it in (50, iters):
+        assert L.issue_rate_probe_run(15, 1, n, it, cyc.data_ptr(), sink.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+    t = cyc.cpu().numpy().astype(np.float64).reshape(n, 2)
+    simd = sink[n:2 * n].cpu().numpy().astype(int)
+    prod = [w for w in range(4) if any(simd[e] == simd[w] for e in range(4, 8))]
+    assert prod, f"no product wave shares a SIMD with an exponential wave: {simd.tolist()}"
+    cpp = [float(np.diff(t[w])[0]) / (iters * 32) for w in prod]
+    # 6 exponentials per product of the partner wave (3 * 64 per 32 products)
+    serial = alone + 6 * ex
+    print(f"    SIMD of each wave {simd.tolist()}; product waves beside exponential waves: "
+          f"{[round(x, 1) for x in cpp]} cycles per product (alone {alone:.1f}; in series with the "
+          f"partner's exponentials {serial:.1f})", flush=True)
+    assert all(0.95 * 31.0 <= x <= 1.1 * serial for x in cpp)
+
+
 def test_exp_beside_fma():
     """v_exp_f32 and v_fma_f32 alternating on separate chains, one wave: the
     cost of the pair against the two alone."""

@@ -189,3 +189,17 @@ def test_int8_scores_beat_fp8_scores_on_outliers():
     print(f"    int8 scores: {res['int8']}; fp8 scores: {res['fp8']}", flush=True)
     assert res["int8"]["rel_l1"] < res["fp8"]["rel_l1"] and res["int8"]["cos"] > res["fp8"]["cos"]
     assert cfg["outliers"]
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_deterministic(d):
+    """Two calls on the same FP8-QK workspace give the same O and LSE bit for
+    bit (no NaN anywhere, so torch.equal compares every value)."""
+    inp = workloads.make_inputs(2, 2, 700, d, "bf16", seed=70 + d, outliers=True)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    prep = attn.sage8_prep(q, k, v, qk="fp8")
+    o1, l1 = attn.fwd_sage8(prep, causal=True, return_lse=True)
+    o2, l2 = attn.fwd_sage8(prep, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

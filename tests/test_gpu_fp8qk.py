@@ -164,7 +164,7 @@ def test_block_sparse_and_scale_edges():
         _check(inp, True, scale, label=f"scale={scale}", check_oracle=scale != 0.0)
 
 
-@pytest.mark.parametrize("cfg_id", [4, 5])
+@pytest.mark.parametrize("cfg_id", [4, 5, 3])
 def test_workload_sampled(cfg_id):
     cfg, inp = workloads.config_inputs(cfg_id)
     rows = workloads.parity_rows(cfg["B"], cfg["H"], cfg["N"], seed=cfg_id, n_random=24)

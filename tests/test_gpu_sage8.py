@@ -237,7 +237,7 @@ def test_sageattn_matches_two_step():
 
 # ------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("cfg_id", [4, 5, 2])
+@pytest.mark.parametrize("cfg_id", [4, 5, 2, 3])
 def test_workload_sampled_rows(cfg_id):
     """Full-size workloads in the launch configuration the benchmark times:
     sampled rows against the fp32 model and the exact attention."""
